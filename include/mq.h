@@ -1,0 +1,176 @@
+/*
+ * mq.h - C ABI of the NVFP4 prefill linear and BF16 decode GEMV library
+ *        (libmq.so, HIP for AMD Instinct MI355X / gfx950).
+ *
+ * The method ("Mix-Quant: Quantized Prefilling, Precise Decoding for Agentic
+ * LLMs"; gist.science English explainer, Technical Summary s.2 Methodology):
+ * prefill linears run with weights and activations both in NVFP4 (W4A4; s.2
+ * System-Level Deployment), a format with one local scale per group of 16
+ * elements plus a tensor-level scale, elements rounded to nearest (s.2
+ * Hybrid Precision Strategy); decode keeps the original BF16 weights (same
+ * passage, Decoding).  This library is that data-parallel path on one GPU:
+ *
+ *   mq_quantize_nvfp4      bf16 [rows][cols] -> NVFP4 (dynamic tensor scale)
+ *   mq_gemm_nvfp4_prefill  C = A . W^T with A, W in NVFP4, fp32 accumulate,
+ *                          bf16 (or fp32) output
+ *   mq_gemv_bf16_decode    Y = X . W^T on bf16 X [M][K] and W [N][K]
+ *
+ * Formats (readings where the pages are silent):
+ *   element   OCP E2M1 4-bit code = sign<<3 | magnitude index, magnitudes
+ *             {0, .5, 1, 1.5, 2, 3, 4, 6}; two codes per byte, even column in
+ *             the low nibble; codes stored [rows][cols/2], row-major.
+ *   group     one OCP E4M3 ("fn", bias 7, max 448) byte per 16 consecutive
+ *             elements of a row, stored [rows][cols/16], row-major.
+ *   tensor    binary32 decode scale s_t = amax/2688 (1.0 if amax == 0), kept
+ *             in a device-resident mq_scale_rec.
+ *   Quantization, per group: rho = (a/6)/s_t, S = E4M3_rne_sat(rho),
+ *   d = value(S)*s_t, e = 1/d (0 if d == 0); per element y = x*e,
+ *   code = signbit(x)<<3 | E2M1_rne_sat(|y|) (NaN y -> 0): each a single
+ *   IEEE binary32 operation.  Results are bit-exact and unique.
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are caller-owned DEVICE memory on the current HIP
+ *     device; the struct arguments themselves (mq_nvfp4) live in host
+ *     memory.  The library allocates no device memory and frees nothing.
+ *   - Arguments are checked synchronously on the host.  On failure the call
+ *     returns an MQ_ERR_* code and launches nothing; mq_last_error() gives a
+ *     thread-local message.  Nothing is thrown or aborted across the ABI.
+ *   - On success, work is queued asynchronously on hip_stream (a
+ *     hipStream_t; NULL = the default stream) and MQ_OK is returned without
+ *     synchronising.  Launch failures seen by hipGetLastError() right after
+ *     the launch give MQ_ERR_LAUNCH.
+ *   - Matrices are contiguous and row-major (leading dimension = columns).
+ *   - Outputs are bit-deterministic: no atomics touch output values.
+ *   - Calls are thread-safe.  Two calls in flight at once must not share an
+ *     output buffer or an mq_scale_rec.
+ */
+#ifndef MQ_H_
+#define MQ_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mq_status;
+#define MQ_OK           0
+#define MQ_ERR_INVALID  1 /* NULL pointer, unknown flag, bad combination   */
+#define MQ_ERR_SHAPE    2 /* a size <= 0, cols or K not a multiple of 16,
+                             or a size whose byte count overflows int64     */
+#define MQ_ERR_ALIGN    3 /* a device pointer not aligned as documented     */
+#define MQ_ERR_DEVICE   4 /* no HIP device, or the current one is not gfx950 */
+#define MQ_ERR_LAUNCH   5 /* a kernel launch reported an error              */
+
+/* Number of per-workgroup partial maxima an mq_scale_rec can hold. */
+#define MQ_AMAX_PARTS 1020
+
+/* Tensor-scale record, DEVICE memory, 4096 bytes, 16-byte aligned.
+ * s_t       binary32 decode scale of the tensor (read by the GEMM epilogue).
+ * amax_bits bit pattern of max|x| that s_t came from (0 when given).
+ * nparts    number of valid entries in part[] (written by the amax pass).
+ * flags     reserved, 0.
+ * part[]    per-workgroup maxima of |x| as binary32 bit patterns; written by
+ *           the amax pass and reduced by whichever kernel consumes the scale.
+ * The record needs no initialisation: every field a call reads was written
+ * earlier in the same call, except s_t under MQ_SCALE_GIVEN (caller-set). */
+typedef struct mq_scale_rec {
+  float s_t;
+  uint32_t amax_bits;
+  uint32_t nparts;
+  uint32_t flags;
+  uint32_t part[MQ_AMAX_PARTS];
+} mq_scale_rec;
+
+/* An NVFP4 matrix of [rows][cols] elements.  HOST struct of DEVICE pointers.
+ * codes  uint8 [rows][cols/2]  (8-byte aligned)
+ * scales uint8 [rows][cols/16] (any alignment)
+ * rec    mq_scale_rec          (16-byte aligned) */
+typedef struct mq_nvfp4 {
+  uint8_t* codes;
+  uint8_t* scales;
+  mq_scale_rec* rec;
+} mq_nvfp4;
+
+/* flags */
+#define MQ_SCALE_DYNAMIC 0u  /* tensor scale from max|x| of this call (default) */
+#define MQ_SCALE_GIVEN   1u  /* use rec->s_t as already set (finite, > 0)      */
+#define MQ_OUT_BF16      0u  /* GEMM output bf16 (default)                      */
+#define MQ_OUT_F32       2u  /* GEMM output binary32 (pre-rounding value)       */
+#define MQ_A_FUSED_BF16  4u  /* GEMM: A given as bf16, quantized in-kernel      */
+
+/*
+ * mq_quantize_nvfp4 - quantize a bf16 matrix to NVFP4.
+ *   The two-level scaling of the gist.science explainer, s.2 Hybrid
+ *   Precision Strategy: tensor scale from the absolute maximum of the whole
+ *   input (taken at run time), an E4M3 scale per 16-element group of a row,
+ *   round-to-nearest-even E2M1 codes.
+ * x_bf16   DEVICE bf16 [rows][cols], 16-byte aligned, finite values.
+ * rows     >= 1.   cols >= 16, cols % 16 == 0.
+ * out      HOST pointer to an mq_nvfp4 whose codes/scales/rec are written.
+ *          out->rec->s_t, amax_bits, nparts and part[] are overwritten
+ *          (with MQ_SCALE_GIVEN only out->rec->s_t is read).
+ * flags    MQ_SCALE_DYNAMIC or MQ_SCALE_GIVEN.
+ * Launches: an amax pass (dynamic only), then the quantizer.
+ */
+mq_status mq_quantize_nvfp4(const void* x_bf16, int64_t rows, int64_t cols,
+                            const mq_nvfp4* out, uint32_t flags,
+                            void* hip_stream);
+
+/*
+ * mq_gemm_nvfp4_prefill - C[M][N] = A[M][K] . W[N][K]^T, NVFP4 operands.
+ *   The W4A4 prefill linear (gist.science explainer, s.2 System-Level
+ *   Deployment, prefill workers).  Every product uses the exact dequantized
+ *   operands g*sigma; accumulation is binary32; the result is multiplied by
+ *   s_tA*s_tW and rounded to nearest-even bf16 (or stored as binary32 with
+ *   MQ_OUT_F32).  No bias.
+ * a        HOST pointer to the quantized activations (codes, scales, rec;
+ *          rec->s_t must already hold A's scale, e.g. from
+ *          mq_quantize_nvfp4 earlier on the same stream).  With
+ *          MQ_A_FUSED_BF16, a->codes and a->scales are ignored (may be NULL)
+ *          and a->rec receives the amax pass of a_bf16 (or supplies s_t
+ *          under MQ_SCALE_GIVEN).
+ * a_bf16   DEVICE bf16 [M][K], 16-byte aligned; only with MQ_A_FUSED_BF16,
+ *          else must be NULL.  The fused path computes exactly the codes
+ *          mq_quantize_nvfp4 would, inside the GEMM.
+ * w        HOST pointer to the quantized weights [N][K] (rec->s_t set).
+ * c        DEVICE output [M][N], bf16 (16-byte aligned) or binary32.
+ * M, N     >= 1.  K >= 16, K % 16 == 0.
+ * flags    MQ_OUT_BF16 | MQ_OUT_F32, optionally | MQ_A_FUSED_BF16, and with
+ *          it optionally | MQ_SCALE_GIVEN.
+ */
+mq_status mq_gemm_nvfp4_prefill(const mq_nvfp4* a, const void* a_bf16,
+                                const mq_nvfp4* w, void* c,
+                                int64_t M, int64_t N, int64_t K,
+                                uint32_t flags, void* hip_stream);
+
+/*
+ * mq_gemv_bf16_decode - Y[M][N] = X[M][K] . W[N][K]^T in bf16.
+ *   The decode step's linear on the original BF16 weights (gist.science
+ *   explainer, s.2 Hybrid Precision Strategy, Decoding; s.2 System-Level
+ *   Deployment, decode workers).  bf16 products, binary32 accumulation,
+ *   nearest-even bf16 output.  Memory-bound on W.
+ * x_bf16   DEVICE bf16 [M][K], 16-byte aligned.
+ * w_bf16   DEVICE bf16 [N][K], 16-byte aligned.
+ * y_bf16   DEVICE bf16 [M][N].
+ * M        1..32 (decode batch).  N >= 1.  K >= 16, K % 16 == 0.
+ * flags    0.
+ */
+mq_status mq_gemv_bf16_decode(const void* x_bf16, const void* w_bf16,
+                              void* y_bf16, int64_t M, int64_t N, int64_t K,
+                              uint32_t flags, void* hip_stream);
+
+/* Static string naming a status code. */
+const char* mq_status_str(mq_status s);
+
+/* Thread-local detail of the last error returned on this thread ("" if none). */
+const char* mq_last_error(void);
+
+/* Library version string. */
+const char* mq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MQ_H_ */
