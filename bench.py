@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""NVFP4 prefill linear throughput on one MI355X, activation quantization included.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|5]
+
+One step = one pass of the prefill hot path over one 8B-shaped decoder layer
+(default: M=4096 tokens through q,k,v,o,gate,up,down): each of the layer's
+four activation tensors is quantized to NVFP4 on the fly (amax pass +
+encode), then every NVFP4 x NVFP4 GEMM that consumes it runs (bf16 output).
+Weights are quantized once before timing (offline, as the method keeps them
+in the low-precision format).  With --config 3 (M=32768) every GEMM instead
+quantizes its bf16 input in its own prologue.  Inputs are seeded synthetic
+bf16 tensors, resident in HBM before the timed region.
+
+Prints one JSON line with the whole-step TFLOP/s, the roofline of the
+dominant kernel (the GEMM; HIP events around every GEMM launch on the
+launching stream), torch's BF16 GEMM at the same shapes for comparison, and
+the CPU oracle's throughput on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 prefill GEMM TFLOP/s incl. act-quant at 8B shapes; % MFMA peak"
+PEAK_F16_MFMA_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", type=int, default=2, choices=(2, 3, 5))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-bf16", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=512, help="activation rows in the CPU sample")
+    return p.parse_args()
+
+
+def dev_bf16(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def setup(cfg_id):
+    import torch
+    import fp4_block_scaled_elem_amd as mq
+    import workloads
+    cfg = workloads.CONFIGS[cfg_id]
+    M = cfg.M[0]
+    acts_host = {a: workloads.activation(cfg_id, a) for a in workloads.ACTS}
+    acts = {a: dev_bf16(b) for a, b in acts_host.items()}
+    qw, wdev = {}, {}
+    for p in cfg.projs:
+        wb = workloads.weight(cfg_id, p)
+        wdev[p] = dev_bf16(wb)
+        qw[p] = mq.quantize(wdev[p])          # offline weight quantization
+    qa = {a: mq.NVFP4.empty(*acts[a].shape) for a in workloads.ACTS}
+    fa = {p: mq.NVFP4(None, None, torch.zeros(mq.REC_BYTES // 4, dtype=torch.int32, device="cuda"))
+          for p in cfg.projs}
+    out = {p: torch.empty((M, cfg.layer.proj_nk(p)[0]), dtype=torch.bfloat16, device="cuda")
+           for p in cfg.projs}
+    torch.cuda.synchronize()
+    return cfg, acts_host, acts, wdev, qw, qa, fa, out
+
+
+def run_step(cfg, acts, qw, qa, fa, out, events=None):
+    import fp4_block_scaled_elem_amd as mq
+    import workloads
+    consumers = {a: [p for p in cfg.projs if workloads.PROJ_INPUT[p] == a] for a in workloads.ACTS}
+    for a in workloads.ACTS:
+        if not cfg.fused_act_quant:
+            if events is not None:
+                events["q"].append(_ev())
+            mq.mq_quantize_nvfp4(acts[a], qa[a])
+            if events is not None:
+                events["q"].append(_ev())
+        for p in consumers[a]:
+            if events is not None:
+                events["g"].append(_ev())
+            if cfg.fused_act_quant:
+                mq.mq_gemm_nvfp4_prefill(fa[p], acts[a], qw[p], out[p], mq.MQ_A_FUSED_BF16)
+            else:
+                mq.mq_gemm_nvfp4_prefill(qa[a], None, qw[p], out[p], 0)
+            if events is not None:
+                events["g"].append(_ev())
+
+
+def _ev():
+    import torch
+    e = torch.cuda.Event(enable_timing=True)
+    e.record()  # on the current stream, which the binding launches on
+    return e
+
+
+def _pairs_ms(evs):
+    return sum(evs[i].elapsed_time(evs[i + 1]) for i in range(0, len(evs), 2))
+
+
+def bf16_reference(cfg, acts, wdev, iters=10):
+    """torch's BF16 GEMM (hipBLASLt) at the same shapes, TFLOP/s."""
+    import torch
+    import torch.nn.functional as F
+    import workloads
+    flops = cfg.flops()
+    for _ in range(3):
+        for p in cfg.projs:
+            F.linear(acts[workloads.PROJ_INPUT[p]], wdev[p])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(iters):
+        for p in cfg.projs:
+            F.linear(acts[workloads.PROJ_INPUT[p]], wdev[p])
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / iters
+    return flops / dt / 1e12
+
+
+def cpu_baseline(cfg_id, acts_host, rows):
+    """The oracle as it stands, on a bounded sample of the same workload:
+    the first ``rows`` tokens of each activation (quantized as a tensor of
+    their own) times 1024 weight rows of every projection (weights quantized
+    beforehand, untimed, as on the GPU)."""
+    import numpy as np
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = 1
+    cfg = workloads.CONFIGS[cfg_id]
+    wq = {}
+    for p in cfg.projs:
+        wb = workloads.weight(cfg_id, p)
+        wq[p] = oracle.quantize_nvfp4(wb[:1024])
+    flops, dt = 0, 0.0
+    for a in workloads.ACTS:
+        xs = acts_host[a][:rows]
+        t0 = time.perf_counter()
+        qa = oracle.quantize_nvfp4(xs)
+        for p in cfg.projs:
+            if workloads.PROJ_INPUT[p] != a:
+                continue
+            c = oracle.gemm_nvfp4_ref(qa, wq[p])
+            flops += 2 * c.shape[0] * c.shape[1] * xs.shape[1]
+        dt += time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
+            "sample": (f"first {rows} tokens of each activation x 1024 weight rows of each of "
+                       f"{len(cfg.projs)} projections ({flops / 1e9:.1f} GFLOP, {dt:.1f} s; NumPy "
+                       f"elementwise steps single-threaded, float64 matmul on {blas} BLAS threads)")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is not part of it", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg, acts_host, acts, wdev, qw, qa, fa, out = setup(args.config)
+    flops = cfg.flops()
+
+    for _ in range(args.warmup):
+        run_step(cfg, acts, qw, qa, fa, out)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps between two device synchronisations;
+    # HIP events around every launch (recorded on the launching stream) give
+    # the per-kernel split
+    events = {"q": [], "g": []}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(cfg, acts, qw, qa, fa, out, events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    value = flops / (wall / args.steps) / 1e12
+    gemm_ms = _pairs_ms(events["g"]) / args.steps
+    q_ms = _pairs_ms(events["q"]) / args.steps if events["q"] else 0.0
+    n_gemm = len(cfg.projs)
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+
+    bf16 = None if args.no_bf16 else bf16_reference(cfg, acts, wdev)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.config, acts_host, args.cpu_rows)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "desc": cfg.desc, "M": cfg.M[0],
+                   "layer": {"d_model": cfg.layer.d_model, "d_kv": cfg.layer.d_kv, "d_ffn": cfg.layer.d_ffn},
+                   "projections": list(cfg.projs), "act_quant": "fused" if cfg.fused_act_quant else "separate",
+                   "flop_per_step": flops},
+        "pct_mfma_peak": round(100.0 * value / PEAK_F16_MFMA_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": "gemm_nvfp4_kernel", "achieved": round(gemm_tflops, 2),
+                     "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / PEAK_F16_MFMA_TFLOPS, 4), "traffic": None,
+                     "launches_per_step": n_gemm, "avg_launch_ms": round(gemm_ms / n_gemm, 4)},
+        "split_ms": {"act_quant": round(q_ms, 4), "gemm": round(gemm_ms, 4)},
+        "bf16_torch_tflops": None if bf16 is None else round(bf16, 2),
+        "ratio_vs_bf16_torch": None if bf16 is None else round(value / bf16, 3),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

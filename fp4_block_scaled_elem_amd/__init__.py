@@ -1,0 +1,227 @@
+"""Python binding of libmq.so: NVFP4 prefill linear + BF16 decode GEMV on MI355X.
+
+Argument marshalling only.  Every step of the path runs in the HIP kernels of
+``libmq.so``; PyTorch supplies device memory and the current stream.  If the
+library has not been built, every entry point raises ``LibraryNotBuilt``
+(there is no fallback of any kind).
+
+Entry points (same names as the C ABI in include/mq.h):
+
+    mq_quantize_nvfp4(x_bf16, out: NVFP4, flags=0, stream=None)
+    mq_gemm_nvfp4_prefill(a: NVFP4, a_bf16, w: NVFP4, c, flags=0, stream=None)
+    mq_gemv_bf16_decode(x_bf16, w_bf16, y_bf16, flags=0, stream=None)
+
+and small conveniences built on them (``quantize``, ``prefill_linear``,
+``decode_linear``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmq.so")
+
+# status codes and flags (mirror include/mq.h)
+MQ_OK = 0
+MQ_ERR_INVALID = 1
+MQ_ERR_SHAPE = 2
+MQ_ERR_ALIGN = 3
+MQ_ERR_DEVICE = 4
+MQ_ERR_LAUNCH = 5
+MQ_SCALE_DYNAMIC = 0
+MQ_SCALE_GIVEN = 1
+MQ_OUT_BF16 = 0
+MQ_OUT_F32 = 2
+MQ_A_FUSED_BF16 = 4
+MQ_AMAX_PARTS = 1020
+REC_BYTES = 16 + 4 * MQ_AMAX_PARTS  # sizeof(mq_scale_rec) = 4096
+
+EXPORTS = ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemv_bf16_decode",
+           "mq_status_str", "mq_last_error", "mq_version")
+
+
+class LibraryNotBuilt(ImportError):
+    pass
+
+
+class MQError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)}: {detail}")
+
+
+class _NVFP4C(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("rec", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmq.so (once); raise LibraryNotBuilt if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise LibraryNotBuilt(
+            f"{LIB_PATH} is missing: build it with `python -m fp4_block_scaled_elem_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, u32, vp = ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p
+    P = ctypes.POINTER(_NVFP4C)
+    L.mq_quantize_nvfp4.argtypes = [vp, i64, i64, P, u32, vp]
+    L.mq_quantize_nvfp4.restype = ctypes.c_int32
+    L.mq_gemm_nvfp4_prefill.argtypes = [P, vp, P, vp, i64, i64, i64, u32, vp]
+    L.mq_gemm_nvfp4_prefill.restype = ctypes.c_int32
+    L.mq_gemv_bf16_decode.argtypes = [vp, vp, vp, i64, i64, i64, u32, vp]
+    L.mq_gemv_bf16_decode.restype = ctypes.c_int32
+    L.mq_status_str.argtypes = [ctypes.c_int32]
+    L.mq_status_str.restype = ctypes.c_char_p
+    L.mq_last_error.argtypes = []
+    L.mq_last_error.restype = ctypes.c_char_p
+    L.mq_version.argtypes = []
+    L.mq_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_str(s: int) -> str:
+    return lib().mq_status_str(s).decode()
+
+
+def last_error() -> str:
+    return lib().mq_last_error().decode()
+
+
+def _check(status: int, where: str):
+    if status != MQ_OK:
+        raise MQError(status, where, last_error())
+
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_ptr(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class NVFP4:
+    """Device buffers of one NVFP4 matrix [rows][cols]: packed E2M1 codes
+    [rows][cols/2] (uint8), E4M3 scale bytes [rows][cols/16] (uint8) and the
+    4096-byte tensor-scale record (s_t is its first binary32)."""
+
+    def __init__(self, codes, scales, rec):
+        self.codes, self.scales, self.rec = codes, scales, rec
+
+    @classmethod
+    def empty(cls, rows: int, cols: int, device="cuda"):
+        import torch
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=device)
+        rec = torch.zeros(REC_BYTES // 4, dtype=torch.int32, device=device)
+        return cls(codes, scales, rec)
+
+    @property
+    def shape(self):
+        return (self.codes.shape[0], self.codes.shape[1] * 2)
+
+    def s_t(self) -> float:
+        """Tensor scale (synchronises)."""
+        return float(self.rec[:1].view(__import__("torch").float32).item())
+
+    def set_s_t(self, value: float):
+        import torch
+        self.rec[:1].view(torch.float32).fill_(value)
+
+    def _c(self):
+        return _NVFP4C(self.codes.data_ptr() if self.codes is not None else None,
+                       self.scales.data_ptr() if self.scales is not None else None,
+                       self.rec.data_ptr())
+
+
+def mq_quantize_nvfp4(x_bf16, out: NVFP4, flags: int = MQ_SCALE_DYNAMIC, stream=None):
+    import torch
+    if x_bf16.dtype != torch.bfloat16 or x_bf16.dim() != 2:
+        raise ValueError("x_bf16 must be a 2-D bfloat16 tensor")
+    rows, cols = x_bf16.shape
+    if out.shape != (rows, cols):
+        raise ValueError(f"out is {out.shape}, x is {(rows, cols)}")
+    oc = out._c()
+    _check(lib().mq_quantize_nvfp4(_dev_ptr(x_bf16, "x_bf16"), rows, cols, ctypes.byref(oc),
+                                   flags, _stream_ptr(stream)), "mq_quantize_nvfp4")
+
+
+def mq_gemm_nvfp4_prefill(a: NVFP4, a_bf16, w: NVFP4, c, flags: int = 0, stream=None):
+    import torch
+    N, K = w.shape
+    if a_bf16 is not None:
+        if a_bf16.dtype != torch.bfloat16 or a_bf16.dim() != 2 or a_bf16.shape[1] != K:
+            raise ValueError("a_bf16 must be bfloat16 [M][K]")
+        M = a_bf16.shape[0]
+    else:
+        M, Ka = a.shape
+        if Ka != K:
+            raise ValueError(f"K mismatch: A has {Ka}, W has {K}")
+    want = torch.float32 if flags & MQ_OUT_F32 else torch.bfloat16
+    if c.dtype != want or tuple(c.shape) != (M, N):
+        raise ValueError(f"c must be {want} [{M}][{N}]")
+    ac, wc = a._c(), w._c()
+    _check(lib().mq_gemm_nvfp4_prefill(ctypes.byref(ac), _dev_ptr(a_bf16, "a_bf16"), ctypes.byref(wc),
+                                       _dev_ptr(c, "c"), M, N, K, flags, _stream_ptr(stream)),
+           "mq_gemm_nvfp4_prefill")
+
+
+def mq_gemv_bf16_decode(x_bf16, w_bf16, y_bf16, flags: int = 0, stream=None):
+    import torch
+    for t, n in ((x_bf16, "x"), (w_bf16, "w"), (y_bf16, "y")):
+        if t.dtype != torch.bfloat16 or t.dim() != 2:
+            raise ValueError(f"{n} must be a 2-D bfloat16 tensor")
+    M, K = x_bf16.shape
+    N = w_bf16.shape[0]
+    if w_bf16.shape[1] != K or tuple(y_bf16.shape) != (M, N):
+        raise ValueError("shape mismatch")
+    _check(lib().mq_gemv_bf16_decode(_dev_ptr(x_bf16, "x"), _dev_ptr(w_bf16, "w"), _dev_ptr(y_bf16, "y"),
+                                     M, N, K, flags, _stream_ptr(stream)), "mq_gemv_bf16_decode")
+
+
+# ---------------------------------------------------------------- helpers --
+
+def quantize(x_bf16, stream=None) -> NVFP4:
+    q = NVFP4.empty(x_bf16.shape[0], x_bf16.shape[1], device=x_bf16.device)
+    mq_quantize_nvfp4(x_bf16, q, stream=stream)
+    return q
+
+
+def prefill_linear(x_bf16, w: NVFP4, out=None, fused: bool = False, rec=None, stream=None):
+    """y = NVFP4(x) . NVFP4(W)^T in bf16, quantizing x on the fly."""
+    import torch
+    M = x_bf16.shape[0]
+    N = w.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x_bf16.device)
+    if fused:
+        a = NVFP4(None, None, rec if rec is not None else
+                  torch.zeros(REC_BYTES // 4, dtype=torch.int32, device=x_bf16.device))
+        mq_gemm_nvfp4_prefill(a, x_bf16, w, y, MQ_A_FUSED_BF16, stream)
+    else:
+        a = quantize(x_bf16, stream)
+        mq_gemm_nvfp4_prefill(a, None, w, y, 0, stream)
+    return y
+
+
+def decode_linear(x_bf16, w_bf16, out=None, stream=None):
+    import torch
+    y = out if out is not None else torch.empty((x_bf16.shape[0], w_bf16.shape[0]),
+                                                dtype=torch.bfloat16, device=x_bf16.device)
+    mq_gemv_bf16_decode(x_bf16, w_bf16, y, 0, stream)
+    return y

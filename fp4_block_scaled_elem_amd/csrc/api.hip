@@ -1,0 +1,172 @@
+// api.hip - the extern "C" entry points of libmq.so.
+//
+// Argument checks run first and touch no HIP API, so every MQ_ERR_INVALID /
+// MQ_ERR_SHAPE / MQ_ERR_ALIGN path works on a host without a GPU.  Only
+// then is the current device looked up (once per device, cached) and the
+// kernels queued on the caller's stream.  Nothing here allocates device
+// memory or synchronises.
+#include <mutex>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "mq_internal.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+mq_status fail(mq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+mq_status fail(mq_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+mq_status ok() {
+  g_err[0] = '\0';
+  return MQ_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+mq_status check_dims(int64_t rows, int64_t cols, const char* rname, const char* cname) {
+  if (rows < 1 || cols < 1) return fail(MQ_ERR_SHAPE, "%s=%lld and %s=%lld must be >= 1", rname, (long long)rows, cname, (long long)cols);
+  if (rows > kMaxDim || cols > kMaxDim || rows * cols > ((int64_t)1 << 40))
+    return fail(MQ_ERR_SHAPE, "%s=%lld x %s=%lld exceeds the supported size", rname, (long long)rows, cname, (long long)cols);
+  return MQ_OK;
+}
+
+std::mutex g_dev_mu;
+mq::DeviceInfo g_dev[64];
+
+mq_status current_device(mq::DeviceInfo& out) {
+  int d = -1;
+  if (hipGetDevice(&d) != hipSuccess || d < 0) {
+    (void)hipGetLastError();
+    return fail(MQ_ERR_DEVICE, "no HIP device available");
+  }
+  if (d >= 64) return fail(MQ_ERR_DEVICE, "device index %d not supported", d);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  mq::DeviceInfo& di = g_dev[d];
+  if (di.device != d) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, d) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MQ_ERR_DEVICE, "hipGetDeviceProperties failed for device %d", d);
+    }
+    di.ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    di.num_cu = prop.multiProcessorCount;
+    di.device = d;
+  }
+  if (!di.ok) return fail(MQ_ERR_DEVICE, "device %d is not gfx950", d);
+  out = di;
+  return MQ_OK;
+}
+
+mq_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MQ_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mq_status_str(mq_status s) {
+  switch (s) {
+    case MQ_OK: return "MQ_OK";
+    case MQ_ERR_INVALID: return "MQ_ERR_INVALID";
+    case MQ_ERR_SHAPE: return "MQ_ERR_SHAPE";
+    case MQ_ERR_ALIGN: return "MQ_ERR_ALIGN";
+    case MQ_ERR_DEVICE: return "MQ_ERR_DEVICE";
+    case MQ_ERR_LAUNCH: return "MQ_ERR_LAUNCH";
+    default: return "MQ_ERR_UNKNOWN";
+  }
+}
+
+const char* mq_last_error(void) { return g_err; }
+
+const char* mq_version(void) { return "mq 0.1.0 (gfx950)"; }
+
+mq_status mq_quantize_nvfp4(const void* x_bf16, int64_t rows, int64_t cols, const mq_nvfp4* out,
+                            uint32_t flags, void* hip_stream) {
+  if (!x_bf16 || !out) return fail(MQ_ERR_INVALID, "x_bf16 and out must not be NULL");
+  if (!out->codes || !out->scales || !out->rec) return fail(MQ_ERR_INVALID, "out->codes, scales and rec must not be NULL");
+  if (flags & ~MQ_SCALE_GIVEN) return fail(MQ_ERR_INVALID, "unknown flags 0x%x", flags);
+  if (mq_status s = check_dims(rows, cols, "rows", "cols")) return s;
+  if (cols % 16) return fail(MQ_ERR_SHAPE, "cols=%lld is not a multiple of 16", (long long)cols);
+  if (!aligned(x_bf16, 16) || !aligned(out->codes, 16) || !aligned(out->scales, 8) || !aligned(out->rec, 16))
+    return fail(MQ_ERR_ALIGN, "x and codes need 16-byte, scales 8-byte, rec 16-byte alignment");
+  mq::DeviceInfo dev;
+  if (mq_status s = current_device(dev)) return s;
+  hipStream_t st = (hipStream_t)hip_stream;
+  const bool given = flags & MQ_SCALE_GIVEN;
+  if (!given) {
+    hipError_t e = mq::launch_amax(x_bf16, rows * cols, out->rec, dev, st);
+    if (e != hipSuccess) return launched(e, "amax");
+  }
+  return launched(mq::launch_quantize(x_bf16, rows * cols, out->codes, out->scales, out->rec, given, dev, st),
+                  "quantize");
+}
+
+mq_status mq_gemm_nvfp4_prefill(const mq_nvfp4* a, const void* a_bf16, const mq_nvfp4* w, void* c,
+                                int64_t M, int64_t N, int64_t K, uint32_t flags, void* hip_stream) {
+  const uint32_t known = MQ_OUT_F32 | MQ_A_FUSED_BF16 | MQ_SCALE_GIVEN;
+  if (flags & ~known) return fail(MQ_ERR_INVALID, "unknown flags 0x%x", flags);
+  const bool fused = flags & MQ_A_FUSED_BF16;
+  if ((flags & MQ_SCALE_GIVEN) && !fused) return fail(MQ_ERR_INVALID, "MQ_SCALE_GIVEN needs MQ_A_FUSED_BF16");
+  if (!a || !w || !c) return fail(MQ_ERR_INVALID, "a, w and c must not be NULL");
+  if (!a->rec || !w->codes || !w->scales || !w->rec) return fail(MQ_ERR_INVALID, "a->rec, w->codes, w->scales, w->rec must not be NULL");
+  if (fused) {
+    if (!a_bf16) return fail(MQ_ERR_INVALID, "MQ_A_FUSED_BF16 needs a_bf16");
+  } else {
+    if (a_bf16) return fail(MQ_ERR_INVALID, "a_bf16 must be NULL without MQ_A_FUSED_BF16");
+    if (!a->codes || !a->scales) return fail(MQ_ERR_INVALID, "a->codes and a->scales must not be NULL");
+  }
+  if (mq_status s = check_dims(M, K, "M", "K")) return s;
+  if (mq_status s = check_dims(N, K, "N", "K")) return s;
+  if (M * N > ((int64_t)1 << 40)) return fail(MQ_ERR_SHAPE, "M*N too large");
+  if (K % 16) return fail(MQ_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
+  if (!aligned(w->codes, 16) || !aligned(w->scales, 8) || !aligned(w->rec, 16) || !aligned(a->rec, 16) ||
+      !aligned(c, 16))
+    return fail(MQ_ERR_ALIGN, "codes and c need 16-byte, scales 8-byte, rec 16-byte alignment");
+  if (fused ? !aligned(a_bf16, 16) : (!aligned(a->codes, 16) || !aligned(a->scales, 8)))
+    return fail(MQ_ERR_ALIGN, "A operand misaligned");
+  mq::DeviceInfo dev;
+  if (mq_status s = current_device(dev)) return s;
+  hipStream_t st = (hipStream_t)hip_stream;
+  const bool out_f32 = flags & MQ_OUT_F32;
+  if (!fused)
+    return launched(mq::launch_gemm(a->codes, a->scales, a->rec, w->codes, w->scales, w->rec, c, M, N, K,
+                                    out_f32, dev, st),
+                    "gemm");
+  const bool given = flags & MQ_SCALE_GIVEN;
+  if (!given) {
+    hipError_t e = mq::launch_amax(a_bf16, M * K, a->rec, dev, st);
+    if (e != hipSuccess) return launched(e, "amax");
+  }
+  return launched(mq::launch_gemm_fused(a_bf16, a->rec, given, w->codes, w->scales, w->rec, c, M, N, K, out_f32,
+                                        dev, st),
+                  "gemm_fused");
+}
+
+mq_status mq_gemv_bf16_decode(const void* x_bf16, const void* w_bf16, void* y_bf16, int64_t M, int64_t N,
+                              int64_t K, uint32_t flags, void* hip_stream) {
+  if (flags) return fail(MQ_ERR_INVALID, "unknown flags 0x%x", flags);
+  if (!x_bf16 || !w_bf16 || !y_bf16) return fail(MQ_ERR_INVALID, "x, w and y must not be NULL");
+  if (M < 1 || M > 32) return fail(MQ_ERR_SHAPE, "M=%lld must be in 1..32", (long long)M);
+  if (mq_status s = check_dims(N, K, "N", "K")) return s;
+  if (K % 16) return fail(MQ_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
+  if (!aligned(x_bf16, 16) || !aligned(w_bf16, 16) || !aligned(y_bf16, 2))
+    return fail(MQ_ERR_ALIGN, "x and w need 16-byte alignment, y 2-byte");
+  mq::DeviceInfo dev;
+  if (mq_status s = current_device(dev)) return s;
+  return launched(mq::launch_gemv(x_bf16, w_bf16, y_bf16, M, N, K, dev, (hipStream_t)hip_stream), "gemv");
+}
+
+}  // extern "C"

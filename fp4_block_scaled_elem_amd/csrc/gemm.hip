@@ -1,0 +1,456 @@
+// gemm.hip - NVFP4 x NVFP4 prefill GEMM, C = A . W^T (gfx950).
+//
+// The W4A4 prefill linear of "Mix-Quant: Quantized Prefilling, Precise
+// Decoding for Agentic LLMs" (gist.science English explainer, Technical
+// Summary s.2, System-Level Deployment: prefill workers run weights and
+// activations in NVFP4).
+//
+// Contraction scheme.  gfx950's block-scaled MFMA takes power-of-two (E8M0)
+// scales per 32 elements; NVFP4 has E4M3 scales per 16, so it cannot be fed
+// to that instruction exactly.  Instead each operand element is dequantized
+// to g * sigma (an E2M1 magnitude times the group's E4M3 scale): at most
+// 2 + 4 significant bits, between 2^-10 and 2688, hence an exact normal
+// binary16.  The products are then exact in the binary32 accumulator of
+// v_mfma_f32_32x32x16_f16, and the two tensor scales are applied once in the
+// epilogue.  The result equals the float64 product of the dequantized
+// operands up to binary32 accumulation and the final bf16 rounding.
+//
+// Data flow per workgroup (256 threads = 4 waves in a 2x2 grid; tile BM x BN;
+// K advanced 128 elements = 8 groups per stage):
+//   HBM --16B loads--> registers --> LDS (packed codes + scale bytes,
+//   double-buffered, rows padded to avoid bank conflicts)
+//   LDS --ds_read_b128--> registers: one dword = 8 codes of one group
+//   cvt fp4->f16 (hardware) * sigma (packed f16 multiply) -> MFMA operand.
+// The K order inside a stage is permuted consistently for A and W so that a
+// lane's 16-byte LDS read feeds four consecutive MFMAs; the sum is unchanged.
+#include "mq_device.h"
+#include "mq_internal.h"
+
+namespace mq {
+
+constexpr int kThreads = 256;
+constexpr int kBK = 128;            // K elements per stage
+constexpr int kRowBytes = kBK / 2;  // packed code bytes per row per stage
+constexpr int kRowStride = 80;      // LDS bytes per code row (64 + 16 pad)
+constexpr int kScaleStride = 8;     // LDS bytes per scale row (8 groups)
+
+struct GemmArgs {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const void* a_bf16;        // fused mode only
+  mq_scale_rec* a_rec;
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  const mq_scale_rec* w_rec;
+  void* c;
+  int M, N, K;
+  int tiles_m, tiles_n;
+  int a_given;               // fused mode: take s_t from a_rec
+};
+
+template <int BM, int BN>
+struct Smem {
+  static constexpr int kA = 0;
+  static constexpr int kW = kA + BM * kRowStride;
+  static constexpr int kAs = kW + BN * kRowStride;
+  static constexpr int kWs = kAs + BM * kScaleStride;
+  static constexpr int kStage = kWs + BN * kScaleStride;
+  static constexpr int kTotal = 2 * kStage;
+};
+
+// ---------------------------------------------------------------- loaders --
+
+// Packed operand (A or W) rows [r0, r0+ROWS) x stage kt into registers.
+template <int ROWS, bool FAST>
+struct PackedLoader {
+  static constexpr int kChunks = ROWS * 4 / kThreads;  // 16-byte pieces per thread
+  u32x4_t code[kChunks > 0 ? kChunks : 1];
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ codes, int r0, int nrows, int K, int kt) {
+    const int tid = threadIdx.x;
+    const int64_t ldc = K / 2;
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+      const int c = tid + kThreads * j;
+      const int row = c >> 2, col = c & 3;
+      int r = r0 + row;
+      r = r < nrows ? r : nrows - 1;  // clamped rows are computed and discarded
+      const uint8_t* p = codes + (int64_t)r * ldc + (int64_t)kt * kRowBytes + col * 16;
+      if (FAST) {
+        code[j] = *(const u32x4_t*)p;
+      } else {
+        // K % 16 == 0 only: rows are 8-byte aligned; load each group alone
+        const int e0 = kt * kBK + col * 32;
+        u32x2_t lo = {0u, 0u}, hi = {0u, 0u};
+        if (e0 < K) lo = *(const u32x2_t*)p;
+        if (e0 + 16 < K) hi = *(const u32x2_t*)(p + 8);
+        code[j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* lds) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) {
+      const int c = tid + kThreads * j;
+      const int row = c >> 2, col = c & 3;
+      *(u32x4_t*)(lds + row * kRowStride + col * 16) = code[j];
+    }
+  }
+};
+
+// Scale bytes for A rows then W rows (BM + BN rows of 8 bytes per stage);
+// with WITH_A false (fused prologue) only the W rows.
+template <int BM, int BN, bool FAST, bool WITH_A>
+struct ScaleLoader {
+  static constexpr int kA = WITH_A ? BM : 0;
+  static constexpr int kRows = kA + BN;
+  static constexpr int kPer = (kRows + kThreads - 1) / kThreads;
+  u32x2_t v[kPer];
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ as, const uint8_t* __restrict__ ws,
+                                       int m0, int n0, int M, int N, int K, int kt) {
+    const int ng = K / kGroup;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int r = threadIdx.x + kThreads * j;
+      v[j] = u32x2_t{0u, 0u};
+      if (r < kRows) {
+        const uint8_t* base;
+        int row;
+        if (r < kA) { row = m0 + r; row = row < M ? row : M - 1; base = as; }
+        else        { row = n0 + r - kA; row = row < N ? row : N - 1; base = ws; }
+        const uint8_t* p = base + (int64_t)row * ng + kt * 8;
+        if (FAST) {
+          v[j] = *(const u32x2_t*)p;
+        } else {
+          uint32_t b[8];
+#pragma unroll
+          for (int g = 0; g < 8; ++g) b[g] = (kt * 8 + g < ng) ? p[g] : 0u;
+          v[j] = u32x2_t{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                         b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* stage) const {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int r = threadIdx.x + kThreads * j;
+      if (r < kRows) {
+        uint8_t* p = r < kA ? stage + Smem<BM, BN>::kAs + r * kScaleStride
+                            : stage + Smem<BM, BN>::kWs + (r - kA) * kScaleStride;
+        *(u32x2_t*)p = v[j];
+      }
+    }
+  }
+};
+
+// bf16 activations quantized on the fly (fused prologue): BM rows x 128
+// elements per stage = BM*8 groups, each thread owning whole groups.  The
+// arithmetic is quantize_group16, bit-identical to the standalone quantizer.
+template <int BM, bool FAST>
+struct FusedALoader {
+  static constexpr int kGroupsPer = BM * 8 / kThreads;
+  u32x4_t raw[kGroupsPer][2];
+
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ a, int m0, int M, int K, int kt) {
+#pragma unroll
+    for (int j = 0; j < kGroupsPer; ++j) {
+      const int gi = threadIdx.x + kThreads * j;
+      const int row = gi >> 3, grp = gi & 7;
+      int r = m0 + row;
+      r = r < M ? r : M - 1;
+      const int e0 = kt * kBK + grp * kGroup;
+      const uint16_t* p = a + (int64_t)r * K + e0;
+      if (FAST || e0 < K) {
+        raw[j][0] = *(const u32x4_t*)p;
+        raw[j][1] = *(const u32x4_t*)(p + 8);
+      } else {
+        raw[j][0] = u32x4_t{0u, 0u, 0u, 0u};
+        raw[j][1] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  template <int BN>
+  __device__ __forceinline__ void quantize_store(uint8_t* stage, float s_t) const {
+#pragma unroll
+    for (int j = 0; j < kGroupsPer; ++j) {
+      const int gi = threadIdx.x + kThreads * j;
+      const int row = gi >> 3, grp = gi & 7;
+      uint32_t w[8] = {raw[j][0][0], raw[j][0][1], raw[j][0][2], raw[j][0][3],
+                       raw[j][1][0], raw[j][1][1], raw[j][1][2], raw[j][1][3]};
+      uint32_t lo, hi;
+      uint32_t S = quantize_group16(w, s_t, lo, hi);
+      *(u32x2_t*)(stage + Smem<BM, BN>::kA + row * kRowStride + grp * 8) = u32x2_t{lo, hi};
+      stage[Smem<BM, BN>::kAs + row * kScaleStride + grp] = (uint8_t)S;
+    }
+  }
+};
+
+// --------------------------------------------------------------- compute --
+
+// 8 E2M1 codes (one dword) times the group scale -> 8 exact binary16 values.
+__device__ __forceinline__ half8_t dequant8(uint32_t codes, uint32_t sigma_pair) {
+  const half2_t s = __builtin_bit_cast(half2_t, sigma_pair);
+  half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s;
+  half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s;
+  half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s;
+  half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s;
+  half8_t r;
+  r[0] = h0[0]; r[1] = h0[1]; r[2] = h1[0]; r[3] = h1[1];
+  r[4] = h2[0]; r[5] = h2[1]; r[6] = h3[0]; r[7] = h3[1];
+  return r;
+}
+
+__device__ __forceinline__ uint32_t sigma_pair_from(uint32_t scale_dword, int byte) {
+  uint32_t h = e4m3_to_f16_bits((scale_dword >> (8 * byte)) & 0xFFu);
+  return h | (h << 16);
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void compute_stage(const uint8_t* stage, f32x16_t (&acc)[BM / 64][BN / 64],
+                                              int wave_m, int wave_n, int li, int lh) {
+  constexpr int TM = BM / 64, TN = BN / 64;
+  const uint8_t* la = stage + Smem<BM, BN>::kA + (wave_m + li) * kRowStride + lh * 16;
+  const uint8_t* lw = stage + Smem<BM, BN>::kW + (wave_n + li) * kRowStride + lh * 16;
+  const uint8_t* las = stage + Smem<BM, BN>::kAs + (wave_m + li) * kScaleStride;
+  const uint8_t* lws = stage + Smem<BM, BN>::kWs + (wave_n + li) * kScaleStride;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    u32x4_t ar[TM], wr[TN];
+    uint32_t as[TM], ws[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      ar[i] = *(const u32x4_t*)(la + i * 32 * kRowStride + t * 32);
+      as[i] = *(const uint32_t*)(las + i * 32 * kScaleStride + t * 4);
+    }
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      wr[i] = *(const u32x4_t*)(lw + i * 32 * kRowStride + t * 32);
+      ws[i] = *(const uint32_t*)(lws + i * 32 * kScaleStride + t * 4);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int sb = 2 * lh + (q >> 1);  // scale byte of this lane's group
+      half8_t ao[TM], wo[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        ao[i] = dequant8(ar[i][q], sigma_pair_from(as[i], sb));
+      }
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        wo[i] = dequant8(wr[i][q], sigma_pair_from(ws[i], sb));
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao[i], wo[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
+  uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int BM, int BN, bool OUT_F32>
+__device__ __forceinline__ void epilogue(const f32x16_t (&acc)[BM / 64][BN / 64], void* c, int M, int N,
+                                         int m0, int n0, int wave_m, int wave_n, int lane, float scale) {
+  constexpr int TM = BM / 64, TN = BN / 64;
+  const int j = lane & 31, ib = (lane >> 5) * 4;
+#pragma unroll
+  for (int fm = 0; fm < TM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < TN; ++fn) {
+      const int n = n0 + wave_n + fn * 32 + j;
+      if (n >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wave_m + fm * 32 + ib + (v & 3) + 8 * (v >> 2);
+        if (m < M) {
+          const float r = acc[fm][fn][v] * scale;
+          if (OUT_F32) ((float*)c)[(int64_t)m * N + n] = r;
+          else ((uint16_t*)c)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(r);
+        }
+      }
+    }
+}
+
+// Tile order: workgroups go round-robin to the 8 XCDs; consecutive logical
+// tiles are put on one XCD (its own L2), and walked in column groups of
+// kGroupM row-tiles so neighbouring workgroups share A and W panels.
+__device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int nwg = tiles_m * tiles_n;
+  int logical = bid;
+  if ((nwg & 7) == 0) logical = (bid & 7) * (nwg >> 3) + (bid >> 3);
+  constexpr int kGroupM = 8;
+  const int per_group = kGroupM * tiles_n;
+  const int g = logical / per_group;
+  const int first = g * kGroupM;
+  const int gm = min(tiles_m - first, kGroupM);
+  const int in = logical - g * per_group;
+  tm = first + in % gm;
+  tn = in / gm;
+}
+
+template <int BM, int BN, bool FAST, bool OUT_F32, bool FUSED>
+__global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int TM = BM / 64, TN = BN / 64;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 31, lh = lane >> 5;
+  const int wave_m = (wave >> 1) * (BM / 2), wave_n = (wave & 1) * (BN / 2);
+  int tm, tn;
+  tile_of(blockIdx.x, args.tiles_m, args.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int M = args.M, N = args.N, K = args.K;
+  const int nk = (K + kBK - 1) / kBK;
+
+  float s_ta;
+  if (FUSED && !args.a_given) {
+    // reduce the amax pass's partial maxima (same rule as the quantizer)
+    __shared__ uint32_t red[kThreads / 64];
+    const uint32_t np = args.a_rec->nparts;
+    uint32_t m = 0;
+    for (uint32_t j = tid; j < np; j += kThreads) {
+      uint32_t v = args.a_rec->part[j];
+      m = m > v ? m : v;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      uint32_t o = __shfl_xor(m, off, 64);
+      m = m > o ? m : o;
+    }
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    m = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) m = m > red[i] ? m : red[i];
+    s_ta = tensor_scale_from_amax(m);
+    if (blockIdx.x == 0 && tid == 0) {
+      args.a_rec->s_t = s_ta;
+      args.a_rec->amax_bits = m;
+    }
+  } else {
+    s_ta = args.a_rec->s_t;
+  }
+  const float scale = s_ta * args.w_rec->s_t;
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  using SM = Smem<BM, BN>;
+  PackedLoader<BM, FAST> la;
+  FusedALoader<BM, FAST> fa;
+  PackedLoader<BN, FAST> lw;
+  ScaleLoader<BM, BN, FAST, !FUSED> ls;
+
+  auto gload = [&](int kt) {
+    if (FUSED) fa.load((const uint16_t*)args.a_bf16, m0, M, K, kt);
+    else la.load(args.a_codes, m0, M, K, kt);
+    lw.load(args.w_codes, n0, N, K, kt);
+    ls.load(args.a_scales, args.w_scales, m0, n0, M, N, K, kt);
+  };
+  auto sstore = [&](uint8_t* stage) {
+    if (FUSED) fa.template quantize_store<BN>(stage, s_ta);
+    else la.store(stage + SM::kA);
+    lw.store(stage + SM::kW);
+    ls.store(stage);
+  };
+
+  gload(0);
+  sstore(smem);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    uint8_t* cur = smem + (kt & 1) * SM::kStage;
+    uint8_t* nxt = smem + ((kt + 1) & 1) * SM::kStage;
+    const bool more = kt + 1 < nk;
+    if (more) gload(kt + 1);
+    compute_stage<BM, BN>(cur, acc, wave_m, wave_n, li, lh);
+    if (more) sstore(nxt);
+    __syncthreads();
+  }
+  epilogue<BM, BN, OUT_F32>(acc, args.c, M, N, m0, n0, wave_m, wave_n, lane, scale);
+}
+
+// ------------------------------------------------------------------ host --
+
+constexpr int kMaxDevices = 64;
+
+template <int BM, int BN, bool FAST, bool OUT_F32, bool FUSED>
+static hipError_t launch_cfg(const GemmArgs& a0, int dev, hipStream_t stream) {
+  GemmArgs a = a0;
+  a.tiles_m = (a.M + BM - 1) / BM;
+  a.tiles_n = (a.N + BN - 1) / BN;
+  auto kern = gemm_nvfp4_kernel<BM, BN, FAST, OUT_F32, FUSED>;
+  constexpr int lds = Smem<BM, BN>::kTotal;
+  static bool attr_done[kMaxDevices] = {};  // benign race: the call is idempotent
+  if (dev < 0 || dev >= kMaxDevices || !attr_done[dev]) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices) attr_done[dev] = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(a.tiles_m * a.tiles_n), dim3(kThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, bool FUSED>
+static hipError_t dispatch_flags(const GemmArgs& a, bool out_f32, int d, hipStream_t s) {
+  const bool fast = (a.K % kBK) == 0;
+  if (fast) return out_f32 ? launch_cfg<BM, BN, true, true, FUSED>(a, d, s) : launch_cfg<BM, BN, true, false, FUSED>(a, d, s);
+  return out_f32 ? launch_cfg<BM, BN, false, true, FUSED>(a, d, s) : launch_cfg<BM, BN, false, false, FUSED>(a, d, s);
+}
+
+// Tile shape: the largest tile that still gives every CU work, judged by
+// how many workgroup "waves" the grid needs and how full the last one is.
+static int pick_tile(int64_t M, int64_t N, int num_cu) {
+  struct Cand { int bm, bn; double eff; };
+  const Cand cands[] = {{256, 256, 1.0}, {256, 128, 0.9}, {128, 256, 0.9}, {128, 128, 0.75}};
+  int best = 0;
+  double best_t = 1e300;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t tiles = ((M + cands[i].bm - 1) / cands[i].bm) * ((N + cands[i].bn - 1) / cands[i].bn);
+    const int64_t rounds = (tiles + num_cu - 1) / num_cu;
+    const double t = (double)rounds * cands[i].bm * cands[i].bn / cands[i].eff;
+    if (t < best_t * 0.999) { best_t = t; best = i; }
+  }
+  return best;
+}
+
+hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const mq_scale_rec* a_rec,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const mq_scale_rec* w_rec,
+                       void* c, int64_t M, int64_t N, int64_t K, bool out_f32, const DeviceInfo& dev,
+                       hipStream_t stream) {
+  GemmArgs a{};
+  a.a_codes = a_codes; a.a_scales = a_scales; a.a_rec = const_cast<mq_scale_rec*>(a_rec);
+  a.w_codes = w_codes; a.w_scales = w_scales; a.w_rec = w_rec;
+  a.c = c; a.M = (int)M; a.N = (int)N; a.K = (int)K;
+  switch (pick_tile(M, N, dev.num_cu)) {
+    case 0: return dispatch_flags<256, 256, false>(a, out_f32, dev.device, stream);
+    case 1: return dispatch_flags<256, 128, false>(a, out_f32, dev.device, stream);
+    case 2: return dispatch_flags<128, 256, false>(a, out_f32, dev.device, stream);
+    default: return dispatch_flags<128, 128, false>(a, out_f32, dev.device, stream);
+  }
+}
+
+hipError_t launch_gemm_fused(const void* a_bf16, mq_scale_rec* a_rec, bool a_given,
+                             const uint8_t* w_codes, const uint8_t* w_scales, const mq_scale_rec* w_rec,
+                             void* c, int64_t M, int64_t N, int64_t K, bool out_f32,
+                             const DeviceInfo& dev, hipStream_t stream) {
+  GemmArgs a{};
+  a.a_bf16 = a_bf16; a.a_rec = a_rec; a.a_given = a_given ? 1 : 0;
+  a.w_codes = w_codes; a.w_scales = w_scales; a.w_rec = w_rec;
+  a.c = c; a.M = (int)M; a.N = (int)N; a.K = (int)K;
+  // a tall A tile is re-quantized once per column tile: keep BM small and
+  // BN wide so the quantize work per MFMA stays low
+  return dispatch_flags<128, 256, true>(a, out_f32, dev.device, stream);
+}
+
+}  // namespace mq

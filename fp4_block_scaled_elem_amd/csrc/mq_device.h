@@ -1,0 +1,124 @@
+// mq_device.h - device-side helpers shared by the NVFP4 kernels (gfx950).
+//
+// NVFP4 as used by the prefill path of "Mix-Quant: Quantized Prefilling,
+// Precise Decoding for Agentic LLMs" (gist.science English explainer,
+// Technical Summary s.2, Hybrid Precision Strategy): a scale per 16-element
+// group plus a tensor-level scale, elements rounded to nearest.  Formats:
+// E2M1 elements, OCP E4M3 ("fn") group scales, binary32 tensor scale
+// s_t = amax / 2688.  Every floating-point step here is a single IEEE
+// binary32 operation (the library is built with -ffp-contract=off and with
+// correctly rounded division), so results are bit-reproducible.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mq {
+
+constexpr int kGroup = 16;          // elements per local (E4M3) scale
+constexpr float kTensorDiv = 2688.0f;  // 6 (E2M1 max) * 448 (E4M3 max)
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// 16-byte streaming load (data read once: do not keep it in the caches).
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// max over the two bf16 magnitudes of a word, as a 15-bit integer.  For
+// non-negative finite floats the bit pattern orders like the value.
+__device__ __forceinline__ uint32_t bf16x2_absmax_bits(uint32_t w) {
+  uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
+  return lo > hi ? lo : hi;
+}
+
+// Nearest E4M3 byte to rho >= 0, ties to even, saturating at 448 (0x7E),
+// subnormals (multiples of 2^-9) kept.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float rho) {
+  if (!(rho < 448.0f)) return 0x7Eu;         // also catches +inf
+  if (rho < 0.015625f) {                      // below 2^-6: fixed step 2^-9
+    float q = __builtin_rintf(rho * 512.0f);  // exact scaling, RNE
+    return (uint32_t)q;                       // 0..8; 8 is the code of 2^-6
+  }
+  uint32_t b = __float_as_uint(rho);
+  uint32_t e = (b >> 23) - 120u;              // biased E4M3 exponent, 1..15
+  uint32_t man = b & 0x7FFFFFu;
+  uint32_t keep = man >> 20;
+  uint32_t rest = man & 0xFFFFFu;
+  uint32_t up = (rest > 0x80000u) || (rest == 0x80000u && (keep & 1u));
+  return ((e << 3) | keep) + up;              // a carry moves into the exponent
+}
+
+// Exact binary32 value of an E4M3 byte (0x00..0x7E).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t s) {
+  uint32_t e = s >> 3, m = s & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+}
+
+// E2M1 magnitude index of |y|: nearest of {0,.5,1,1.5,2,3,4,6}, ties to the
+// even index, saturating; NaN -> 0.  Each comparison is one threshold, '>'
+// where the tie goes down to an even index and '>=' where it goes up.
+__device__ __forceinline__ uint32_t e2m1_mag(float y) {
+  float t = __builtin_fabsf(y);
+  return (uint32_t)(t > 0.25f) + (uint32_t)(t >= 0.75f) + (uint32_t)(t > 1.25f) +
+         (uint32_t)(t >= 1.75f) + (uint32_t)(t > 2.5f) + (uint32_t)(t >= 3.5f) +
+         (uint32_t)(t > 5.0f);
+}
+
+// Tensor scale from the absolute maximum's bit pattern.
+__device__ __forceinline__ float tensor_scale_from_amax(uint32_t amax_bits) {
+  float a = __uint_as_float(amax_bits);
+  return a > 0.0f ? a / kTensorDiv : 1.0f;
+}
+
+// Quantize one group of 16 bf16 values (8 words, element 2i in the low half
+// of word i).  Writes 8 code bytes (two words, even element in the low
+// nibble) and returns the E4M3 scale byte.
+__device__ __forceinline__ uint32_t quantize_group16(const uint32_t w[8], float s_t,
+                                                     uint32_t& codes_lo, uint32_t& codes_hi) {
+  uint32_t am = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t m = bf16x2_absmax_bits(w[i]);
+    am = am > m ? am : m;
+  }
+  float a = __uint_as_float(am << 16);
+  float rho = (a / 6.0f) / s_t;
+  uint32_t S = e4m3_from_f32(rho);
+  float d = e4m3_to_f32(S) * s_t;
+  float e = d > 0.0f ? 1.0f / d : 0.0f;
+  uint32_t c[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float x0 = bf16_lo(w[i]), x1 = bf16_hi(w[i]);
+    uint32_t c0 = e2m1_mag(x0 * e) | ((w[i] >> 12) & 8u);   // sign of x0 (bit 15)
+    uint32_t c1 = e2m1_mag(x1 * e) | ((w[i] >> 28) & 8u);   // sign of x1 (bit 31)
+    c[i >> 2] |= (c0 | (c1 << 4)) << ((i & 3) * 8);
+  }
+  codes_lo = c[0];
+  codes_hi = c[1];
+  return S;
+}
+
+// E4M3 byte -> binary16 bits (exact: every E4M3 value is a normal binary16).
+// Normal E4M3 (exponent field >= 1): same mantissa bits, exponent bias 15
+// instead of 7, i.e. (s << 7) + (8 << 10).  Subnormal E4M3 m * 2^-9 is built
+// from the small integer m with one exact multiply; no binary16 subnormal is
+// ever formed.
+__device__ __forceinline__ uint32_t e4m3_to_f16_bits(uint32_t s) {
+  if (s & 0x78u) return (s << 7) + 0x2000u;
+  _Float16 v = (_Float16)(float)s * (_Float16)0x1p-9f;
+  return (uint32_t)__builtin_bit_cast(uint16_t, v);
+}
+
+}  // namespace mq

@@ -1,0 +1,32 @@
+// mq_internal.h - host-side declarations shared by the library's sources.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mq.h"
+
+namespace mq {
+
+struct DeviceInfo {
+  int device = -1;
+  int num_cu = 0;
+  int ok = 0;  // gfx950
+};
+
+hipError_t launch_amax(const void* x_bf16, int64_t nelem, mq_scale_rec* rec, const DeviceInfo& dev,
+                       hipStream_t stream);
+hipError_t launch_quantize(const void* x_bf16, int64_t nelem, uint8_t* codes, uint8_t* scales,
+                           mq_scale_rec* rec, bool given, const DeviceInfo& dev, hipStream_t stream);
+hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const mq_scale_rec* a_rec,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const mq_scale_rec* w_rec,
+                       void* c, int64_t M, int64_t N, int64_t K, bool out_f32, const DeviceInfo& dev,
+                       hipStream_t stream);
+hipError_t launch_gemm_fused(const void* a_bf16, mq_scale_rec* a_rec, bool a_given,
+                             const uint8_t* w_codes, const uint8_t* w_scales, const mq_scale_rec* w_rec,
+                             void* c, int64_t M, int64_t N, int64_t K, bool out_f32,
+                             const DeviceInfo& dev, hipStream_t stream);
+hipError_t launch_gemv(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
+                       const DeviceInfo& dev, hipStream_t stream);
+
+}  // namespace mq

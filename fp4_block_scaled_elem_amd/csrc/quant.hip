@@ -1,0 +1,162 @@
+// quant.hip - dynamic activation quantization to NVFP4 (gfx950).
+//
+// Two passes, because the tensor-level scale of NVFP4 (gist.science English
+// explainer of "Mix-Quant: Quantized Prefilling, Precise Decoding for Agentic
+// LLMs", Technical Summary s.2, Hybrid Precision Strategy) depends on the
+// absolute maximum of the whole input, which must be known before any code
+// can be emitted:
+//   1. amax_kernel: streaming max|x| over the bf16 input; each workgroup
+//      writes one partial maximum into the scale record (no atomics, no
+//      pre-zeroed memory needed).
+//   2. quantize_kernel: every workgroup reduces the partials (at most a few
+//      KB, L2-resident), derives s_t, then encodes 16-element groups.  One
+//      lane owns 8 consecutive elements (one 16-byte load, fully coalesced);
+//      the two lanes of a group exchange their half maxima with one
+//      cross-lane swap.
+// Both passes are HBM-bound: 2 bytes read per element for the amax, 2 read
+// plus 0.5625 written per element for the encode.
+#include "mq_device.h"
+#include "mq_internal.h"
+
+namespace mq {
+
+constexpr int kQThreads = 256;
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = __shfl_xor(v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t uint4_absmax(uint4 v) {
+  uint32_t a = bf16x2_absmax_bits(v.x), b = bf16x2_absmax_bits(v.y);
+  uint32_t c = bf16x2_absmax_bits(v.z), d = bf16x2_absmax_bits(v.w);
+  a = a > b ? a : b;
+  c = c > d ? c : d;
+  return a > c ? a : c;
+}
+
+// Block-wide max of a per-thread value; every thread gets the result.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* sh) {
+  v = wave_max_u32(v);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  uint32_t r = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r = r > sh[i] ? r : sh[i];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kQThreads) void amax_kernel(const uint4* __restrict__ x, int64_t n16,
+                                                         mq_scale_rec* __restrict__ rec) {
+  __shared__ uint32_t sh[kQThreads / 64];
+  const int64_t stride = (int64_t)gridDim.x * kQThreads;
+  int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
+  uint32_t m0 = 0, m1 = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    uint4 a = ld_stream(&x[i]);
+    uint4 b = ld_stream(&x[i + stride]);
+    uint4 c = ld_stream(&x[i + 2 * stride]);
+    uint4 d = ld_stream(&x[i + 3 * stride]);
+    uint32_t ma = uint4_absmax(a), mb = uint4_absmax(b), mc = uint4_absmax(c), md = uint4_absmax(d);
+    ma = ma > mb ? ma : mb;
+    mc = mc > md ? mc : md;
+    m0 = m0 > ma ? m0 : ma;
+    m1 = m1 > mc ? m1 : mc;
+  }
+  for (; i < n16; i += stride) {
+    uint32_t ma = uint4_absmax(x[i]);
+    m0 = m0 > ma ? m0 : ma;
+  }
+  uint32_t m = block_max_u32(m0 > m1 ? m0 : m1, sh);
+  if (threadIdx.x == 0) {
+    rec->part[blockIdx.x] = m << 16;  // binary32 bits of the bf16 magnitude
+    if (blockIdx.x == 0) rec->nparts = gridDim.x;
+  }
+}
+
+// Reduce the partial maxima of a record; every thread gets amax's bits.
+__device__ __forceinline__ uint32_t reduce_parts(const mq_scale_rec* __restrict__ rec, uint32_t* sh) {
+  const uint32_t n = rec->nparts;
+  uint32_t m = 0;
+  for (uint32_t j = threadIdx.x; j < n; j += blockDim.x) {
+    uint32_t v = rec->part[j];
+    m = m > v ? m : v;
+  }
+  return block_max_u32(m, sh);
+}
+
+__global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __restrict__ x, int64_t nhalf,
+                                                             uint32_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales,
+                                                             mq_scale_rec* __restrict__ rec, int given) {
+  __shared__ uint32_t sh[kQThreads / 64];
+  float s_t;
+  if (given) {
+    s_t = rec->s_t;
+  } else {
+    uint32_t amax = reduce_parts(rec, sh);
+    s_t = tensor_scale_from_amax(amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      rec->s_t = s_t;
+      rec->amax_bits = amax;
+    }
+  }
+  const int64_t stride = (int64_t)gridDim.x * kQThreads;  // a multiple of 2
+  // nhalf and stride are even and a pair starts on an even index, so both
+  // lanes of a group enter and leave the loop together
+  for (int64_t h = (int64_t)blockIdx.x * kQThreads + threadIdx.x; h < nhalf; h += stride) {
+    uint4 v = ld_stream(&x[h]);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t am = uint4_absmax(v);
+    uint32_t other = __shfl_xor(am, 1, 64);
+    am = am > other ? am : other;
+    float a = __uint_as_float(am << 16);
+    float rho = (a / 6.0f) / s_t;
+    uint32_t S = e4m3_from_f32(rho);
+    float d = e4m3_to_f32(S) * s_t;
+    float e = d > 0.0f ? 1.0f / d : 0.0f;
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x0 = bf16_lo(w[i]), x1 = bf16_hi(w[i]);
+      uint32_t c0 = e2m1_mag(x0 * e) | ((w[i] >> 12) & 8u);
+      uint32_t c1 = e2m1_mag(x1 * e) | ((w[i] >> 28) & 8u);
+      c |= (c0 | (c1 << 4)) << (i * 8);
+    }
+    codes[h] = c;
+    if ((h & 1) == 0) scales[h >> 1] = (uint8_t)S;
+  }
+}
+
+static int grid_for(int64_t items, int threads, int max_blocks) {
+  int64_t b = (items + threads - 1) / threads;
+  if (b > max_blocks) b = max_blocks;
+  if (b < 1) b = 1;
+  return (int)b;
+}
+
+hipError_t launch_amax(const void* x_bf16, int64_t nelem, mq_scale_rec* rec, const DeviceInfo& dev,
+                       hipStream_t stream) {
+  const int64_t n16 = nelem / 8;
+  int blocks = grid_for((n16 + 3) / 4, kQThreads, dev.num_cu * 4);
+  if (blocks > MQ_AMAX_PARTS) blocks = MQ_AMAX_PARTS;
+  hipLaunchKernelGGL(amax_kernel, dim3(blocks), dim3(kQThreads), 0, stream,
+                     (const uint4*)x_bf16, n16, rec);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* x_bf16, int64_t nelem, uint8_t* codes, uint8_t* scales,
+                           mq_scale_rec* rec, bool given, const DeviceInfo& dev, hipStream_t stream) {
+  const int64_t nhalf = nelem / 8;  // 8 elements per lane, two lanes per group
+  int blocks = grid_for(nhalf, kQThreads, dev.num_cu * 8);
+  hipLaunchKernelGGL(quantize_kernel, dim3(blocks), dim3(kQThreads), 0, stream,
+                     (const uint4*)x_bf16, nhalf, (uint32_t*)codes, scales, rec, given ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace mq

@@ -1,0 +1,143 @@
+"""The C ABI: libmq.so loads, exports every function include/mq.h declares,
+and rejects bad arguments with the documented status before any HIP call
+(CPU; no kernel is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp4_block_scaled_elem_amd as mq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mq.h")
+
+
+def _header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mq_[a-z0-9_]+)\s*\(", src)))
+
+
+def _header_defines():
+    out = {}
+    for m in re.finditer(r"#define\s+(MQ_[A-Z0-9_]+)\s+(\d+)u?", open(HEADER).read()):
+        out[m.group(1)] = int(m.group(2))
+    return out
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mq.LIB_PATH):
+        pytest.skip("libmq.so not built")
+    return mq.lib()
+
+
+def test_header_declares_the_three_entry_points():
+    fns = _header_functions()
+    for f in ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemv_bf16_decode"):
+        assert f in fns
+
+
+def test_every_declared_symbol_is_exported(L):
+    for f in _header_functions():
+        assert hasattr(L, f), f
+    assert set(_header_functions()) <= set(mq.EXPORTS)
+
+
+def test_python_constants_match_header():
+    d = _header_defines()
+    for k, v in d.items():
+        assert getattr(mq, k) == v, k
+    assert mq.REC_BYTES == 4096
+
+
+def test_status_strings(L):
+    for code, name in [(0, "MQ_OK"), (1, "MQ_ERR_INVALID"), (2, "MQ_ERR_SHAPE"), (3, "MQ_ERR_ALIGN"),
+                       (4, "MQ_ERR_DEVICE"), (5, "MQ_ERR_LAUNCH")]:
+        assert mq.status_str(code) == name
+    assert L.mq_version().decode().startswith("mq ")
+
+
+# fake, never dereferenced device addresses (checks happen first)
+P16 = 0x10000
+P8 = 0x10008
+P1 = 0x10001
+
+
+def _q(codes, scales, rec):
+    return ctypes.byref(mq._NVFP4C(codes, scales, rec))
+
+
+def test_quantize_argument_errors(L):
+    f = L.mq_quantize_nvfp4
+    assert f(None, 4, 16, _q(P16, P16, P16), 0, None) == mq.MQ_ERR_INVALID
+    assert f(P16, 4, 16, None, 0, None) == mq.MQ_ERR_INVALID
+    assert f(P16, 4, 16, _q(None, P16, P16), 0, None) == mq.MQ_ERR_INVALID
+    assert f(P16, 4, 16, _q(P16, P16, P16), 8, None) == mq.MQ_ERR_INVALID
+    assert "flags" in mq.last_error()
+    assert f(P16, 0, 16, _q(P16, P16, P16), 0, None) == mq.MQ_ERR_SHAPE
+    assert f(P16, 4, 24, _q(P16, P16, P16), 0, None) == mq.MQ_ERR_SHAPE
+    assert f(P16, 4, -16, _q(P16, P16, P16), 0, None) == mq.MQ_ERR_SHAPE
+    assert f(P16, 1 << 31, 16, _q(P16, P16, P16), 0, None) == mq.MQ_ERR_SHAPE
+    assert f(P8, 4, 16, _q(P16, P16, P16), 0, None) == mq.MQ_ERR_ALIGN
+    assert f(P16, 4, 16, _q(P8, P16, P16), 0, None) == mq.MQ_ERR_ALIGN
+    assert f(P16, 4, 16, _q(P16, P1, P16), 0, None) == mq.MQ_ERR_ALIGN
+    assert f(P16, 4, 16, _q(P16, P16, P8), 0, None) == mq.MQ_ERR_ALIGN
+
+
+def test_gemm_argument_errors(L):
+    f = L.mq_gemm_nvfp4_prefill
+    a, w = _q(P16, P16, P16), _q(P16, P16, P16)
+    assert f(None, None, w, P16, 4, 4, 16, 0, None) == mq.MQ_ERR_INVALID
+    assert f(a, None, None, P16, 4, 4, 16, 0, None) == mq.MQ_ERR_INVALID
+    assert f(a, None, w, None, 4, 4, 16, 0, None) == mq.MQ_ERR_INVALID
+    assert f(a, None, w, P16, 4, 4, 16, 64, None) == mq.MQ_ERR_INVALID
+    assert f(a, None, w, P16, 4, 4, 16, mq.MQ_SCALE_GIVEN, None) == mq.MQ_ERR_INVALID
+    assert f(a, P16, w, P16, 4, 4, 16, 0, None) == mq.MQ_ERR_INVALID             # a_bf16 without fused
+    assert f(a, None, w, P16, 4, 4, 16, mq.MQ_A_FUSED_BF16, None) == mq.MQ_ERR_INVALID
+    assert f(_q(None, None, P16), None, w, P16, 4, 4, 16, 0, None) == mq.MQ_ERR_INVALID
+    assert f(a, None, w, P16, 4, 4, 40, 0, None) == mq.MQ_ERR_SHAPE
+    assert f(a, None, w, P16, 0, 4, 16, 0, None) == mq.MQ_ERR_SHAPE
+    assert f(a, None, w, P16, 4, 0, 16, 0, None) == mq.MQ_ERR_SHAPE
+    assert f(a, None, w, P16, 4, 4, 0, 0, None) == mq.MQ_ERR_SHAPE
+    assert f(a, None, w, P8, 4, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
+    assert f(_q(P8, P16, P16), None, w, P16, 4, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
+    assert f(a, None, _q(P16, P1, P16), P16, 4, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
+    assert f(_q(None, None, P16), P8, w, P16, 4, 4, 16, mq.MQ_A_FUSED_BF16, None) == mq.MQ_ERR_ALIGN
+
+
+def test_gemv_argument_errors(L):
+    f = L.mq_gemv_bf16_decode
+    assert f(None, P16, P16, 1, 4, 16, 0, None) == mq.MQ_ERR_INVALID
+    assert f(P16, P16, P16, 1, 4, 16, 1, None) == mq.MQ_ERR_INVALID
+    assert f(P16, P16, P16, 0, 4, 16, 0, None) == mq.MQ_ERR_SHAPE
+    assert f(P16, P16, P16, 33, 4, 16, 0, None) == mq.MQ_ERR_SHAPE
+    assert f(P16, P16, P16, 1, 4, 17, 0, None) == mq.MQ_ERR_SHAPE
+    assert f(P16, P16, P16, 1, 0, 16, 0, None) == mq.MQ_ERR_SHAPE
+    assert f(P8, P16, P16, 1, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
+    assert f(P16, P16, P1, 1, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
+
+
+def _no_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="valid fake pointers would be launched on a real GPU")
+def test_valid_arguments_without_a_gpu_report_device_error(L):
+    assert L.mq_quantize_nvfp4(P16, 4, 16, _q(P16, P16, P16), 0, None) == mq.MQ_ERR_DEVICE
+    assert L.mq_gemm_nvfp4_prefill(_q(P16, P16, P16), None, _q(P16, P16, P16), P16, 4, 4, 16, 0,
+                                   None) == mq.MQ_ERR_DEVICE
+    assert L.mq_gemv_bf16_decode(P16, P16, P16, 1, 4, 16, 0, None) == mq.MQ_ERR_DEVICE
+    assert mq.last_error()
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(mq, "_lib", None)
+    monkeypatch.setattr(mq, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(mq.LibraryNotBuilt):
+        mq.lib()
