@@ -191,8 +191,11 @@ struct FusedALoader {
 // --------------------------------------------------------------- compute --
 
 // 8 E2M1 codes (one dword) times the group scale -> 8 exact binary16 values.
-__device__ __forceinline__ half8_t dequant8(uint32_t codes, uint32_t sigma_pair) {
-  const half2_t s = __builtin_bit_cast(half2_t, sigma_pair);
+// The hardware conversion yields the E2M1 values themselves (its scale
+// operand only applies a power of two, so it is left at 1); one packed
+// binary16 multiply per pair applies the E4M3 group scale exactly.
+__device__ __forceinline__ half8_t dequant8(uint32_t codes, _Float16 sigma) {
+  const half2_t s = {sigma, sigma};
   half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s;
   half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s;
   half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s;
@@ -203,11 +206,23 @@ __device__ __forceinline__ half8_t dequant8(uint32_t codes, uint32_t sigma_pair)
   return r;
 }
 
-__device__ __forceinline__ uint32_t sigma_pair_from(uint32_t scale_dword, int byte) {
-  uint32_t h = e4m3_to_f16_bits((scale_dword >> (8 * byte)) & 0xFFu);
-  return h | (h << 16);
+// The two E4M3 scales a lane needs from one scale dword (bytes 2h and 2h+1)
+// as a binary16 pair, without branches: the bit pattern s<<7 read as
+// binary16 is value(s) * 2^-8 for every E4M3 byte, normal or subnormal (the
+// formats share their subnormal layout and differ by 8 in exponent bias), and
+// one exact packed multiply by 256 restores the value (binary16 subnormals
+// are kept: the kernels run with denormals enabled).
+__device__ __forceinline__ half2_t sigma_pair(uint32_t scale_dword, uint32_t sel) {
+  typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+  const uint32_t b = __builtin_amdgcn_perm(0u, scale_dword, sel);  // (s_lo << 8) | (s_hi << 24)
+  const u16x2_t h = __builtin_bit_cast(u16x2_t, b) >> (uint16_t)1;
+  return __builtin_bit_cast(half2_t, h) * half2_t{(_Float16)256.0f, (_Float16)256.0f};
 }
 
+// One 128-deep stage for one wave: TM x TN fragments of 32x32, eight
+// K16 steps.  Step s uses, for a lane (i, h), the dword s&3 of its 16-byte
+// read of sub-chunk s>>2, i.e. group 4*(s>>2) + 2h + ((s&3)>>1).  Operands of
+// step s+1 are dequantized while the MFMAs of step s run.
 template <int BM, int BN>
 __device__ __forceinline__ void compute_stage(const uint8_t* stage, f32x16_t (&acc)[BM / 64][BN / 64],
                                               int wave_m, int wave_n, int li, int lh) {
@@ -216,37 +231,55 @@ __device__ __forceinline__ void compute_stage(const uint8_t* stage, f32x16_t (&a
   const uint8_t* lw = stage + Smem<BM, BN>::kW + (wave_n + li) * kRowStride + lh * 16;
   const uint8_t* las = stage + Smem<BM, BN>::kAs + (wave_m + li) * kScaleStride;
   const uint8_t* lws = stage + Smem<BM, BN>::kWs + (wave_n + li) * kScaleStride;
+  const uint32_t sel = lh ? 0x030C020Cu : 0x010C000Cu;
+
+  u32x4_t ra[2][TM], rw[2][TN];
+  u32x2_t sa[TM], sw[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    sa[i] = *(const u32x2_t*)(las + i * 32 * kScaleStride);
+    ra[0][i] = *(const u32x4_t*)(la + i * 32 * kRowStride);
+    ra[1][i] = *(const u32x4_t*)(la + i * 32 * kRowStride + 32);
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    sw[j] = *(const u32x2_t*)(lws + j * 32 * kScaleStride);
+    rw[0][j] = *(const u32x4_t*)(lw + j * 32 * kRowStride);
+    rw[1][j] = *(const u32x4_t*)(lw + j * 32 * kRowStride + 32);
+  }
+  half2_t pa[2][TM], pw[2][TN];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    u32x4_t ar[TM], wr[TN];
-    uint32_t as[TM], ws[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      ar[i] = *(const u32x4_t*)(la + i * 32 * kRowStride + t * 32);
-      as[i] = *(const uint32_t*)(las + i * 32 * kScaleStride + t * 4);
-    }
+    for (int i = 0; i < TM; ++i) pa[t][i] = sigma_pair(sa[i][t], sel);
 #pragma unroll
-    for (int i = 0; i < TN; ++i) {
-      wr[i] = *(const u32x4_t*)(lw + i * 32 * kRowStride + t * 32);
-      ws[i] = *(const uint32_t*)(lws + i * 32 * kScaleStride + t * 4);
-    }
+    for (int j = 0; j < TN; ++j) pw[t][j] = sigma_pair(sw[j][t], sel);
+  }
+
+  half8_t oa[2][TM], ow[2][TN];
+  auto dequant_step = [&](int s, int buf) {
+    const int t = s >> 2, q = s & 3;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int sb = 2 * lh + (q >> 1);  // scale byte of this lane's group
-      half8_t ao[TM], wo[TN];
+    for (int i = 0; i < TM; ++i) oa[buf][i] = dequant8(ra[t][i][q], pa[t][i][q >> 1]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        ao[i] = dequant8(ar[i][q], sigma_pair_from(as[i], sb));
+    for (int j = 0; j < TN; ++j) ow[buf][j] = dequant8(rw[t][j][q], pw[t][j][q >> 1]);
+  };
+  dequant_step(0, 0);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    if (s < 7) dequant_step(s + 1, (s + 1) & 1);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa[s & 1][i], ow[s & 1][j], acc[i][j], 0, 0, 0);
+    if (s < 7) {
+      // interleave: one MFMA, then a slice of the next step's dequant VALU
+#pragma unroll
+      for (int k = 0; k < TM * TN; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, (8 * (TM + TN) + TM * TN - 1) / (TM * TN), 0);
       }
-#pragma unroll
-      for (int i = 0; i < TN; ++i) {
-        wo[i] = dequant8(wr[i][q], sigma_pair_from(ws[i], sb));
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ao[i], wo[j], acc[i][j], 0, 0, 0);
     }
   }
 }
