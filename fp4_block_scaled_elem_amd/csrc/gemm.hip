@@ -15,14 +15,17 @@
 // epilogue.  The result equals the float64 product of the dequantized
 // operands up to binary32 accumulation and the final bf16 rounding.
 //
-// Data flow per workgroup (256 threads = 4 waves in a 2x2 grid; tile BM x BN;
-// K advanced 128 elements = 8 groups per stage):
-//   HBM --16B loads--> registers --> LDS (packed codes + scale bytes,
-//   double-buffered, rows padded to avoid bank conflicts)
-//   LDS --ds_read_b128--> registers: one dword = 8 codes of one group
+// Data flow per workgroup (256 threads = 4 waves in a 2x2 grid, one wave per
+// SIMD; tile BM x BN; K advanced 128 elements = 8 groups per stage):
+//   HBM --16-byte loads--> registers --> LDS ring of three stages (packed
+//   codes + scale bytes)
+//   LDS --8-byte reads--> registers: two dwords = codes of two K16 steps
 //   cvt fp4->f16 (hardware) * sigma (packed f16 multiply) -> MFMA operand.
-// The K order inside a stage is permuted consistently for A and W so that a
-// lane's 16-byte LDS read feeds four consecutive MFMAs; the sum is unchanged.
+// Every wave runs a register pipeline: the operands of step s+1 are
+// dequantized while the MFMAs of step s run, and the next stage's codes,
+// scales and first operands are prepared inside the current stage, so the
+// MFMA stream only pauses at the one barrier per stage.  The K order inside
+// a stage is permuted identically for A and W (the sum is unchanged).
 #include "mq_device.h"
 #include "mq_internal.h"
 
@@ -31,7 +34,9 @@ namespace mq {
 constexpr int kThreads = 256;
 constexpr int kBK = 128;            // K elements per stage
 constexpr int kRowBytes = kBK / 2;  // packed code bytes per row per stage
-constexpr int kRowStride = 80;      // LDS bytes per code row (64 + 16 pad)
+// LDS bytes per code row: 64 + 8 pad.  With 18 dwords per row, the 8-byte
+// reads of 16 consecutive rows hit 32 distinct banks.
+constexpr int kRowStride = 72;
 constexpr int kScaleStride = 8;     // LDS bytes per scale row (8 groups)
 
 struct GemmArgs {
@@ -55,8 +60,15 @@ struct Smem {
   static constexpr int kAs = kW + BN * kRowStride;
   static constexpr int kWs = kAs + BM * kScaleStride;
   static constexpr int kStage = kWs + BN * kScaleStride;
-  static constexpr int kTotal = 2 * kStage;
+  static constexpr int kTotal = 3 * kStage;  // ring of three stages
 };
+
+// Scale bytes of one row and stage, g0..g7, are kept in LDS as
+// [g0 g1 g4 g5 | g2 g3 g6 g7]: the lane of half h (K offsets 32h..32h+31 of
+// each 64-element sub-chunk) then finds all four of its scales in dword h.
+__device__ __forceinline__ u32x2_t permute_scales(u32x2_t g) {
+  return u32x2_t{__builtin_amdgcn_perm(g[1], g[0], 0x05040100u), __builtin_amdgcn_perm(g[1], g[0], 0x07060302u)};
+}
 
 // ---------------------------------------------------------------- loaders --
 
@@ -94,7 +106,9 @@ struct PackedLoader {
     for (int j = 0; j < kChunks; ++j) {
       const int c = tid + kThreads * j;
       const int row = c >> 2, col = c & 3;
-      *(u32x4_t*)(lds + row * kRowStride + col * 16) = code[j];
+      uint8_t* p = lds + row * kRowStride + col * 16;
+      *(u32x2_t*)p = u32x2_t{code[j][0], code[j][1]};
+      *(u32x2_t*)(p + 8) = u32x2_t{code[j][2], code[j][3]};
     }
   }
 };
@@ -106,6 +120,7 @@ struct ScaleLoader {
   static constexpr int kA = WITH_A ? BM : 0;
   static constexpr int kRows = kA + BN;
   static constexpr int kPer = (kRows + kThreads - 1) / kThreads;
+  static constexpr bool kFull = kRows % kThreads == 0;
   u32x2_t v[kPer];
 
   __device__ __forceinline__ void load(const uint8_t* __restrict__ as, const uint8_t* __restrict__ ws,
@@ -115,7 +130,7 @@ struct ScaleLoader {
     for (int j = 0; j < kPer; ++j) {
       const int r = threadIdx.x + kThreads * j;
       v[j] = u32x2_t{0u, 0u};
-      if (r < kRows) {
+      if (kFull || r < kRows) {
         const uint8_t* base;
         int row;
         if (r < kA) { row = m0 + r; row = row < M ? row : M - 1; base = as; }
@@ -137,10 +152,10 @@ struct ScaleLoader {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int r = threadIdx.x + kThreads * j;
-      if (r < kRows) {
+      if (kFull || r < kRows) {
         uint8_t* p = r < kA ? stage + Smem<BM, BN>::kAs + r * kScaleStride
                             : stage + Smem<BM, BN>::kWs + (r - kA) * kScaleStride;
-        *(u32x2_t*)p = v[j];
+        *(u32x2_t*)p = permute_scales(v[j]);
       }
     }
   }
@@ -172,6 +187,8 @@ struct FusedALoader {
       }
     }
   }
+  // Quantize the loaded groups into the stage's A codes; each scale byte goes
+  // to its permuted position in the row.
   template <int BN>
   __device__ __forceinline__ void quantize_store(uint8_t* stage, float s_t) const {
 #pragma unroll
@@ -183,7 +200,9 @@ struct FusedALoader {
       uint32_t lo, hi;
       uint32_t S = quantize_group16(w, s_t, lo, hi);
       *(u32x2_t*)(stage + Smem<BM, BN>::kA + row * kRowStride + grp * 8) = u32x2_t{lo, hi};
-      stage[Smem<BM, BN>::kAs + row * kScaleStride + grp] = (uint8_t)S;
+      // [g0 g1 g4 g5 | g2 g3 g6 g7]: bit 1 and bit 2 of the group index swap
+      const int pos = (grp & 1) | ((grp & 4) >> 1) | ((grp & 2) << 1);
+      stage[Smem<BM, BN>::kAs + row * kScaleStride + pos] = (uint8_t)S;
     }
   }
 };
@@ -206,12 +225,12 @@ __device__ __forceinline__ half8_t dequant8(uint32_t codes, _Float16 sigma) {
   return r;
 }
 
-// The two E4M3 scales a lane needs from one scale dword (bytes 2h and 2h+1)
-// as a binary16 pair, without branches: the bit pattern s<<7 read as
-// binary16 is value(s) * 2^-8 for every E4M3 byte, normal or subnormal (the
-// formats share their subnormal layout and differ by 8 in exponent bias), and
-// one exact packed multiply by 256 restores the value (binary16 subnormals
-// are kept: the kernels run with denormals enabled).
+// Two E4M3 scale bytes of a dword (bytes 0,1 or 2,3 by `sel`) as a binary16
+// pair, without branches: the bit pattern s<<7 read as binary16 is
+// value(s) * 2^-8 for every E4M3 byte, normal or subnormal (the formats share
+// their subnormal layout and differ by 8 in exponent bias), and one exact
+// packed multiply by 256 restores the value (binary16 subnormals are kept:
+// the kernels run with denormals enabled).
 __device__ __forceinline__ half2_t sigma_pair(uint32_t scale_dword, uint32_t sel) {
   typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
   const uint32_t b = __builtin_amdgcn_perm(0u, scale_dword, sel);  // (s_lo << 8) | (s_hi << 24)
@@ -219,69 +238,107 @@ __device__ __forceinline__ half2_t sigma_pair(uint32_t scale_dword, uint32_t sel
   return __builtin_bit_cast(half2_t, h) * half2_t{(_Float16)256.0f, (_Float16)256.0f};
 }
 
-// One 128-deep stage for one wave: TM x TN fragments of 32x32, eight
-// K16 steps.  Step s uses, for a lane (i, h), the dword s&3 of its 16-byte
-// read of sub-chunk s>>2, i.e. group 4*(s>>2) + 2h + ((s&3)>>1).  Operands of
-// step s+1 are dequantized while the MFMAs of step s run.
+// Per-wave register pipeline over 128-deep stages (TM x TN fragments of
+// 32x32, eight K16 steps per stage).  A lane (i, h) handles, in step s, the
+// eight codes at byte 32*(s>>2) + 16h + 4*(s&3) of its fragment row, i.e.
+// group 4*(s>>2) + 2h + ((s&3)>>1).  Codes come from LDS two steps at a time
+// (8 bytes); the four scales of a lane and stage come in one dword.
 template <int BM, int BN>
-__device__ __forceinline__ void compute_stage(const uint8_t* stage, f32x16_t (&acc)[BM / 64][BN / 64],
-                                              int wave_m, int wave_n, int li, int lh) {
-  constexpr int TM = BM / 64, TN = BN / 64;
-  const uint8_t* la = stage + Smem<BM, BN>::kA + (wave_m + li) * kRowStride + lh * 16;
-  const uint8_t* lw = stage + Smem<BM, BN>::kW + (wave_n + li) * kRowStride + lh * 16;
-  const uint8_t* las = stage + Smem<BM, BN>::kAs + (wave_m + li) * kScaleStride;
-  const uint8_t* lws = stage + Smem<BM, BN>::kWs + (wave_n + li) * kScaleStride;
-  const uint32_t sel = lh ? 0x030C020Cu : 0x010C000Cu;
+struct WavePipe {
+  static constexpr int TM = BM / 64, TN = BN / 64;
+  u32x2_t ca[2][TM], cw[2][TN];   // codes of a step pair, double-buffered
+  uint32_t sa[TM], sw[TN];        // the lane's four scale bytes per fragment
+  half2_t pa[2][TM], pw[2][TN];   // sigma pairs, sub-chunks 0 and 1
+  half8_t oa[2][TM], ow[2][TN];   // dequantized operands, double-buffered
+  int a_off, w_off, as_off, ws_off;
 
-  u32x4_t ra[2][TM], rw[2][TN];
-  u32x2_t sa[TM], sw[TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    sa[i] = *(const u32x2_t*)(las + i * 32 * kScaleStride);
-    ra[0][i] = *(const u32x4_t*)(la + i * 32 * kRowStride);
-    ra[1][i] = *(const u32x4_t*)(la + i * 32 * kRowStride + 32);
+  __device__ __forceinline__ void init(int wave_m, int wave_n, int li, int lh) {
+    a_off = Smem<BM, BN>::kA + (wave_m + li) * kRowStride + lh * 16;
+    w_off = Smem<BM, BN>::kW + (wave_n + li) * kRowStride + lh * 16;
+    as_off = Smem<BM, BN>::kAs + (wave_m + li) * kScaleStride + lh * 4;
+    ws_off = Smem<BM, BN>::kWs + (wave_n + li) * kScaleStride + lh * 4;
   }
+  // codes of step pair P (steps 2P, 2P+1) into buffer B
+  template <int P, int B>
+  __device__ __forceinline__ void read_pair(const uint8_t* stage) {
+    constexpr int off = 32 * (P >> 1) + 8 * (P & 1);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    sw[j] = *(const u32x2_t*)(lws + j * 32 * kScaleStride);
-    rw[0][j] = *(const u32x4_t*)(lw + j * 32 * kRowStride);
-    rw[1][j] = *(const u32x4_t*)(lw + j * 32 * kRowStride + 32);
+    for (int i = 0; i < TM; ++i) ca[B][i] = *(const u32x2_t*)(stage + a_off + i * 32 * kRowStride + off);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) cw[B][j] = *(const u32x2_t*)(stage + w_off + j * 32 * kRowStride + off);
   }
-  half2_t pa[2][TM], pw[2][TN];
+  __device__ __forceinline__ void read_scales(const uint8_t* stage) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+    for (int i = 0; i < TM; ++i) sa[i] = *(const uint32_t*)(stage + as_off + i * 32 * kScaleStride);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) pa[t][i] = sigma_pair(sa[i][t], sel);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) pw[t][j] = sigma_pair(sw[j][t], sel);
+    for (int j = 0; j < TN; ++j) sw[j] = *(const uint32_t*)(stage + ws_off + j * 32 * kScaleStride);
   }
-
-  half8_t oa[2][TM], ow[2][TN];
-  auto dequant_step = [&](int s, int buf) {
-    const int t = s >> 2, q = s & 3;
+  __device__ __forceinline__ void sigmas() {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) oa[buf][i] = dequant8(ra[t][i][q], pa[t][i][q >> 1]);
+    for (int i = 0; i < TM; ++i) {
+      pa[0][i] = sigma_pair(sa[i], 0x010C000Cu);
+      pa[1][i] = sigma_pair(sa[i], 0x030C020Cu);
+    }
 #pragma unroll
-    for (int j = 0; j < TN; ++j) ow[buf][j] = dequant8(rw[t][j][q], pw[t][j][q >> 1]);
-  };
-  dequant_step(0, 0);
+    for (int j = 0; j < TN; ++j) {
+      pw[0][j] = sigma_pair(sw[j], 0x010C000Cu);
+      pw[1][j] = sigma_pair(sw[j], 0x030C020Cu);
+    }
+  }
+  // operands of step S into operand buffer B
+  template <int S, int B>
+  __device__ __forceinline__ void dequant() {
+    constexpr int cb = (S >> 1) & 1, w = S & 1, t = S >> 2, g = (S & 3) >> 1;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    if (s < 7) dequant_step(s + 1, (s + 1) & 1);
+    for (int i = 0; i < TM; ++i) oa[B][i] = dequant8(ca[cb][i][w], pa[t][i][g]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) ow[B][j] = dequant8(cw[cb][j][w], pw[t][j][g]);
+  }
+  template <int B>
+  __device__ __forceinline__ void mfma(f32x16_t (&acc)[TM][TN]) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa[s & 1][i], ow[s & 1][j], acc[i][j], 0, 0, 0);
-    if (s < 7) {
-      // interleave: one MFMA, then a slice of the next step's dequant VALU
-#pragma unroll
-      for (int k = 0; k < TM * TN; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, (8 * (TM + TN) + TM * TN - 1) / (TM * TN), 0);
-      }
-    }
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa[B][i], ow[B][j], acc[i][j], 0, 0, 0);
   }
+};
+
+// Interleave the MFMAs of one step with the VALU issued for the next one:
+// one MFMA, then its share of the dequantization.  The sched_barrier at the
+// end keeps each step a scheduling region of its own, so the groups cannot
+// pull work from later steps (which would stretch register live ranges).
+template <int NMFMA, int NVALU>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int k = 0; k < NMFMA; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, (NVALU + NMFMA - 1) / NMFMA, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Step S of a stage: LDS reads for later steps, dequantization of step S+1
+// (or of the next stage's step 0), the MFMAs of step S, and one phase of the
+// global->LDS fill of the stage after next.
+template <int S, int BM, int BN, typename Fill>
+__device__ __forceinline__ void run_step(WavePipe<BM, BN>& p, f32x16_t (&acc)[BM / 64][BN / 64],
+                                         const uint8_t* cur, const uint8_t* nxt, Fill& fill) {
+  constexpr int TM = BM / 64, TN = BN / 64, NM = TM * TN, ND = 8 * (TM + TN);
+  if (S == 0) p.template read_pair<1, 1>(cur);
+  if (S == 2) p.template read_pair<2, 0>(cur);
+  if (S == 4) p.template read_pair<3, 1>(cur);
+  if (S == 4) p.read_scales(nxt);
+  if (S == 6) p.template read_pair<0, 0>(nxt);
+  if (S == 7) p.sigmas();  // the next stage's; this stage's were last used in step 6
+  if (S < 7) p.template dequant<(S + 1) & 7, (S + 1) & 1>();
+  else p.template dequant<0, 0>();
+  p.template mfma<S & 1>(acc);
+  interleave<NM, ND + (S == 7 ? 6 * (TM + TN) : 0)>();
+  if (S == 0) fill(0);
+  if (S == 2) fill(1);
+  if (S == 4) fill(2);
+  if (S == 6) fill(3);
 }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
@@ -398,16 +455,53 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
     ls.store(stage);
   };
 
+  // prologue: stages 0 and 1 into LDS, the pipe primed with stage 0
   gload(0);
   sstore(smem);
+  gload(nk > 1 ? 1 : 0);
+  sstore(smem + SM::kStage);
   __syncthreads();
+  WavePipe<BM, BN> pipe;
+  pipe.init(wave_m, wave_n, li, lh);
+  pipe.template read_pair<0, 0>(smem);
+  pipe.read_scales(smem);
+  pipe.sigmas();
+  pipe.template dequant<0, 0>();
+
+  // Ring of three LDS stages: stage kt is computed from slot kt%3 while
+  // slot (kt+1)%3 (written before the previous barrier) is read for the next
+  // stage and slot (kt+2)%3 receives the stage after next, loaded from
+  // global memory in phases (A codes, W codes, scales) across the stage.
+  // Past the last stage the loads and reads are clamped to valid data and
+  // their results ignored, so the loop body has no branches.
   for (int kt = 0; kt < nk; ++kt) {
-    uint8_t* cur = smem + (kt & 1) * SM::kStage;
-    uint8_t* nxt = smem + ((kt + 1) & 1) * SM::kStage;
-    const bool more = kt + 1 < nk;
-    if (more) gload(kt + 1);
-    compute_stage<BM, BN>(cur, acc, wave_m, wave_n, li, lh);
-    if (more) sstore(nxt);
+    const uint8_t* cur = smem + (kt % 3) * SM::kStage;
+    const uint8_t* nxt = smem + ((kt + 1) % 3) * SM::kStage;
+    uint8_t* slot = smem + ((kt + 2) % 3) * SM::kStage;
+    const int kf = kt + 2 < nk ? kt + 2 : nk - 1;
+    auto fill = [&](int phase) {
+      if (phase == 0) {
+        if (FUSED) fa.load((const uint16_t*)args.a_bf16, m0, M, K, kf);
+        else la.load(args.a_codes, m0, M, K, kf);
+      } else if (phase == 1) {
+        if (FUSED) fa.template quantize_store<BN>(slot, s_ta);
+        else la.store(slot + SM::kA);
+        lw.load(args.w_codes, n0, N, K, kf);
+      } else if (phase == 2) {
+        lw.store(slot + SM::kW);
+        ls.load(args.a_scales, args.w_scales, m0, n0, M, N, K, kf);
+      } else {
+        ls.store(slot);
+      }
+    };
+    run_step<0>(pipe, acc, cur, nxt, fill);
+    run_step<1>(pipe, acc, cur, nxt, fill);
+    run_step<2>(pipe, acc, cur, nxt, fill);
+    run_step<3>(pipe, acc, cur, nxt, fill);
+    run_step<4>(pipe, acc, cur, nxt, fill);
+    run_step<5>(pipe, acc, cur, nxt, fill);
+    run_step<6>(pipe, acc, cur, nxt, fill);
+    run_step<7>(pipe, acc, cur, nxt, fill);
     __syncthreads();
   }
   epilogue<BM, BN, OUT_F32>(acc, args.c, M, N, m0, n0, wave_m, wave_n, lane, scale);
@@ -441,14 +535,18 @@ static hipError_t dispatch_flags(const GemmArgs& a, bool out_f32, int d, hipStre
   return out_f32 ? launch_cfg<BM, BN, false, true, FUSED>(a, d, s) : launch_cfg<BM, BN, false, false, FUSED>(a, d, s);
 }
 
-// Tile shape: the largest tile that still gives every CU work, judged by
-// how many workgroup "waves" the grid needs and how full the last one is.
-static int pick_tile(int64_t M, int64_t N, int num_cu) {
+// Tile shape: estimated time = rounds of workgroups over the CUs x tile
+// area / relative efficiency.  Smaller wave tiles dequantize more operand
+// fragments per MFMA; the efficiencies are measured MI355X rates relative to
+// the 256x256 tile.
+// The ragged-K variant of the 256x256 tile does not fit its registers, so
+// K % 128 != 0 starts from the next size.
+static int pick_tile(int64_t M, int64_t N, int64_t K, int num_cu) {
   struct Cand { int bm, bn; double eff; };
-  const Cand cands[] = {{256, 256, 1.0}, {256, 128, 0.9}, {128, 256, 0.9}, {128, 128, 0.75}};
-  int best = 0;
+  const Cand cands[] = {{256, 256, 1.0}, {256, 128, 0.65}, {128, 256, 0.65}, {128, 128, 0.57}};
+  int best = 1;
   double best_t = 1e300;
-  for (int i = 0; i < 4; ++i) {
+  for (int i = (K % kBK) ? 1 : 0; i < 4; ++i) {
     const int64_t tiles = ((M + cands[i].bm - 1) / cands[i].bm) * ((N + cands[i].bn - 1) / cands[i].bn);
     const int64_t rounds = (tiles + num_cu - 1) / num_cu;
     const double t = (double)rounds * cands[i].bm * cands[i].bn / cands[i].eff;
@@ -465,7 +563,7 @@ hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const mq
   a.a_codes = a_codes; a.a_scales = a_scales; a.a_rec = const_cast<mq_scale_rec*>(a_rec);
   a.w_codes = w_codes; a.w_scales = w_scales; a.w_rec = w_rec;
   a.c = c; a.M = (int)M; a.N = (int)N; a.K = (int)K;
-  switch (pick_tile(M, N, dev.num_cu)) {
+  switch (pick_tile(M, N, K, dev.num_cu)) {
     case 0: return dispatch_flags<256, 256, false>(a, out_f32, dev.device, stream);
     case 1: return dispatch_flags<256, 128, false>(a, out_f32, dev.device, stream);
     case 2: return dispatch_flags<128, 256, false>(a, out_f32, dev.device, stream);
