@@ -44,7 +44,22 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=512, help="activation rows in the CPU sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB) three "
+                        "times, as the reference for scaling HBM byte counters")
     return p.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = (1 << 30) // 2
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": 1 << 30, "bytes_written": 1 << 30, "launches": 3,
+                                           "kernel": "torch.neg (elementwise, bf16)"}}), flush=True)
 
 
 def dev_bf16(bits):
@@ -171,6 +186,9 @@ def main():
     import torch
     import workloads
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     cfg, acts_host, acts, wdev, qw, qa, fa, out = setup(args.config)
     flops = cfg.flops()
 

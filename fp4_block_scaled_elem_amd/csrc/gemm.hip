@@ -300,20 +300,21 @@ struct WavePipe {
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa[B][i], ow[B][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ow[B][j], oa[B][i], acc[i][j], 0, 0, 0);
   }
 };
 
 // Interleave the MFMAs of one step with the VALU issued for the next one:
-// one MFMA, then its share of the dequantization.  The sched_barrier at the
-// end keeps each step a scheduling region of its own, so the groups cannot
-// pull work from later steps (which would stretch register live ranges).
+// a share of the dequantization, then one MFMA (measured faster on gfx950
+// than MFMA-first slots).  The sched_barrier at the end keeps each step a
+// scheduling region of its own, so the groups cannot pull work from later
+// steps (which would stretch register live ranges).
 template <int NMFMA, int NVALU>
 __device__ __forceinline__ void interleave() {
 #pragma unroll
   for (int k = 0; k < NMFMA; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, (NVALU + NMFMA - 1) / NMFMA, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -341,32 +342,57 @@ __device__ __forceinline__ void run_step(WavePipe<BM, BN>& p, f32x16_t (&acc)[BM
   if (S == 6) fill(3);
 }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
-  uint32_t u = __float_as_uint(v);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
+// Epilogue.  Each 32x32 accumulator holds D = W_j . A_i^T, so lane l owns
+// output row m = l%32 of the fragment and, in register group g, the four
+// consecutive columns 8g + 4(l/32) .. +3.  They are scaled by s_tA * s_tW,
+// rounded (nearest-even, hardware conversion) and stored 8 bytes (bf16) or
+// 16 bytes (binary32) at a time; ragged or unaligned edges fall back to
+// single elements.
 template <int BM, int BN, bool OUT_F32>
 __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[BM / 64][BN / 64], void* c, int M, int N,
                                          int m0, int n0, int wave_m, int wave_n, int lane, float scale) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
   constexpr int TM = BM / 64, TN = BN / 64;
-  const int j = lane & 31, ib = (lane >> 5) * 4;
+  const bool vec = (N & 3) == 0;
 #pragma unroll
-  for (int fm = 0; fm < TM; ++fm)
+  for (int fm = 0; fm < TM; ++fm) {
+    const int m = m0 + wave_m + fm * 32 + (lane & 31);
+    if (m >= M) continue;
 #pragma unroll
     for (int fn = 0; fn < TN; ++fn) {
-      const int n = n0 + wave_n + fn * 32 + j;
-      if (n >= N) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wave_m + fm * 32 + ib + (v & 3) + 8 * (v >> 2);
-        if (m < M) {
-          const float r = acc[fm][fn][v] * scale;
-          if (OUT_F32) ((float*)c)[(int64_t)m * N + n] = r;
-          else ((uint16_t*)c)[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(r);
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wave_n + fn * 32 + 8 * g + 4 * (lane >> 5);
+        float r[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q] = acc[fm][fn][4 * g + q] * scale;
+        const int64_t off = (int64_t)m * N + n;
+        if (vec && n + 3 < N) {
+          if (OUT_F32) {
+            *(f32x4_t*)((float*)c + off) = f32x4_t{r[0], r[1], r[2], r[3]};
+          } else {
+            const bf16x2_t lo = __builtin_convertvector(f32x2_t{r[0], r[1]}, bf16x2_t);
+            const bf16x2_t hi = __builtin_convertvector(f32x2_t{r[2], r[3]}, bf16x2_t);
+            *(u32x2_t*)((uint16_t*)c + off) =
+                u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (n + q < N) {
+              if (OUT_F32) {
+                ((float*)c)[off + q] = r[q];
+              } else {
+                const bf16x2_t b = __builtin_convertvector(f32x2_t{r[q], r[q]}, bf16x2_t);
+                ((uint16_t*)c)[off + q] = (uint16_t)(__builtin_bit_cast(uint32_t, b) & 0xFFFFu);
+              }
+            }
+          }
         }
       }
     }
+  }
 }
 
 // Tile order: workgroups go round-robin to the 8 XCDs; consecutive logical

@@ -81,9 +81,45 @@ __device__ __forceinline__ float tensor_scale_from_amax(uint32_t amax_bits) {
   return a > 0.0f ? a / kTensorDiv : 1.0f;
 }
 
-// Quantize one group of 16 bf16 values (8 words, element 2i in the low half
-// of word i).  Writes 8 code bytes (two words, even element in the low
-// nibble) and returns the E4M3 scale byte.
+// Codes of 8 bf16 values (4 words, element 2i in the low half of word i)
+// under the reciprocal scale e: byte i = code(2i) | code(2i+1) << 4.
+// The hardware fp32->fp4 conversion (scale 1: no extra power of two) rounds
+// y = x*e to the nearest E2M1 value with ties to the even code, saturates at
+// 6 and keeps the sign of y; that equals e2m1_mag(y) | signbit(x) << 3 for
+// every non-NaN binary32 y (checked exhaustively on gfx950 over all 2^32
+// patterns).  y is NaN only for x = +-0 with e = +inf (a group scale whose
+// reciprocal overflows); those elements get the sign-only code, as
+// e2m1_mag(NaN) = 0 prescribes.
+__device__ __forceinline__ uint32_t encode8(const uint32_t w[4], float e) {
+  uint32_t c = 0;
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, bf16_lo(w[0]) * e, bf16_hi(w[0]) * e, 1.0f, 0);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, bf16_lo(w[1]) * e, bf16_hi(w[1]) * e, 1.0f, 1);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, bf16_lo(w[2]) * e, bf16_hi(w[2]) * e, 1.0f, 2);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, bf16_lo(w[3]) * e, bf16_hi(w[3]) * e, 1.0f, 3);
+  if (__builtin_expect(e > 3.0e38f, 0)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if ((w[i] & 0x7FFFu) == 0) c = (c & ~(0xFu << (8 * i))) | (((w[i] >> 15) & 1u) << (8 * i + 3));
+      if ((w[i] & 0x7FFF0000u) == 0) c = (c & ~(0xF0u << (8 * i))) | ((w[i] >> 31) << (8 * i + 7));
+    }
+  }
+  return c;
+}
+
+// Group scale of a group whose absolute maximum has the bf16 magnitude bits
+// am: returns the E4M3 byte S and sets e = 1 / (value(S) * s_t) (0 when that
+// product is 0).  Each step is one IEEE binary32 operation.
+__device__ __forceinline__ uint32_t group_scale(uint32_t am, float s_t, float& e) {
+  float a = __uint_as_float(am << 16);
+  float rho = (a / 6.0f) / s_t;
+  uint32_t S = e4m3_from_f32(rho);
+  float d = e4m3_to_f32(S) * s_t;
+  e = d > 0.0f ? 1.0f / d : 0.0f;
+  return S;
+}
+
+// Quantize one group of 16 bf16 values (8 words).  Writes 8 code bytes (two
+// words, even element in the low nibble) and returns the E4M3 scale byte.
 __device__ __forceinline__ uint32_t quantize_group16(const uint32_t w[8], float s_t,
                                                      uint32_t& codes_lo, uint32_t& codes_hi) {
   uint32_t am = 0;
@@ -92,21 +128,10 @@ __device__ __forceinline__ uint32_t quantize_group16(const uint32_t w[8], float 
     uint32_t m = bf16x2_absmax_bits(w[i]);
     am = am > m ? am : m;
   }
-  float a = __uint_as_float(am << 16);
-  float rho = (a / 6.0f) / s_t;
-  uint32_t S = e4m3_from_f32(rho);
-  float d = e4m3_to_f32(S) * s_t;
-  float e = d > 0.0f ? 1.0f / d : 0.0f;
-  uint32_t c[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float x0 = bf16_lo(w[i]), x1 = bf16_hi(w[i]);
-    uint32_t c0 = e2m1_mag(x0 * e) | ((w[i] >> 12) & 8u);   // sign of x0 (bit 15)
-    uint32_t c1 = e2m1_mag(x1 * e) | ((w[i] >> 28) & 8u);   // sign of x1 (bit 31)
-    c[i >> 2] |= (c0 | (c1 << 4)) << ((i & 3) * 8);
-  }
-  codes_lo = c[0];
-  codes_hi = c[1];
+  float e;
+  uint32_t S = group_scale(am, s_t, e);
+  codes_lo = encode8(w, e);
+  codes_hi = encode8(w + 4, e);
   return S;
 }
 

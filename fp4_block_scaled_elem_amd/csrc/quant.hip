@@ -12,7 +12,8 @@
 //      KB, L2-resident), derives s_t, then encodes 16-element groups.  One
 //      lane owns 8 consecutive elements (one 16-byte load, fully coalesced);
 //      the two lanes of a group exchange their half maxima with one
-//      cross-lane swap.
+//      cross-lane swap; the element codes come from the hardware fp4
+//      conversion of x * e.
 // Both passes are HBM-bound: 2 bytes read per element for the amax, 2 read
 // plus 0.5625 written per element for the encode.
 #include "mq_device.h"
@@ -90,6 +91,9 @@ __device__ __forceinline__ uint32_t reduce_parts(const mq_scale_rec* __restrict_
   return block_max_u32(m, sh);
 }
 
+// One lane owns 8 consecutive elements (one 16-byte load); the two lanes of a
+// 16-element group swap their half maxima.  Each lane works on four
+// half-groups per iteration, one stride apart, so four loads are in flight.
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __restrict__ x, int64_t nhalf,
                                                              uint32_t* __restrict__ codes,
                                                              uint8_t* __restrict__ scales,
@@ -106,29 +110,37 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
       rec->amax_bits = amax;
     }
   }
-  const int64_t stride = (int64_t)gridDim.x * kQThreads;  // a multiple of 2
   // nhalf and stride are even and a pair starts on an even index, so both
-  // lanes of a group enter and leave the loop together
-  for (int64_t h = (int64_t)blockIdx.x * kQThreads + threadIdx.x; h < nhalf; h += stride) {
-    uint4 v = ld_stream(&x[h]);
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t am = uint4_absmax(v);
-    uint32_t other = __shfl_xor(am, 1, 64);
-    am = am > other ? am : other;
-    float a = __uint_as_float(am << 16);
-    float rho = (a / 6.0f) / s_t;
-    uint32_t S = e4m3_from_f32(rho);
-    float d = e4m3_to_f32(S) * s_t;
-    float e = d > 0.0f ? 1.0f / d : 0.0f;
-    uint32_t c = 0;
+  // lanes of a group enter and leave every loop iteration together
+  const int64_t stride = (int64_t)gridDim.x * kQThreads;
+  constexpr int U = 4;
+  int64_t h = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
+  for (; h + (U - 1) * stride < nhalf; h += U * stride) {
+    uint4 v[U];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x0 = bf16_lo(w[i]), x1 = bf16_hi(w[i]);
-      uint32_t c0 = e2m1_mag(x0 * e) | ((w[i] >> 12) & 8u);
-      uint32_t c1 = e2m1_mag(x1 * e) | ((w[i] >> 28) & 8u);
-      c |= (c0 | (c1 << 4)) << (i * 8);
+    for (int u = 0; u < U; ++u) v[u] = ld_stream(&x[h + u * stride]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      uint32_t am = uint4_absmax(v[u]);
+      const uint32_t other = __shfl_xor(am, 1, 64);
+      am = am > other ? am : other;
+      float e;
+      const uint32_t S = group_scale(am, s_t, e);
+      const int64_t hu = h + u * stride;
+      codes[hu] = encode8(w, e);
+      if ((hu & 1) == 0) scales[hu >> 1] = (uint8_t)S;
     }
-    codes[h] = c;
+  }
+  for (; h < nhalf; h += stride) {
+    const uint4 v = ld_stream(&x[h]);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t am = uint4_absmax(v);
+    const uint32_t other = __shfl_xor(am, 1, 64);
+    am = am > other ? am : other;
+    float e;
+    const uint32_t S = group_scale(am, s_t, e);
+    codes[h] = encode8(w, e);
     if ((h & 1) == 0) scales[h >> 1] = (uint8_t)S;
   }
 }
@@ -153,7 +165,7 @@ hipError_t launch_amax(const void* x_bf16, int64_t nelem, mq_scale_rec* rec, con
 hipError_t launch_quantize(const void* x_bf16, int64_t nelem, uint8_t* codes, uint8_t* scales,
                            mq_scale_rec* rec, bool given, const DeviceInfo& dev, hipStream_t stream) {
   const int64_t nhalf = nelem / 8;  // 8 elements per lane, two lanes per group
-  int blocks = grid_for(nhalf, kQThreads, dev.num_cu * 8);
+  int blocks = grid_for((nhalf + 3) / 4, kQThreads, dev.num_cu * 8);
   hipLaunchKernelGGL(quantize_kernel, dim3(blocks), dim3(kQThreads), 0, stream,
                      (const uint4*)x_bf16, nhalf, (uint32_t*)codes, scales, rec, given ? 1 : 0);
   return hipGetLastError();

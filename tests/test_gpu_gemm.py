@@ -184,3 +184,17 @@ def test_cfg3_fused_projection_sampled(proj):
 def test_cfg5_projection_sampled(proj):
     announce("gemm cfg5 sampled", proj)
     _sampled_projection(5, proj)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 512, 1024), (300, 260, 4112), (64, 1003, 512)])
+def test_bf16_output_is_nearest_even_rounding_of_f32_output(M, N, K):
+    # kernel property (no oracle involved): the bf16 mode stores exactly the
+    # round-to-nearest-even of what the binary32 mode stores
+    announce("gemm bf16 == rne(f32)", M, N, K)
+    import torch
+    mq = _mq()
+    qa = mq.quantize(to_dev_bf16(workloads.random_bf16((M, K), 31, 1.0, "lognormal_mixed")))
+    qw = mq.quantize(to_dev_bf16(workloads.random_bf16((N, K), 32, 0.02)))
+    c32 = _gemm(qa, qw, M, N, f32=True).cpu().numpy()
+    c16 = _gemm(qa, qw, M, N).view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(c16, workloads.f32_to_bf16_bits(c32))
