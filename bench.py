@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--config", type=int, default=2, choices=(2, 3, 5))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=512, help="activation rows in the CPU sample")
+    p.add_argument("--cpu-rows", type=int, default=2048, help="activation rows in the CPU sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB) three "
                         "times, as the reference for scaling HBM byte counters")
@@ -177,6 +177,22 @@ def cpu_baseline(cfg_id, acts_host, rows):
                        f"elementwise steps single-threaded, float64 matmul on {blas} BLAS threads)")}
 
 
+def gemm_traffic(workload):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    or None when the GEMM source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"gemm_traffic_{workload}.json")
+    src = os.path.join(ROOT, "fp4_block_scaled_elem_amd", "csrc", "gemm.hip")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except (OSError, ValueError):
+        return None
+    if rec.get("gemm_source_sha256_16") != h:
+        return None
+    return int(rec["bytes_per_launch"])
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -236,7 +252,7 @@ def main():
         "pct_mfma_peak": round(100.0 * value / PEAK_F16_MFMA_TFLOPS, 2),
         "roofline": {"bound": "mfma", "kernel": "gemm_nvfp4_kernel", "achieved": round(gemm_tflops, 2),
                      "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / PEAK_F16_MFMA_TFLOPS, 4), "traffic": None,
+                     "frac": round(gemm_tflops / PEAK_F16_MFMA_TFLOPS, 4), "traffic": gemm_traffic(cfg.name),
                      "launches_per_step": n_gemm, "avg_launch_ms": round(gemm_ms / n_gemm, 4)},
         "split_ms": {"act_quant": round(q_ms, 4), "gemm": round(gemm_ms, 4)},
         "bf16_torch_tflops": None if bf16 is None else round(bf16, 2),
