@@ -242,11 +242,12 @@ __device__ __forceinline__ half2_t sigma_pair(uint32_t scale_dword, uint32_t sel
 // 32x32, eight K16 steps per stage).  A lane (i, h) handles, in step s, the
 // eight codes at byte 32*(s>>2) + 16h + 4*(s&3) of its fragment row, i.e.
 // group 4*(s>>2) + 2h + ((s&3)>>1).  Codes come from LDS two steps at a time
-// (8 bytes); the four scales of a lane and stage come in one dword.
+// (8 bytes), each pair into its own buffer two steps before it is used; the
+// four scales of a lane and stage come in one dword.
 template <int BM, int BN>
 struct WavePipe {
   static constexpr int TM = BM / 64, TN = BN / 64;
-  u32x2_t ca[2][TM], cw[2][TN];   // codes of a step pair, double-buffered
+  u32x2_t ca[4][TM], cw[4][TN];   // codes of step pairs 0..3
   uint32_t sa[TM], sw[TN];        // the lane's four scale bytes per fragment
   half2_t pa[2][TM], pw[2][TN];   // sigma pairs, sub-chunks 0 and 1
   half8_t oa[2][TM], ow[2][TN];   // dequantized operands, double-buffered
@@ -258,14 +259,14 @@ struct WavePipe {
     as_off = Smem<BM, BN>::kAs + (wave_m + li) * kScaleStride + lh * 4;
     ws_off = Smem<BM, BN>::kWs + (wave_n + li) * kScaleStride + lh * 4;
   }
-  // codes of step pair P (steps 2P, 2P+1) into buffer B
-  template <int P, int B>
+  // codes of step pair P (steps 2P, 2P+1)
+  template <int P>
   __device__ __forceinline__ void read_pair(const uint8_t* stage) {
     constexpr int off = 32 * (P >> 1) + 8 * (P & 1);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) ca[B][i] = *(const u32x2_t*)(stage + a_off + i * 32 * kRowStride + off);
+    for (int i = 0; i < TM; ++i) ca[P][i] = *(const u32x2_t*)(stage + a_off + i * 32 * kRowStride + off);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) cw[B][j] = *(const u32x2_t*)(stage + w_off + j * 32 * kRowStride + off);
+    for (int j = 0; j < TN; ++j) cw[P][j] = *(const u32x2_t*)(stage + w_off + j * 32 * kRowStride + off);
   }
   __device__ __forceinline__ void read_scales(const uint8_t* stage) {
 #pragma unroll
@@ -288,7 +289,7 @@ struct WavePipe {
   // operands of step S into operand buffer B
   template <int S, int B>
   __device__ __forceinline__ void dequant() {
-    constexpr int cb = (S >> 1) & 1, w = S & 1, t = S >> 2, g = (S & 3) >> 1;
+    constexpr int cb = S >> 1, w = S & 1, t = S >> 2, g = (S & 3) >> 1;
 #pragma unroll
     for (int i = 0; i < TM; ++i) oa[B][i] = dequant8(ca[cb][i][w], pa[t][i][g]);
 #pragma unroll
@@ -326,11 +327,11 @@ template <int S, int BM, int BN, typename Fill>
 __device__ __forceinline__ void run_step(WavePipe<BM, BN>& p, f32x16_t (&acc)[BM / 64][BN / 64],
                                          const uint8_t* cur, const uint8_t* nxt, Fill& fill) {
   constexpr int TM = BM / 64, TN = BN / 64, NM = TM * TN, ND = 8 * (TM + TN);
-  if (S == 0) p.template read_pair<1, 1>(cur);
-  if (S == 2) p.template read_pair<2, 0>(cur);
-  if (S == 4) p.template read_pair<3, 1>(cur);
+  if (S == 1) p.template read_pair<2>(cur);
+  if (S == 3) p.template read_pair<3>(cur);
   if (S == 4) p.read_scales(nxt);
-  if (S == 6) p.template read_pair<0, 0>(nxt);
+  if (S == 5) p.template read_pair<0>(nxt);
+  if (S == 7) p.template read_pair<1>(nxt);
   if (S == 7) p.sigmas();  // the next stage's; this stage's were last used in step 6
   if (S < 7) p.template dequant<(S + 1) & 7, (S + 1) & 1>();
   else p.template dequant<0, 0>();
@@ -339,7 +340,12 @@ __device__ __forceinline__ void run_step(WavePipe<BM, BN>& p, f32x16_t (&acc)[BM
   if (S == 0) fill(0);
   if (S == 2) fill(1);
   if (S == 4) fill(2);
-  if (S == 6) fill(3);
+  if (S == 6) {
+    fill(3);
+    // the fill's last LDS writes stay ahead of step 7's reads, so the stage
+    // can end by waiting for all but those reads (see the main loop)
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Epilogue.  Each 32x32 accumulator holds D = W_j . A_i^T, so lane l owns
@@ -489,7 +495,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
   __syncthreads();
   WavePipe<BM, BN> pipe;
   pipe.init(wave_m, wave_n, li, lh);
-  pipe.template read_pair<0, 0>(smem);
+  pipe.template read_pair<0>(smem);
+  pipe.template read_pair<1>(smem);
   pipe.read_scales(smem);
   pipe.sigmas();
   pipe.template dequant<0, 0>();
@@ -500,10 +507,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
   // global memory in phases (A codes, W codes, scales) across the stage.
   // Past the last stage the loads and reads are clamped to valid data and
   // their results ignored, so the loop body has no branches.
+  uint8_t* cur = smem;
+  uint8_t* nxt = smem + SM::kStage;
+  uint8_t* slot = smem + 2 * SM::kStage;
   for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t* cur = smem + (kt % 3) * SM::kStage;
-    const uint8_t* nxt = smem + ((kt + 1) % 3) * SM::kStage;
-    uint8_t* slot = smem + ((kt + 2) % 3) * SM::kStage;
     const int kf = kt + 2 < nk ? kt + 2 : nk - 1;
     auto fill = [&](int phase) {
       if (phase == 0) {
@@ -528,7 +535,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
     run_step<5>(pipe, acc, cur, nxt, fill);
     run_step<6>(pipe, acc, cur, nxt, fill);
     run_step<7>(pipe, acc, cur, nxt, fill);
-    __syncthreads();
+    // End of stage: every LDS write of this stage's fill must be complete
+    // before any wave reads that slot.  LDS operations complete in order, and
+    // after the last fill write each wave issued exactly TM + TN reads (the
+    // next stage's second code pair), so waiting until at most that many LDS
+    // operations are outstanding suffices; those reads stay in flight across
+    // the barrier.  (s_waitcnt: vmcnt and expcnt left at their maxima.)
+    __builtin_amdgcn_s_waitcnt(0xC07F | ((TM + TN) << 8));
+    __builtin_amdgcn_s_barrier();
+    uint8_t* done = cur;
+    cur = nxt;
+    nxt = slot;
+    slot = done;
   }
   epilogue<BM, BN, OUT_F32>(acc, args.c, M, N, m0, n0, wave_m, wave_n, lane, scale);
 }
