@@ -354,47 +354,81 @@ __device__ __forceinline__ void run_step(WavePipe<BM, BN>& p, f32x16_t (&acc)[BM
 // rounded (nearest-even, hardware conversion) and stored 8 bytes (bf16) or
 // 16 bytes (binary32) at a time; ragged or unaligned edges fall back to
 // single elements.
+// Output through LDS.  The MFMA result layout gives each lane four
+// consecutive columns of 32 different rows, so storing straight from the
+// accumulators would scatter every store instruction over 32 rows (32
+// partial cache lines).  Instead the tile goes to LDS 64 rows at a time (32
+// rows from each wave row) and is stored back row-contiguously: every lane
+// stores 4 consecutive columns and a wave covers whole rows.  The LDS row
+// pitch is padded by one lane access, which keeps both the column-scattered
+// writes and the row reads free of bank conflicts.
 template <int BM, int BN, bool OUT_F32>
-__device__ __forceinline__ void epilogue(const f32x16_t (&acc)[BM / 64][BN / 64], void* c, int M, int N,
-                                         int m0, int n0, int wave_m, int wave_n, int lane, float scale) {
+__device__ __forceinline__ void epilogue(const f32x16_t (&acc)[BM / 64][BN / 64], uint8_t* smem, void* c, int M,
+                                         int N, int m0, int n0, int wave, int lane, float scale) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   constexpr int TM = BM / 64, TN = BN / 64;
-  const bool vec = (N & 3) == 0;
+  constexpr int E = OUT_F32 ? 4 : 2;       // bytes per output element
+  constexpr int W = 4 * E;                 // bytes per lane access
+  constexpr int P = BN * E + W;            // LDS row pitch
+  constexpr int R = 64 * P;                // LDS bytes of one 64-row pass
+  constexpr bool kDouble = 2 * R <= Smem<BM, BN>::kTotal;
+  static_assert(R <= Smem<BM, BN>::kTotal, "output pass must fit the operand ring");
+  constexpr int kLanesRow = BN / 4;
+  constexpr int kRowsIter = kThreads / kLanesRow;
+  const int li = lane & 31, lh = lane >> 5;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int tid = wave * 64 + lane;
+  const int cl = tid % kLanesRow, rl0 = tid / kLanesRow;
+  const int n = n0 + 4 * cl;
+  const bool vec = (N & 3) == 0 && n + 3 < N;
+  __syncthreads();  // every wave is done with the operand ring
 #pragma unroll
   for (int fm = 0; fm < TM; ++fm) {
-    const int m = m0 + wave_m + fm * 32 + (lane & 31);
-    if (m >= M) continue;
+    uint8_t* buf = smem + (kDouble ? (fm & 1) * R : 0);
+    if (!kDouble && fm > 0) __syncthreads();
 #pragma unroll
     for (int fn = 0; fn < TN; ++fn) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wave_n + fn * 32 + 8 * g + 4 * (lane >> 5);
-        float r[4];
+        const int col = wc * (BN / 2) + fn * 32 + 8 * g + 4 * lh;
+        uint8_t* dst = buf + (wr * 32 + li) * P + col * E;
+        const f32x4_t r = f32x4_t{acc[fm][fn][4 * g], acc[fm][fn][4 * g + 1], acc[fm][fn][4 * g + 2],
+                                  acc[fm][fn][4 * g + 3]} * scale;
+        if (OUT_F32) {
+          *(f32x4_t*)dst = r;
+        } else {
+          const bf16x2_t lo = __builtin_convertvector(f32x2_t{r[0], r[1]}, bf16x2_t);
+          const bf16x2_t hi = __builtin_convertvector(f32x2_t{r[2], r[3]}, bf16x2_t);
+          *(u32x2_t*)dst = u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        }
+      }
+    }
+    __syncthreads();
 #pragma unroll
-        for (int q = 0; q < 4; ++q) r[q] = acc[fm][fn][4 * g + q] * scale;
-        const int64_t off = (int64_t)m * N + n;
-        if (vec && n + 3 < N) {
-          if (OUT_F32) {
-            *(f32x4_t*)((float*)c + off) = f32x4_t{r[0], r[1], r[2], r[3]};
-          } else {
-            const bf16x2_t lo = __builtin_convertvector(f32x2_t{r[0], r[1]}, bf16x2_t);
-            const bf16x2_t hi = __builtin_convertvector(f32x2_t{r[2], r[3]}, bf16x2_t);
-            *(u32x2_t*)((uint16_t*)c + off) =
-                u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-          }
+    for (int it = 0; it < 64 / kRowsIter; ++it) {
+      const int lr = it * kRowsIter + rl0;
+      const int m = m0 + (lr >> 5) * (BM / 2) + fm * 32 + (lr & 31);
+      if (m >= M) continue;
+      const uint8_t* src = buf + lr * P + cl * W;
+      const int64_t off = (int64_t)m * N + n;
+      if (OUT_F32) {
+        const f32x4_t v = *(const f32x4_t*)src;
+        if (vec) {
+          *(f32x4_t*)((float*)c + off) = v;
         } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (n + q < N) {
-              if (OUT_F32) {
-                ((float*)c)[off + q] = r[q];
-              } else {
-                const bf16x2_t b = __builtin_convertvector(f32x2_t{r[q], r[q]}, bf16x2_t);
-                ((uint16_t*)c)[off + q] = (uint16_t)(__builtin_bit_cast(uint32_t, b) & 0xFFFFu);
-              }
-            }
-          }
+          for (int q = 0; q < 4; ++q)
+            if (n + q < N) ((float*)c)[off + q] = v[q];
+        }
+      } else {
+        const u32x2_t v = *(const u32x2_t*)src;
+        if (vec) {
+          *(u32x2_t*)((uint16_t*)c + off) = v;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (n + q < N) ((uint16_t*)c)[off + q] = (uint16_t)(v[q >> 1] >> (16 * (q & 1)));
         }
       }
     }
@@ -548,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
     nxt = slot;
     slot = done;
   }
-  epilogue<BM, BN, OUT_F32>(acc, args.c, M, N, m0, n0, wave_m, wave_n, lane, scale);
+  epilogue<BM, BN, OUT_F32>(acc, smem, args.c, M, N, m0, n0, wave, lane, scale);
 }
 
 // ------------------------------------------------------------------ host --
