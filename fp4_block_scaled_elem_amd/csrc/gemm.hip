@@ -17,9 +17,10 @@
 //
 // Data flow per workgroup (256 threads = 4 waves in a 2x2 grid, one wave per
 // SIMD; tile BM x BN; K advanced 128 elements = 8 groups per stage):
-//   HBM --16-byte loads--> registers --> LDS ring of three stages (packed
-//   codes + scale bytes)
-//   LDS --8-byte reads--> registers: two dwords = codes of two K16 steps
+//   HBM --direct-to-LDS loads (no registers)--> LDS ring of three stages
+//   (packed codes + scale bytes); the fused prologue and shapes with
+//   K % 128 != 0 go through registers instead
+//   LDS --16-byte reads--> registers: four dwords = codes of four K16 steps
 //   cvt fp4->f16 (hardware) * sigma (packed f16 multiply) -> MFMA operand.
 // Every wave runs a register pipeline: the operands of step s+1 are
 // dequantized while the MFMAs of step s run, and the next stage's codes,
@@ -34,10 +35,15 @@ namespace mq {
 constexpr int kThreads = 256;
 constexpr int kBK = 128;            // K elements per stage
 constexpr int kRowBytes = kBK / 2;  // packed code bytes per row per stage
-// LDS bytes per code row: 64 + 8 pad.  With 18 dwords per row, the 8-byte
-// reads of 16 consecutive rows hit 32 distinct banks.
-constexpr int kRowStride = 72;
-constexpr int kScaleStride = 8;     // LDS bytes per scale row (8 groups)
+constexpr int kRowStride = 64;     // LDS bytes per code row and stage
+constexpr int kScaleStride = 8;    // LDS bytes per scale row (8 groups)
+
+// Code rows in LDS hold four 16-byte chunks, chunk c of row r at position
+// c ^ swz(r).  Sixteen consecutive rows reading the same chunk then cover
+// every bank position of a 64-byte-row layout once per four rows (and once per
+// two rows for groups of eight), so the pipe's 16-byte reads are conflict
+// free, while whole rows stay contiguous for the direct-to-LDS copies.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
 struct GemmArgs {
   const uint8_t* a_codes;
@@ -63,12 +69,6 @@ struct Smem {
   static constexpr int kTotal = 3 * kStage;  // ring of three stages
 };
 
-// Scale bytes of one row and stage, g0..g7, are kept in LDS as
-// [g0 g1 g4 g5 | g2 g3 g6 g7]: the lane of half h (K offsets 32h..32h+31 of
-// each 64-element sub-chunk) then finds all four of its scales in dword h.
-__device__ __forceinline__ u32x2_t permute_scales(u32x2_t g) {
-  return u32x2_t{__builtin_amdgcn_perm(g[1], g[0], 0x05040100u), __builtin_amdgcn_perm(g[1], g[0], 0x07060302u)};
-}
 
 // ---------------------------------------------------------------- loaders --
 
@@ -106,9 +106,7 @@ struct PackedLoader {
     for (int j = 0; j < kChunks; ++j) {
       const int c = tid + kThreads * j;
       const int row = c >> 2, col = c & 3;
-      uint8_t* p = lds + row * kRowStride + col * 16;
-      *(u32x2_t*)p = u32x2_t{code[j][0], code[j][1]};
-      *(u32x2_t*)(p + 8) = u32x2_t{code[j][2], code[j][3]};
+      *(u32x4_t*)(lds + row * kRowStride + ((col ^ swz(row)) << 4)) = code[j];
     }
   }
 };
@@ -155,7 +153,7 @@ struct ScaleLoader {
       if (kFull || r < kRows) {
         uint8_t* p = r < kA ? stage + Smem<BM, BN>::kAs + r * kScaleStride
                             : stage + Smem<BM, BN>::kWs + (r - kA) * kScaleStride;
-        *(u32x2_t*)p = permute_scales(v[j]);
+        *(u32x2_t*)p = v[j];
       }
     }
   }
@@ -187,8 +185,7 @@ struct FusedALoader {
       }
     }
   }
-  // Quantize the loaded groups into the stage's A codes; each scale byte goes
-  // to its permuted position in the row.
+  // Quantize the loaded groups into the stage's A codes and scale bytes.
   template <int BN>
   __device__ __forceinline__ void quantize_store(uint8_t* stage, float s_t) const {
 #pragma unroll
@@ -199,10 +196,82 @@ struct FusedALoader {
                        raw[j][1][0], raw[j][1][1], raw[j][1][2], raw[j][1][3]};
       uint32_t lo, hi;
       uint32_t S = quantize_group16(w, s_t, lo, hi);
-      *(u32x2_t*)(stage + Smem<BM, BN>::kA + row * kRowStride + grp * 8) = u32x2_t{lo, hi};
-      // [g0 g1 g4 g5 | g2 g3 g6 g7]: bit 1 and bit 2 of the group index swap
-      const int pos = (grp & 1) | ((grp & 4) >> 1) | ((grp & 2) << 1);
-      stage[Smem<BM, BN>::kAs + row * kScaleStride + pos] = (uint8_t)S;
+      const int chunk = (grp >> 1) ^ swz(row);
+      *(u32x2_t*)(stage + Smem<BM, BN>::kA + row * kRowStride + chunk * 16 + (grp & 1) * 8) = u32x2_t{lo, hi};
+      stage[Smem<BM, BN>::kAs + row * kScaleStride + grp] = (uint8_t)S;
+    }
+  }
+};
+
+// Direct global->LDS copies of one stage (FAST shapes, K % 128 == 0).  One
+// buffer_load ... lds instruction fills a contiguous stretch of LDS, lane l
+// writing bytes [l*size, (l+1)*size) of it: 16 code rows (64 bytes each) per
+// 16-byte instruction, 32 scale rows (8 bytes) per 4-byte instruction.  The
+// chunk swizzle is applied by the choice of the global chunk each lane
+// copies.  The rows of a stage are A's then W's (WITH_A) or W's alone (fused
+// prologue), contiguous in LDS.  Each operand is addressed through a buffer
+// resource covering exactly its tile's rows: the lane offset (one VGPR) is
+// fixed, the stage offset is a scalar, and an access outside the tile would
+// read zeros rather than other memory.
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, kBufferWord3);
+}
+
+template <int BM, int BN, bool WITH_A>
+struct DmaLoader {
+  static constexpr int kRA = WITH_A ? BM : 0;
+  static constexpr int kRows = kRA + BN;
+  static constexpr int kCode = kRows / 16 / 4;    // code copies per wave
+  static constexpr int kScale = kRows / 32 / 4;   // scale copies per wave
+  static_assert(kCode * 64 == kRows && kScale * 128 == kRows, "tile rows");
+  uint32_t coff[kCode], soff[kScale];
+  __amdgpu_buffer_rsrc_t ra, rw, rsa, rsw;
+  int wave;
+
+  // Requires BM * K / 2 < 2^31 (checked by the host).
+  __device__ __forceinline__ void init(const GemmArgs& g, int m0, int n0) {
+    const int lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ldc = g.K / 2, ng = g.K / kGroup;
+    const int ma = min(BM, g.M - m0), nw = min(BN, g.N - n0);  // valid rows of the tiles
+    if (WITH_A) {
+      ra = tile_rsrc(g.a_codes + (int64_t)m0 * ldc, (int64_t)ma * ldc);
+      rsa = tile_rsrc(g.a_scales + (int64_t)m0 * ng, (int64_t)ma * ng);
+    }
+    rw = tile_rsrc(g.w_codes + (int64_t)n0 * ldc, (int64_t)nw * ldc);
+    rsw = tile_rsrc(g.w_scales + (int64_t)n0 * ng, (int64_t)nw * ng);
+#pragma unroll
+    for (int j = 0; j < kCode; ++j) {
+      const int r = 16 * (wave + 4 * j) + (lane >> 2);
+      const int row = r < kRA ? min(r, ma - 1) : min(r - kRA, nw - 1);  // clamped rows are discarded later
+      coff[j] = (uint32_t)(row * ldc + (((lane & 3) ^ swz(r)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < kScale; ++j) {
+      const int r = 32 * (wave + 4 * j) + (lane >> 1);
+      const int row = r < kRA ? min(r, ma - 1) : min(r - kRA, nw - 1);
+      soff[j] = (uint32_t)(row * ng + ((lane & 1) << 2));
+    }
+  }
+  __device__ __forceinline__ void codes(uint8_t* stage, int kt) const {
+    uint8_t* lds = stage + (WITH_A ? Smem<BM, BN>::kA : Smem<BM, BN>::kW);
+#pragma unroll
+    for (int j = 0; j < kCode; ++j) {
+      const int t = wave + 4 * j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(WITH_A && 16 * t < kRA ? ra : rw, (lds_void_t*)(lds + 1024 * t), 16,
+                                               (int)coff[j], kt * kRowBytes, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void scales(uint8_t* stage, int kt) const {
+    uint8_t* lds = stage + (WITH_A ? Smem<BM, BN>::kAs : Smem<BM, BN>::kWs);
+#pragma unroll
+    for (int j = 0; j < kScale; ++j) {
+      const int t = wave + 4 * j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(WITH_A && 32 * t < kRA ? rsa : rsw, (lds_void_t*)(lds + 256 * t), 4,
+                                               (int)soff[j], kt * 8, 0, 0);
     }
   }
 };
@@ -240,33 +309,39 @@ __device__ __forceinline__ half2_t sigma_pair(uint32_t scale_dword, uint32_t sel
 
 // Per-wave register pipeline over 128-deep stages (TM x TN fragments of
 // 32x32, eight K16 steps per stage).  A lane (i, h) handles, in step s, the
-// eight codes at byte 32*(s>>2) + 16h + 4*(s&3) of its fragment row, i.e.
-// group 4*(s>>2) + 2h + ((s&3)>>1).  Codes come from LDS two steps at a time
-// (8 bytes), each pair into its own buffer two steps before it is used; the
-// four scales of a lane and stage come in one dword.
+// eight codes at byte 32h + 4s of its fragment row (K elements 64h + 8s ..
+// +7, group 4h + s/2): the two lane halves split the stage's K range, so a
+// step's 16 K elements are 8 from each half, the same for A and W.  Codes
+// come from LDS four steps at a time (logical chunk 2h + q for steps
+// 4q..4q+3), each chunk into its own buffer; the lane's four scales are
+// dword h of the row's eight scale bytes.
 template <int BM, int BN>
 struct WavePipe {
   static constexpr int TM = BM / 64, TN = BN / 64;
-  u32x2_t ca[4][TM], cw[4][TN];   // codes of step pairs 0..3
+  u32x4_t ca[2][TM], cw[2][TN];   // codes of steps 0..3 and 4..7
   uint32_t sa[TM], sw[TN];        // the lane's four scale bytes per fragment
   half2_t pa[2][TM], pw[2][TN];   // sigma pairs, sub-chunks 0 and 1
   half8_t oa[2][TM], ow[2][TN];   // dequantized operands, double-buffered
-  int a_off, w_off, as_off, ws_off;
+  int a_off[2], w_off[2], as_off, ws_off;
 
   __device__ __forceinline__ void init(int wave_m, int wave_n, int li, int lh) {
-    a_off = Smem<BM, BN>::kA + (wave_m + li) * kRowStride + lh * 16;
-    w_off = Smem<BM, BN>::kW + (wave_n + li) * kRowStride + lh * 16;
-    as_off = Smem<BM, BN>::kAs + (wave_m + li) * kScaleStride + lh * 4;
-    ws_off = Smem<BM, BN>::kWs + (wave_n + li) * kScaleStride + lh * 4;
+    // fragment rows differ by multiples of 32, which leave swz unchanged
+    const int x = swz(li);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      a_off[q] = Smem<BM, BN>::kA + (wave_m + li) * kRowStride + (((2 * lh + q) ^ x) << 4);
+      w_off[q] = Smem<BM, BN>::kW + (wave_n + li) * kRowStride + (((2 * lh + q) ^ x) << 4);
+    }
+    as_off = Smem<BM, BN>::kAs + (wave_m + li) * kScaleStride + 4 * lh;
+    ws_off = Smem<BM, BN>::kWs + (wave_n + li) * kScaleStride + 4 * lh;
   }
-  // codes of step pair P (steps 2P, 2P+1)
-  template <int P>
-  __device__ __forceinline__ void read_pair(const uint8_t* stage) {
-    constexpr int off = 32 * (P >> 1) + 8 * (P & 1);
+  // codes of steps 4Q..4Q+3
+  template <int Q>
+  __device__ __forceinline__ void read_chunk(const uint8_t* stage) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) ca[P][i] = *(const u32x2_t*)(stage + a_off + i * 32 * kRowStride + off);
+    for (int i = 0; i < TM; ++i) ca[Q][i] = *(const u32x4_t*)(stage + a_off[Q] + i * 32 * kRowStride);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) cw[P][j] = *(const u32x2_t*)(stage + w_off + j * 32 * kRowStride + off);
+    for (int j = 0; j < TN; ++j) cw[Q][j] = *(const u32x4_t*)(stage + w_off[Q] + j * 32 * kRowStride);
   }
   __device__ __forceinline__ void read_scales(const uint8_t* stage) {
 #pragma unroll
@@ -289,11 +364,11 @@ struct WavePipe {
   // operands of step S into operand buffer B
   template <int S, int B>
   __device__ __forceinline__ void dequant() {
-    constexpr int cb = S >> 1, w = S & 1, t = S >> 2, g = (S & 3) >> 1;
+    constexpr int q = S >> 2, w = S & 3, g = (S & 3) >> 1;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) oa[B][i] = dequant8(ca[cb][i][w], pa[t][i][g]);
+    for (int i = 0; i < TM; ++i) oa[B][i] = dequant8(ca[q][i][w], pa[q][i][g]);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) ow[B][j] = dequant8(cw[cb][j][w], pw[t][j][g]);
+    for (int j = 0; j < TN; ++j) ow[B][j] = dequant8(cw[q][j][w], pw[q][j][g]);
   }
   template <int B>
   __device__ __forceinline__ void mfma(f32x16_t (&acc)[TM][TN]) {
@@ -320,48 +395,36 @@ __device__ __forceinline__ void interleave() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Step S of a stage: LDS reads for later steps, dequantization of step S+1
-// (or of the next stage's step 0), the MFMAs of step S, and one phase of the
-// global->LDS fill of the stage after next.
+// Step S of a stage: LDS reads for the next stage (first chunk in step 3,
+// scales in step 4, second chunk in step 7, each after the buffer's last use
+// in this stage), dequantization of step S+1 (or of the next stage's step 0),
+// the MFMAs of step S, and step S's part of the fill of the stage after next.
 template <int S, int BM, int BN, typename Fill>
 __device__ __forceinline__ void run_step(WavePipe<BM, BN>& p, f32x16_t (&acc)[BM / 64][BN / 64],
-                                         const uint8_t* cur, const uint8_t* nxt, Fill& fill) {
+                                         const uint8_t* nxt, Fill& fill) {
   constexpr int TM = BM / 64, TN = BN / 64, NM = TM * TN, ND = 8 * (TM + TN);
-  if (S == 1) p.template read_pair<2>(cur);
-  if (S == 3) p.template read_pair<3>(cur);
+  if (S == 3) p.template read_chunk<0>(nxt);
   if (S == 4) p.read_scales(nxt);
-  if (S == 5) p.template read_pair<0>(nxt);
-  if (S == 7) p.template read_pair<1>(nxt);
+  if (S == 7) p.template read_chunk<1>(nxt);
   if (S == 7) p.sigmas();  // the next stage's; this stage's were last used in step 6
   if (S < 7) p.template dequant<(S + 1) & 7, (S + 1) & 1>();
   else p.template dequant<0, 0>();
   p.template mfma<S & 1>(acc);
   interleave<NM, ND + (S == 7 ? 6 * (TM + TN) : 0)>();
-  if (S == 0) fill(0);
-  if (S == 2) fill(1);
-  if (S == 4) fill(2);
-  if (S == 6) {
-    fill(3);
-    // the fill's last LDS writes stay ahead of step 7's reads, so the stage
-    // can end by waiting for all but those reads (see the main loop)
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  fill(S);
 }
 
 // Epilogue.  Each 32x32 accumulator holds D = W_j . A_i^T, so lane l owns
 // output row m = l%32 of the fragment and, in register group g, the four
-// consecutive columns 8g + 4(l/32) .. +3.  They are scaled by s_tA * s_tW,
-// rounded (nearest-even, hardware conversion) and stored 8 bytes (bf16) or
-// 16 bytes (binary32) at a time; ragged or unaligned edges fall back to
-// single elements.
-// Output through LDS.  The MFMA result layout gives each lane four
-// consecutive columns of 32 different rows, so storing straight from the
+// consecutive columns 8g + 4(l/32) .. +3.  They are scaled by s_tA * s_tW and
+// rounded (nearest-even, hardware conversion).  Storing straight from the
 // accumulators would scatter every store instruction over 32 rows (32
 // partial cache lines).  Instead the tile goes to LDS 64 rows at a time (32
 // rows from each wave row) and is stored back row-contiguously: every lane
 // stores 4 consecutive columns and a wave covers whole rows.  The LDS row
 // pitch is padded by one lane access, which keeps both the column-scattered
-// writes and the row reads free of bank conflicts.
+// writes and the row reads free of bank conflicts; ragged or unaligned edges
+// fall back to single elements.
 template <int BM, int BN, bool OUT_F32>
 __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[BM / 64][BN / 64], uint8_t* smem, void* c, int M,
                                          int N, int m0, int n0, int wave, int lane, float scale) {
@@ -503,79 +566,98 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   using SM = Smem<BM, BN>;
+  // FAST shapes copy packed operands straight into LDS (A too unless it is
+  // quantized here); the fused A tile and all operands of ragged-K shapes go
+  // through registers.
+  DmaLoader<BM, BN, !FUSED> dma;
   PackedLoader<BM, FAST> la;
   FusedALoader<BM, FAST> fa;
   PackedLoader<BN, FAST> lw;
   ScaleLoader<BM, BN, FAST, !FUSED> ls;
+  if constexpr (FAST) dma.init(args, m0, n0);
 
-  auto gload = [&](int kt) {
-    if (FUSED) fa.load((const uint16_t*)args.a_bf16, m0, M, K, kt);
-    else la.load(args.a_codes, m0, M, K, kt);
-    lw.load(args.w_codes, n0, N, K, kt);
-    ls.load(args.a_scales, args.w_scales, m0, n0, M, N, K, kt);
-  };
-  auto sstore = [&](uint8_t* stage) {
-    if (FUSED) fa.template quantize_store<BN>(stage, s_ta);
-    else la.store(stage + SM::kA);
-    lw.store(stage + SM::kW);
-    ls.store(stage);
+  auto load_stage = [&](uint8_t* stage, int kt) {
+    if constexpr (FAST) {
+      dma.codes(stage, kt);
+      dma.scales(stage, kt);
+    }
+    if constexpr (FUSED) {
+      fa.load((const uint16_t*)args.a_bf16, m0, M, K, kt);
+      fa.template quantize_store<BN>(stage, s_ta);
+    } else if constexpr (!FAST) {
+      la.load(args.a_codes, m0, M, K, kt);
+      la.store(stage + SM::kA);
+    }
+    if constexpr (!FAST) {
+      lw.load(args.w_codes, n0, N, K, kt);
+      lw.store(stage + SM::kW);
+      ls.load(args.a_scales, args.w_scales, m0, n0, M, N, K, kt);
+      ls.store(stage);
+    }
   };
 
   // prologue: stages 0 and 1 into LDS, the pipe primed with stage 0
-  gload(0);
-  sstore(smem);
-  gload(nk > 1 ? 1 : 0);
-  sstore(smem + SM::kStage);
+  load_stage(smem, 0);
+  load_stage(smem + SM::kStage, nk > 1 ? 1 : 0);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): direct-to-LDS copies included
   __syncthreads();
   WavePipe<BM, BN> pipe;
   pipe.init(wave_m, wave_n, li, lh);
-  pipe.template read_pair<0>(smem);
-  pipe.template read_pair<1>(smem);
+  pipe.template read_chunk<0>(smem);
+  pipe.template read_chunk<1>(smem);
   pipe.read_scales(smem);
   pipe.sigmas();
   pipe.template dequant<0, 0>();
 
-  // Ring of three LDS stages: stage kt is computed from slot kt%3 while
-  // slot (kt+1)%3 (written before the previous barrier) is read for the next
-  // stage and slot (kt+2)%3 receives the stage after next, loaded from
-  // global memory in phases (A codes, W codes, scales) across the stage.
-  // Past the last stage the loads and reads are clamped to valid data and
-  // their results ignored, so the loop body has no branches.
+  // Ring of three LDS stages: stage kt is computed from slot kt%3 (its
+  // operands were read into registers during the previous stage), slot
+  // (kt+1)%3 is read for the next stage and slot (kt+2)%3 receives the stage
+  // after next.  Past the last stage the loads and reads are clamped to
+  // valid data and their results ignored, so the loop body has no branches.
   uint8_t* cur = smem;
   uint8_t* nxt = smem + SM::kStage;
   uint8_t* slot = smem + 2 * SM::kStage;
   for (int kt = 0; kt < nk; ++kt) {
     const int kf = kt + 2 < nk ? kt + 2 : nk - 1;
-    auto fill = [&](int phase) {
-      if (phase == 0) {
-        if (FUSED) fa.load((const uint16_t*)args.a_bf16, m0, M, K, kf);
-        else la.load(args.a_codes, m0, M, K, kf);
-      } else if (phase == 1) {
-        if (FUSED) fa.template quantize_store<BN>(slot, s_ta);
-        else la.store(slot + SM::kA);
-        lw.load(args.w_codes, n0, N, K, kf);
-      } else if (phase == 2) {
-        lw.store(slot + SM::kW);
-        ls.load(args.a_scales, args.w_scales, m0, n0, M, N, K, kf);
+    auto fill = [&](int step) {
+      if constexpr (FAST) {
+        if (step == 0) dma.codes(slot, kf);
+        if (step == 1) dma.scales(slot, kf);
+        if constexpr (FUSED) {
+          if (step == 0) fa.load((const uint16_t*)args.a_bf16, m0, M, K, kf);
+          if (step == 2) fa.template quantize_store<BN>(slot, s_ta);
+        }
       } else {
-        ls.store(slot);
+        if (step == 0) {
+          if (FUSED) fa.load((const uint16_t*)args.a_bf16, m0, M, K, kf);
+          else la.load(args.a_codes, m0, M, K, kf);
+        } else if (step == 2) {
+          if (FUSED) fa.template quantize_store<BN>(slot, s_ta);
+          else la.store(slot + SM::kA);
+          lw.load(args.w_codes, n0, N, K, kf);
+        } else if (step == 4) {
+          lw.store(slot + SM::kW);
+          ls.load(args.a_scales, args.w_scales, m0, n0, M, N, K, kf);
+        } else if (step == 6) {
+          ls.store(slot);
+        }
       }
     };
-    run_step<0>(pipe, acc, cur, nxt, fill);
-    run_step<1>(pipe, acc, cur, nxt, fill);
-    run_step<2>(pipe, acc, cur, nxt, fill);
-    run_step<3>(pipe, acc, cur, nxt, fill);
-    run_step<4>(pipe, acc, cur, nxt, fill);
-    run_step<5>(pipe, acc, cur, nxt, fill);
-    run_step<6>(pipe, acc, cur, nxt, fill);
-    run_step<7>(pipe, acc, cur, nxt, fill);
-    // End of stage: every LDS write of this stage's fill must be complete
-    // before any wave reads that slot.  LDS operations complete in order, and
-    // after the last fill write each wave issued exactly TM + TN reads (the
-    // next stage's second code pair), so waiting until at most that many LDS
-    // operations are outstanding suffices; those reads stay in flight across
-    // the barrier.  (s_waitcnt: vmcnt and expcnt left at their maxima.)
-    __builtin_amdgcn_s_waitcnt(0xC07F | ((TM + TN) << 8));
+    run_step<0>(pipe, acc, nxt, fill);
+    run_step<1>(pipe, acc, nxt, fill);
+    run_step<2>(pipe, acc, nxt, fill);
+    run_step<3>(pipe, acc, nxt, fill);
+    run_step<4>(pipe, acc, nxt, fill);
+    run_step<5>(pipe, acc, nxt, fill);
+    run_step<6>(pipe, acc, nxt, fill);
+    run_step<7>(pipe, acc, nxt, fill);
+    // End of stage: the fill of the stage after next must be complete in LDS
+    // before any wave reads it: all direct copies (vmcnt) and all LDS writes.
+    // LDS operations complete in order and after the last fill write each
+    // wave issued exactly TM + TN reads (the next stage's second chunk, from
+    // a slot nobody writes now), so those may stay in flight across the
+    // barrier.  (s_waitcnt: vmcnt 0, expcnt at its maximum.)
+    __builtin_amdgcn_s_waitcnt(0x0070 | ((TM + TN) << 8));
     __builtin_amdgcn_s_barrier();
     uint8_t* done = cur;
     cur = nxt;
@@ -606,9 +688,13 @@ static hipError_t launch_cfg(const GemmArgs& a0, int dev, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The fast variant needs whole stages (K % 128 == 0) and buffer offsets of a
+// 256-row tile below 2^31 (256 * K/2 < 2^31).
+static bool fast_shape(int64_t K) { return K % kBK == 0 && K < (int64_t(1) << 24); }
+
 template <int BM, int BN, bool FUSED>
 static hipError_t dispatch_flags(const GemmArgs& a, bool out_f32, int d, hipStream_t s) {
-  const bool fast = (a.K % kBK) == 0;
+  const bool fast = fast_shape(a.K);
   if (fast) return out_f32 ? launch_cfg<BM, BN, true, true, FUSED>(a, d, s) : launch_cfg<BM, BN, true, false, FUSED>(a, d, s);
   return out_f32 ? launch_cfg<BM, BN, false, true, FUSED>(a, d, s) : launch_cfg<BM, BN, false, false, FUSED>(a, d, s);
 }
@@ -618,13 +704,13 @@ static hipError_t dispatch_flags(const GemmArgs& a, bool out_f32, int d, hipStre
 // fragments per MFMA; the efficiencies are measured MI355X rates relative to
 // the 256x256 tile.
 // The ragged-K variant of the 256x256 tile does not fit its registers, so
-// K % 128 != 0 starts from the next size.
+// shapes outside the fast variant start from the next size.
 static int pick_tile(int64_t M, int64_t N, int64_t K, int num_cu) {
   struct Cand { int bm, bn; double eff; };
   const Cand cands[] = {{256, 256, 1.0}, {256, 128, 0.65}, {128, 256, 0.65}, {128, 128, 0.57}};
   int best = 1;
   double best_t = 1e300;
-  for (int i = (K % kBK) ? 1 : 0; i < 4; ++i) {
+  for (int i = fast_shape(K) ? 0 : 1; i < 4; ++i) {
     const int64_t tiles = ((M + cands[i].bm - 1) / cands[i].bm) * ((N + cands[i].bn - 1) / cands[i].bn);
     const int64_t rounds = (tiles + num_cu - 1) / num_cu;
     const double t = (double)rounds * cands[i].bm * cands[i].bn / cands[i].eff;
