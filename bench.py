@@ -7,6 +7,9 @@ One step = one pass of the prefill hot path over one 8B-shaped decoder layer
 (default: M=4096 tokens through q,k,v,o,gate,up,down): each of the layer's
 four activation tensors is quantized to NVFP4 on the fly (amax pass +
 encode), then every NVFP4 x NVFP4 GEMM that consumes it runs (bf16 output).
+Projections that read the same activation share a launch where that fills
+the GPU better (k with v, gate with up: mq_gemm_nvfp4_prefill_grouped);
+``--launches separate`` runs one launch per projection instead.
 Weights are quantized once before timing (offline, as the method keeps them
 in the low-precision format).  With --config 3 (M=32768) every GEMM instead
 quantizes its bf16 input in its own prologue.  Inputs are seeded synthetic
@@ -41,6 +44,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", type=int, default=2, choices=(2, 3, 5))
+    p.add_argument("--launches", choices=("grouped", "separate"), default="grouped",
+                   help="grouped: k+v and gate+up as one launch each; separate: one launch per projection")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=2048, help="activation rows in the CPU sample")
@@ -90,10 +95,27 @@ def setup(cfg_id):
     return cfg, acts_host, acts, wdev, qw, qa, fa, out
 
 
-def run_step(cfg, acts, qw, qa, fa, out, events=None):
+# projections launched together (they read the same activation)
+GROUPED = (("q",), ("k", "v"), ("o",), ("gate", "up"), ("down",))
+
+
+def launch_plan(cfg, mode):
+    """[(activation, (projections of one launch))] in execution order."""
+    import workloads
+    groups = GROUPED if mode == "grouped" else tuple((p,) for p in cfg.projs)
+    plan = []
+    for a in workloads.ACTS:
+        for g in groups:
+            g = tuple(p for p in g if p in cfg.projs and workloads.PROJ_INPUT[p] == a)
+            if g:
+                plan.append((a, g))
+    assert sorted(p for _, g in plan for p in g) == sorted(cfg.projs)
+    return plan
+
+
+def run_step(cfg, plan, acts, qw, qa, fa, out, events=None):
     import fp4_block_scaled_elem_amd as mq
     import workloads
-    consumers = {a: [p for p in cfg.projs if workloads.PROJ_INPUT[p] == a] for a in workloads.ACTS}
     for a in workloads.ACTS:
         if not cfg.fused_act_quant:
             if events is not None:
@@ -101,13 +123,19 @@ def run_step(cfg, acts, qw, qa, fa, out, events=None):
             mq.mq_quantize_nvfp4(acts[a], qa[a])
             if events is not None:
                 events["q"].append(_ev())
-        for p in consumers[a]:
+        for act, g in plan:
+            if act != a:
+                continue
             if events is not None:
                 events["g"].append(_ev())
             if cfg.fused_act_quant:
-                mq.mq_gemm_nvfp4_prefill(fa[p], acts[a], qw[p], out[p], mq.MQ_A_FUSED_BF16)
+                A, x, flags = fa[g[0]], acts[a], mq.MQ_A_FUSED_BF16
             else:
-                mq.mq_gemm_nvfp4_prefill(qa[a], None, qw[p], out[p], 0)
+                A, x, flags = qa[a], None, 0
+            if len(g) == 1:
+                mq.mq_gemm_nvfp4_prefill(A, x, qw[g[0]], out[g[0]], flags)
+            else:
+                mq.mq_gemm_nvfp4_prefill_grouped(A, x, [qw[p] for p in g], [out[p] for p in g], flags)
             if events is not None:
                 events["g"].append(_ev())
 
@@ -207,9 +235,10 @@ def main():
         return
     cfg, acts_host, acts, wdev, qw, qa, fa, out = setup(args.config)
     flops = cfg.flops()
+    plan = launch_plan(cfg, args.launches)
 
     for _ in range(args.warmup):
-        run_step(cfg, acts, qw, qa, fa, out)
+        run_step(cfg, plan, acts, qw, qa, fa, out)
     torch.cuda.synchronize()
 
     # timed region: exactly K steps between two device synchronisations;
@@ -219,14 +248,14 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        run_step(cfg, acts, qw, qa, fa, out, events)
+        run_step(cfg, plan, acts, qw, qa, fa, out, events)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
     value = flops / (wall / args.steps) / 1e12
     gemm_ms = _pairs_ms(events["g"]) / args.steps
     q_ms = _pairs_ms(events["q"]) / args.steps if events["q"] else 0.0
-    n_gemm = len(cfg.projs)
+    n_gemm = len(plan)
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
 
     bf16 = None if args.no_bf16 else bf16_reference(cfg, acts, wdev)
@@ -248,6 +277,7 @@ def main():
         "config": {"workload": cfg.name, "desc": cfg.desc, "M": cfg.M[0],
                    "layer": {"d_model": cfg.layer.d_model, "d_kv": cfg.layer.d_kv, "d_ffn": cfg.layer.d_ffn},
                    "projections": list(cfg.projs), "act_quant": "fused" if cfg.fused_act_quant else "separate",
+                   "launches": ["+".join(g) for _, g in plan],
                    "flop_per_step": flops},
         "pct_mfma_peak": round(100.0 * value / PEAK_F16_MFMA_TFLOPS, 2),
         "roofline": {"bound": "mfma", "kernel": "gemm_nvfp4_kernel", "achieved": round(gemm_tflops, 2),

@@ -9,6 +9,7 @@ Entry points (same names as the C ABI in include/mq.h):
 
     mq_quantize_nvfp4(x_bf16, out: NVFP4, flags=0, stream=None)
     mq_gemm_nvfp4_prefill(a: NVFP4, a_bf16, w: NVFP4, c, flags=0, stream=None)
+    mq_gemm_nvfp4_prefill_grouped(a: NVFP4, a_bf16, ws: [NVFP4], cs: [tensor], flags=0, stream=None)
     mq_gemv_bf16_decode(x_bf16, w_bf16, y_bf16, flags=0, stream=None)
 
 and small conveniences built on them (``quantize``, ``prefill_linear``,
@@ -36,10 +37,11 @@ MQ_OUT_BF16 = 0
 MQ_OUT_F32 = 2
 MQ_A_FUSED_BF16 = 4
 MQ_AMAX_PARTS = 1020
+MQ_MAX_GROUP = 4
 REC_BYTES = 16 + 4 * MQ_AMAX_PARTS  # sizeof(mq_scale_rec) = 4096
 
-EXPORTS = ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemv_bf16_decode",
-           "mq_status_str", "mq_last_error", "mq_version")
+EXPORTS = ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemm_nvfp4_prefill_grouped",
+           "mq_gemv_bf16_decode", "mq_status_str", "mq_last_error", "mq_version")
 
 
 class LibraryNotBuilt(ImportError):
@@ -74,6 +76,9 @@ def lib():
     L.mq_quantize_nvfp4.restype = ctypes.c_int32
     L.mq_gemm_nvfp4_prefill.argtypes = [P, vp, P, vp, i64, i64, i64, u32, vp]
     L.mq_gemm_nvfp4_prefill.restype = ctypes.c_int32
+    L.mq_gemm_nvfp4_prefill_grouped.argtypes = [P, vp, ctypes.c_int32, P, ctypes.POINTER(vp),
+                                                ctypes.POINTER(i64), i64, i64, u32, vp]
+    L.mq_gemm_nvfp4_prefill_grouped.restype = ctypes.c_int32
     L.mq_gemv_bf16_decode.argtypes = [vp, vp, vp, i64, i64, i64, u32, vp]
     L.mq_gemv_bf16_decode.restype = ctypes.c_int32
     L.mq_status_str.argtypes = [ctypes.c_int32]
@@ -180,6 +185,36 @@ def mq_gemm_nvfp4_prefill(a: NVFP4, a_bf16, w: NVFP4, c, flags: int = 0, stream=
     _check(lib().mq_gemm_nvfp4_prefill(ctypes.byref(ac), _dev_ptr(a_bf16, "a_bf16"), ctypes.byref(wc),
                                        _dev_ptr(c, "c"), M, N, K, flags, _stream_ptr(stream)),
            "mq_gemm_nvfp4_prefill")
+
+
+def mq_gemm_nvfp4_prefill_grouped(a: NVFP4, a_bf16, ws, cs, flags: int = 0, stream=None):
+    """cs[g] = A . ws[g]^T for every g, one launch (ws share K; len 1..MQ_MAX_GROUP)."""
+    import torch
+    if len(ws) != len(cs) or not ws:
+        raise ValueError("ws and cs must be non-empty lists of the same length")
+    K = ws[0].shape[1]
+    if any(w.shape[1] != K for w in ws):
+        raise ValueError("all weights must have the same K")
+    if a_bf16 is not None:
+        if a_bf16.dtype != torch.bfloat16 or a_bf16.dim() != 2 or a_bf16.shape[1] != K:
+            raise ValueError("a_bf16 must be bfloat16 [M][K]")
+        M = a_bf16.shape[0]
+    else:
+        M, Ka = a.shape
+        if Ka != K:
+            raise ValueError(f"K mismatch: A has {Ka}, W has {K}")
+    want = torch.float32 if flags & MQ_OUT_F32 else torch.bfloat16
+    for w, c in zip(ws, cs):
+        if c.dtype != want or tuple(c.shape) != (M, w.shape[0]):
+            raise ValueError(f"each c must be {want} [{M}][N_g]")
+    n = len(ws)
+    wc = (_NVFP4C * n)(*[w._c() for w in ws])
+    cp = (ctypes.c_void_p * n)(*[_dev_ptr(c, "c").value for c in cs])
+    nn = (ctypes.c_int64 * n)(*[w.shape[0] for w in ws])
+    ac = a._c()
+    _check(lib().mq_gemm_nvfp4_prefill_grouped(ctypes.byref(ac), _dev_ptr(a_bf16, "a_bf16"), n, wc, cp, nn,
+                                               M, K, flags, _stream_ptr(stream)),
+           "mq_gemm_nvfp4_prefill_grouped")
 
 
 def mq_gemv_bf16_decode(x_bf16, w_bf16, y_bf16, flags: int = 0, stream=None):

@@ -114,14 +114,17 @@ mq_status mq_quantize_nvfp4(const void* x_bf16, int64_t rows, int64_t cols, cons
                   "quantize");
 }
 
-mq_status mq_gemm_nvfp4_prefill(const mq_nvfp4* a, const void* a_bf16, const mq_nvfp4* w, void* c,
-                                int64_t M, int64_t N, int64_t K, uint32_t flags, void* hip_stream) {
+mq_status mq_gemm_nvfp4_prefill_grouped(const mq_nvfp4* a, const void* a_bf16, int32_t n_group,
+                                        const mq_nvfp4* w, void* const* c, const int64_t* N, int64_t M,
+                                        int64_t K, uint32_t flags, void* hip_stream) {
   const uint32_t known = MQ_OUT_F32 | MQ_A_FUSED_BF16 | MQ_SCALE_GIVEN;
   if (flags & ~known) return fail(MQ_ERR_INVALID, "unknown flags 0x%x", flags);
   const bool fused = flags & MQ_A_FUSED_BF16;
   if ((flags & MQ_SCALE_GIVEN) && !fused) return fail(MQ_ERR_INVALID, "MQ_SCALE_GIVEN needs MQ_A_FUSED_BF16");
-  if (!a || !w || !c) return fail(MQ_ERR_INVALID, "a, w and c must not be NULL");
-  if (!a->rec || !w->codes || !w->scales || !w->rec) return fail(MQ_ERR_INVALID, "a->rec, w->codes, w->scales, w->rec must not be NULL");
+  if (n_group < 1 || n_group > MQ_MAX_GROUP)
+    return fail(MQ_ERR_INVALID, "n_group=%d must be in 1..%d", (int)n_group, MQ_MAX_GROUP);
+  if (!a || !w || !c || !N) return fail(MQ_ERR_INVALID, "a, w, c and N must not be NULL");
+  if (!a->rec) return fail(MQ_ERR_INVALID, "a->rec must not be NULL");
   if (fused) {
     if (!a_bf16) return fail(MQ_ERR_INVALID, "MQ_A_FUSED_BF16 needs a_bf16");
   } else {
@@ -129,30 +132,41 @@ mq_status mq_gemm_nvfp4_prefill(const mq_nvfp4* a, const void* a_bf16, const mq_
     if (!a->codes || !a->scales) return fail(MQ_ERR_INVALID, "a->codes and a->scales must not be NULL");
   }
   if (mq_status s = check_dims(M, K, "M", "K")) return s;
-  if (mq_status s = check_dims(N, K, "N", "K")) return s;
-  if (M * N > ((int64_t)1 << 40)) return fail(MQ_ERR_SHAPE, "M*N too large");
   if (K % 16) return fail(MQ_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
-  if (!aligned(w->codes, 16) || !aligned(w->scales, 8) || !aligned(w->rec, 16) || !aligned(a->rec, 16) ||
-      !aligned(c, 16))
-    return fail(MQ_ERR_ALIGN, "codes and c need 16-byte, scales 8-byte, rec 16-byte alignment");
+  if (!aligned(a->rec, 16)) return fail(MQ_ERR_ALIGN, "a->rec needs 16-byte alignment");
   if (fused ? !aligned(a_bf16, 16) : (!aligned(a->codes, 16) || !aligned(a->scales, 8)))
     return fail(MQ_ERR_ALIGN, "A operand misaligned");
+  mq::GemmWeight gw[MQ_MAX_GROUP];
+  int64_t ncols = 0;
+  for (int g = 0; g < n_group; ++g) {
+    const mq_nvfp4& wg = w[g];
+    if (!wg.codes || !wg.scales || !wg.rec || !c[g])
+      return fail(MQ_ERR_INVALID, "group %d: w codes, scales, rec and c must not be NULL", g);
+    if (mq_status s = check_dims(N[g], K, "N", "K")) return s;
+    if (M * N[g] > ((int64_t)1 << 40)) return fail(MQ_ERR_SHAPE, "group %d: M*N too large", g);
+    if (!aligned(wg.codes, 16) || !aligned(wg.scales, 8) || !aligned(wg.rec, 16) || !aligned(c[g], 16))
+      return fail(MQ_ERR_ALIGN, "group %d: codes and c need 16-byte, scales 8-byte, rec 16-byte alignment", g);
+    ncols += N[g];
+    gw[g] = mq::GemmWeight{wg.codes, wg.scales, wg.rec, c[g], N[g]};
+  }
+  if (ncols > kMaxDim) return fail(MQ_ERR_SHAPE, "the groups' N add up to more than %lld", (long long)kMaxDim);
   mq::DeviceInfo dev;
   if (mq_status s = current_device(dev)) return s;
   hipStream_t st = (hipStream_t)hip_stream;
-  const bool out_f32 = flags & MQ_OUT_F32;
-  if (!fused)
-    return launched(mq::launch_gemm(a->codes, a->scales, a->rec, w->codes, w->scales, w->rec, c, M, N, K,
-                                    out_f32, dev, st),
-                    "gemm");
   const bool given = flags & MQ_SCALE_GIVEN;
-  if (!given) {
+  if (fused && !given) {
     hipError_t e = mq::launch_amax(a_bf16, M * K, a->rec, dev, st);
     if (e != hipSuccess) return launched(e, "amax");
   }
-  return launched(mq::launch_gemm_fused(a_bf16, a->rec, given, w->codes, w->scales, w->rec, c, M, N, K, out_f32,
-                                        dev, st),
-                  "gemm_fused");
+  const mq::GemmOperandA A{fused ? nullptr : a->codes, fused ? nullptr : a->scales, fused ? a_bf16 : nullptr,
+                           a->rec, given};
+  return launched(mq::launch_gemm(A, gw, n_group, M, K, flags & MQ_OUT_F32, dev, st), fused ? "gemm_fused" : "gemm");
+}
+
+mq_status mq_gemm_nvfp4_prefill(const mq_nvfp4* a, const void* a_bf16, const mq_nvfp4* w, void* c,
+                                int64_t M, int64_t N, int64_t K, uint32_t flags, void* hip_stream) {
+  if (!w || !c) return fail(MQ_ERR_INVALID, "a, w and c must not be NULL");
+  return mq_gemm_nvfp4_prefill_grouped(a, a_bf16, 1, w, &c, &N, M, K, flags, hip_stream);
 }
 
 mq_status mq_gemv_bf16_decode(const void* x_bf16, const void* w_bf16, void* y_bf16, int64_t M, int64_t N,

@@ -45,19 +45,48 @@ constexpr int kScaleStride = 8;    // LDS bytes per scale row (8 groups)
 // free, while whole rows stay contiguous for the direct-to-LDS copies.
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
+// One launch computes C_g = A . W_g^T for up to kMaxGroup weights sharing A;
+// the column tiles of the groups follow each other (group g owns column
+// tiles [tn_end[g-1], tn_end[g])).
+constexpr int kMaxGroup = MQ_MAX_GROUP;
+
 struct GemmArgs {
   const uint8_t* a_codes;
   const uint8_t* a_scales;
   const void* a_bf16;        // fused mode only
   mq_scale_rec* a_rec;
+  const uint8_t* w_codes[kMaxGroup];
+  const uint8_t* w_scales[kMaxGroup];
+  const mq_scale_rec* w_rec[kMaxGroup];
+  void* c[kMaxGroup];
+  int n[kMaxGroup];
+  int tn_end[kMaxGroup];
+  int ngroup;
+  int M, K;
+  int tiles_m, tiles_n;      // tiles_n: all groups
+  int a_given;               // fused mode: take s_t from a_rec
+};
+
+// The group of column tile tn and its operands, selected with constant
+// indices only (the argument arrays stay in the kernel-argument segment).
+struct GroupView {
   const uint8_t* w_codes;
   const uint8_t* w_scales;
   const mq_scale_rec* w_rec;
   void* c;
-  int M, N, K;
-  int tiles_m, tiles_n;
-  int a_given;               // fused mode: take s_t from a_rec
+  int N, tn0;
 };
+
+__device__ __forceinline__ GroupView group_of(const GemmArgs& a, int tn) {
+  GroupView v{a.w_codes[0], a.w_scales[0], a.w_rec[0], a.c[0], a.n[0], 0};
+#pragma unroll
+  for (int g = 1; g < kMaxGroup; ++g) {
+    if (g < a.ngroup && tn >= a.tn_end[g - 1]) {
+      v = GroupView{a.w_codes[g], a.w_scales[g], a.w_rec[g], a.c[g], a.n[g], a.tn_end[g - 1]};
+    }
+  }
+  return v;
+}
 
 template <int BM, int BN>
 struct Smem {
@@ -232,17 +261,18 @@ struct DmaLoader {
   int wave;
 
   // Requires BM * K / 2 < 2^31 (checked by the host).
-  __device__ __forceinline__ void init(const GemmArgs& g, int m0, int n0) {
+  __device__ __forceinline__ void init(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
+                                       const uint8_t* w_scales, int M, int N, int K, int m0, int n0) {
     const int lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int ldc = g.K / 2, ng = g.K / kGroup;
-    const int ma = min(BM, g.M - m0), nw = min(BN, g.N - n0);  // valid rows of the tiles
+    const int ldc = K / 2, ng = K / kGroup;
+    const int ma = min(BM, M - m0), nw = min(BN, N - n0);  // valid rows of the tiles
     if (WITH_A) {
-      ra = tile_rsrc(g.a_codes + (int64_t)m0 * ldc, (int64_t)ma * ldc);
-      rsa = tile_rsrc(g.a_scales + (int64_t)m0 * ng, (int64_t)ma * ng);
+      ra = tile_rsrc(a_codes + (int64_t)m0 * ldc, (int64_t)ma * ldc);
+      rsa = tile_rsrc(a_scales + (int64_t)m0 * ng, (int64_t)ma * ng);
     }
-    rw = tile_rsrc(g.w_codes + (int64_t)n0 * ldc, (int64_t)nw * ldc);
-    rsw = tile_rsrc(g.w_scales + (int64_t)n0 * ng, (int64_t)nw * ng);
+    rw = tile_rsrc(w_codes + (int64_t)n0 * ldc, (int64_t)nw * ldc);
+    rsw = tile_rsrc(w_scales + (int64_t)n0 * ng, (int64_t)nw * ng);
 #pragma unroll
     for (int j = 0; j < kCode; ++j) {
       const int r = 16 * (wave + 4 * j) + (lane >> 2);
@@ -524,8 +554,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
   const int wave_m = (wave >> 1) * (BM / 2), wave_n = (wave & 1) * (BN / 2);
   int tm, tn;
   tile_of(blockIdx.x, args.tiles_m, args.tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int M = args.M, N = args.N, K = args.K;
+  const GroupView grp = group_of(args, tn);
+  const int m0 = tm * BM, n0 = (tn - grp.tn0) * BN;
+  const int M = args.M, N = grp.N, K = args.K;
   const int nk = (K + kBK - 1) / kBK;
 
   float s_ta;
@@ -555,7 +586,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
   } else {
     s_ta = args.a_rec->s_t;
   }
-  const float scale = s_ta * args.w_rec->s_t;
+  const float scale = s_ta * grp.w_rec->s_t;
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -574,7 +605,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
   FusedALoader<BM, FAST> fa;
   PackedLoader<BN, FAST> lw;
   ScaleLoader<BM, BN, FAST, !FUSED> ls;
-  if constexpr (FAST) dma.init(args, m0, n0);
+  if constexpr (FAST) dma.init(args.a_codes, args.a_scales, grp.w_codes, grp.w_scales, M, N, K, m0, n0);
 
   auto load_stage = [&](uint8_t* stage, int kt) {
     if constexpr (FAST) {
@@ -589,9 +620,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
       la.store(stage + SM::kA);
     }
     if constexpr (!FAST) {
-      lw.load(args.w_codes, n0, N, K, kt);
+      lw.load(grp.w_codes, n0, N, K, kt);
       lw.store(stage + SM::kW);
-      ls.load(args.a_scales, args.w_scales, m0, n0, M, N, K, kt);
+      ls.load(args.a_scales, grp.w_scales, m0, n0, M, N, K, kt);
       ls.store(stage);
     }
   };
@@ -634,10 +665,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
         } else if (step == 2) {
           if (FUSED) fa.template quantize_store<BN>(slot, s_ta);
           else la.store(slot + SM::kA);
-          lw.load(args.w_codes, n0, N, K, kf);
+          lw.load(grp.w_codes, n0, N, K, kf);
         } else if (step == 4) {
           lw.store(slot + SM::kW);
-          ls.load(args.a_scales, args.w_scales, m0, n0, M, N, K, kf);
+          ls.load(args.a_scales, grp.w_scales, m0, n0, M, N, K, kf);
         } else if (step == 6) {
           ls.store(slot);
         }
@@ -664,7 +695,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
     nxt = slot;
     slot = done;
   }
-  epilogue<BM, BN, OUT_F32>(acc, smem, args.c, M, N, m0, n0, wave, lane, scale);
+  epilogue<BM, BN, OUT_F32>(acc, smem, grp.c, M, N, m0, n0, wave, lane, scale);
 }
 
 // ------------------------------------------------------------------ host --
@@ -675,7 +706,12 @@ template <int BM, int BN, bool FAST, bool OUT_F32, bool FUSED>
 static hipError_t launch_cfg(const GemmArgs& a0, int dev, hipStream_t stream) {
   GemmArgs a = a0;
   a.tiles_m = (a.M + BM - 1) / BM;
-  a.tiles_n = (a.N + BN - 1) / BN;
+  int tn = 0;
+  for (int g = 0; g < a.ngroup; ++g) {
+    tn += (a.n[g] + BN - 1) / BN;
+    a.tn_end[g] = tn;
+  }
+  a.tiles_n = tn;
   auto kern = gemm_nvfp4_kernel<BM, BN, FAST, OUT_F32, FUSED>;
   constexpr int lds = Smem<BM, BN>::kTotal;
   static bool attr_done[kMaxDevices] = {};  // benign race: the call is idempotent
@@ -705,13 +741,15 @@ static hipError_t dispatch_flags(const GemmArgs& a, bool out_f32, int d, hipStre
 // the 256x256 tile.
 // The ragged-K variant of the 256x256 tile does not fit its registers, so
 // shapes outside the fast variant start from the next size.
-static int pick_tile(int64_t M, int64_t N, int64_t K, int num_cu) {
+static int pick_tile(int64_t M, const int64_t* N, int ngroup, int64_t K, int num_cu) {
   struct Cand { int bm, bn; double eff; };
   const Cand cands[] = {{256, 256, 1.0}, {256, 128, 0.65}, {128, 256, 0.65}, {128, 128, 0.57}};
   int best = 1;
   double best_t = 1e300;
   for (int i = fast_shape(K) ? 0 : 1; i < 4; ++i) {
-    const int64_t tiles = ((M + cands[i].bm - 1) / cands[i].bm) * ((N + cands[i].bn - 1) / cands[i].bn);
+    int64_t tn = 0;
+    for (int g = 0; g < ngroup; ++g) tn += (N[g] + cands[i].bn - 1) / cands[i].bn;
+    const int64_t tiles = ((M + cands[i].bm - 1) / cands[i].bm) * tn;
     const int64_t rounds = (tiles + num_cu - 1) / num_cu;
     const double t = (double)rounds * cands[i].bm * cands[i].bn / cands[i].eff;
     if (t < best_t * 0.999) { best_t = t; best = i; }
@@ -719,33 +757,28 @@ static int pick_tile(int64_t M, int64_t N, int64_t K, int num_cu) {
   return best;
 }
 
-hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const mq_scale_rec* a_rec,
-                       const uint8_t* w_codes, const uint8_t* w_scales, const mq_scale_rec* w_rec,
-                       void* c, int64_t M, int64_t N, int64_t K, bool out_f32, const DeviceInfo& dev,
-                       hipStream_t stream) {
+hipError_t launch_gemm(const GemmOperandA& A, const GemmWeight* w, int ngroup, int64_t M, int64_t K, bool out_f32,
+                       const DeviceInfo& dev, hipStream_t stream) {
   GemmArgs a{};
-  a.a_codes = a_codes; a.a_scales = a_scales; a.a_rec = const_cast<mq_scale_rec*>(a_rec);
-  a.w_codes = w_codes; a.w_scales = w_scales; a.w_rec = w_rec;
-  a.c = c; a.M = (int)M; a.N = (int)N; a.K = (int)K;
-  switch (pick_tile(M, N, K, dev.num_cu)) {
+  a.a_codes = A.codes; a.a_scales = A.scales; a.a_bf16 = A.bf16; a.a_rec = A.rec;
+  a.a_given = A.given ? 1 : 0;
+  int64_t n[kMaxGroup];
+  for (int g = 0; g < ngroup; ++g) {
+    a.w_codes[g] = w[g].codes; a.w_scales[g] = w[g].scales; a.w_rec[g] = w[g].rec;
+    a.c[g] = w[g].c; a.n[g] = (int)w[g].n;
+    n[g] = w[g].n;
+  }
+  a.ngroup = ngroup;
+  a.M = (int)M; a.K = (int)K;
+  // fused: a tall A tile is re-quantized once per column tile, so BM stays
+  // small and BN wide to keep the quantize work per MFMA low
+  if (A.bf16) return dispatch_flags<128, 256, true>(a, out_f32, dev.device, stream);
+  switch (pick_tile(M, n, ngroup, K, dev.num_cu)) {
     case 0: return dispatch_flags<256, 256, false>(a, out_f32, dev.device, stream);
     case 1: return dispatch_flags<256, 128, false>(a, out_f32, dev.device, stream);
     case 2: return dispatch_flags<128, 256, false>(a, out_f32, dev.device, stream);
     default: return dispatch_flags<128, 128, false>(a, out_f32, dev.device, stream);
   }
-}
-
-hipError_t launch_gemm_fused(const void* a_bf16, mq_scale_rec* a_rec, bool a_given,
-                             const uint8_t* w_codes, const uint8_t* w_scales, const mq_scale_rec* w_rec,
-                             void* c, int64_t M, int64_t N, int64_t K, bool out_f32,
-                             const DeviceInfo& dev, hipStream_t stream) {
-  GemmArgs a{};
-  a.a_bf16 = a_bf16; a.a_rec = a_rec; a.a_given = a_given ? 1 : 0;
-  a.w_codes = w_codes; a.w_scales = w_scales; a.w_rec = w_rec;
-  a.c = c; a.M = (int)M; a.N = (int)N; a.K = (int)K;
-  // a tall A tile is re-quantized once per column tile: keep BM small and
-  // BN wide so the quantize work per MFMA stays low
-  return dispatch_flags<128, 256, true>(a, out_f32, dev.device, stream);
 }
 
 }  // namespace mq

@@ -18,14 +18,27 @@ hipError_t launch_amax(const void* x_bf16, int64_t nelem, mq_scale_rec* rec, con
                        hipStream_t stream);
 hipError_t launch_quantize(const void* x_bf16, int64_t nelem, uint8_t* codes, uint8_t* scales,
                            mq_scale_rec* rec, bool given, const DeviceInfo& dev, hipStream_t stream);
-hipError_t launch_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const mq_scale_rec* a_rec,
-                       const uint8_t* w_codes, const uint8_t* w_scales, const mq_scale_rec* w_rec,
-                       void* c, int64_t M, int64_t N, int64_t K, bool out_f32, const DeviceInfo& dev,
-                       hipStream_t stream);
-hipError_t launch_gemm_fused(const void* a_bf16, mq_scale_rec* a_rec, bool a_given,
-                             const uint8_t* w_codes, const uint8_t* w_scales, const mq_scale_rec* w_rec,
-                             void* c, int64_t M, int64_t N, int64_t K, bool out_f32,
-                             const DeviceInfo& dev, hipStream_t stream);
+// A operand of a GEMM launch: packed (codes, scales) or, fused, bf16 values
+// quantized in the kernel (rec then receives or, when given, supplies s_t).
+struct GemmOperandA {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const void* bf16;
+  mq_scale_rec* rec;
+  bool given;
+};
+
+// One weight of a (grouped) GEMM launch and its output C [M][n].
+struct GemmWeight {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const mq_scale_rec* rec;
+  void* c;
+  int64_t n;
+};
+
+hipError_t launch_gemm(const GemmOperandA& a, const GemmWeight* w, int ngroup, int64_t M, int64_t K, bool out_f32,
+                       const DeviceInfo& dev, hipStream_t stream);
 hipError_t launch_gemv(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                        const DeviceInfo& dev, hipStream_t stream);
 

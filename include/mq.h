@@ -13,6 +13,9 @@
  *   mq_quantize_nvfp4      bf16 [rows][cols] -> NVFP4 (dynamic tensor scale)
  *   mq_gemm_nvfp4_prefill  C = A . W^T with A, W in NVFP4, fp32 accumulate,
  *                          bf16 (or fp32) output
+ *   mq_gemm_nvfp4_prefill_grouped
+ *                          the same for several weights that share A, in one
+ *                          launch
  *   mq_gemv_bf16_decode    Y = X . W^T on bf16 X [M][K] and W [N][K]
  *
  * Formats (readings where the pages are silent):
@@ -64,6 +67,9 @@ typedef int32_t mq_status;
 
 /* Number of per-workgroup partial maxima an mq_scale_rec can hold. */
 #define MQ_AMAX_PARTS 1020
+
+/* Most weights one mq_gemm_nvfp4_prefill_grouped call takes. */
+#define MQ_MAX_GROUP 4
 
 /* Tensor-scale record, DEVICE memory, 4096 bytes, 16-byte aligned.
  * s_t       binary32 decode scale of the tensor (read by the GEMM epilogue).
@@ -143,6 +149,30 @@ mq_status mq_gemm_nvfp4_prefill(const mq_nvfp4* a, const void* a_bf16,
                                 const mq_nvfp4* w, void* c,
                                 int64_t M, int64_t N, int64_t K,
                                 uint32_t flags, void* hip_stream);
+
+/*
+ * mq_gemm_nvfp4_prefill_grouped - C_g[M][N_g] = A[M][K] . W_g[N_g][K]^T for
+ *   g = 0 .. n_group-1: the prefill linears that read one activation (the
+ *   gate and up projections of an MLP, or k and v) as a single launch, whose
+ *   workgroups cover all the outputs' tiles.  Same arithmetic as
+ *   mq_gemm_nvfp4_prefill (gist.science explainer, s.2 System-Level
+ *   Deployment); each C_g is bit-identical to what mq_gemm_nvfp4_prefill(a,
+ *   a_bf16, &w[g], c[g], M, N[g], K, flags, hip_stream) writes.
+ * a, a_bf16, M, K, flags   as for mq_gemm_nvfp4_prefill; with
+ *          MQ_A_FUSED_BF16 the amax pass over a_bf16 runs once for all
+ *          groups.
+ * n_group  1 .. MQ_MAX_GROUP.
+ * w        HOST array of n_group weights W_g [N_g][K] (rec->s_t set each).
+ * c        HOST array of n_group DEVICE outputs C_g [M][N_g], same element
+ *          type and alignment rules as c of mq_gemm_nvfp4_prefill; the
+ *          outputs must not overlap.
+ * N        HOST array of the n_group column counts, each >= 1.
+ */
+mq_status mq_gemm_nvfp4_prefill_grouped(const mq_nvfp4* a, const void* a_bf16,
+                                        int32_t n_group, const mq_nvfp4* w,
+                                        void* const* c, const int64_t* N,
+                                        int64_t M, int64_t K,
+                                        uint32_t flags, void* hip_stream);
 
 /*
  * mq_gemv_bf16_decode - Y[M][N] = X[M][K] . W[N][K]^T in bf16.

@@ -33,9 +33,10 @@ def L():
     return mq.lib()
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     fns = _header_functions()
-    for f in ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemv_bf16_decode"):
+    for f in ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemm_nvfp4_prefill_grouped",
+              "mq_gemv_bf16_decode"):
         assert f in fns
 
 
@@ -107,6 +108,35 @@ def test_gemm_argument_errors(L):
     assert f(_q(None, None, P16), P8, w, P16, 4, 4, 16, mq.MQ_A_FUSED_BF16, None) == mq.MQ_ERR_ALIGN
 
 
+def _grouped(L, a, a_bf16, ws, cs, ns, M=4, K=16, flags=0, n_group=None):
+    n = len(ws)
+    wa = (mq._NVFP4C * max(n, 1))(*[mq._NVFP4C(*w) for w in ws])
+    ca = (ctypes.c_void_p * max(n, 1))(*cs)
+    na = (ctypes.c_int64 * max(n, 1))(*ns)
+    return L.mq_gemm_nvfp4_prefill_grouped(a, a_bf16, n if n_group is None else n_group, wa, ca, na, M, K,
+                                           flags, None)
+
+
+def test_grouped_gemm_argument_errors(L):
+    a = _q(P16, P16, P16)
+    w = (P16, P16, P16)
+    g = lambda **kw: _grouped(L, a, None, [w, w], [P16, P16], [4, 4], **kw)
+    assert g(n_group=0) == mq.MQ_ERR_INVALID
+    assert g(n_group=mq.MQ_MAX_GROUP + 1) == mq.MQ_ERR_INVALID
+    assert "n_group" in mq.last_error()
+    assert g(flags=64) == mq.MQ_ERR_INVALID
+    assert L.mq_gemm_nvfp4_prefill_grouped(a, None, 1, None, None, None, 4, 16, 0, None) == mq.MQ_ERR_INVALID
+    assert _grouped(L, a, None, [w, (P16, None, P16)], [P16, P16], [4, 4]) == mq.MQ_ERR_INVALID
+    assert _grouped(L, a, None, [w, w], [P16, None], [4, 4]) == mq.MQ_ERR_INVALID
+    assert "group 1" in mq.last_error()
+    assert _grouped(L, a, None, [w, w], [P16, P16], [4, 0]) == mq.MQ_ERR_SHAPE
+    assert g(K=40) == mq.MQ_ERR_SHAPE
+    assert _grouped(L, a, None, [w, w], [P16, P16], [1 << 30, 1 << 30], M=1) == mq.MQ_ERR_SHAPE
+    assert _grouped(L, a, None, [w, w], [P16, P8], [4, 4]) == mq.MQ_ERR_ALIGN
+    assert _grouped(L, a, None, [w, (P16, P1, P16)], [P16, P16], [4, 4]) == mq.MQ_ERR_ALIGN
+    assert _grouped(L, _q(None, None, P16), P8, [w], [P16], [4], flags=mq.MQ_A_FUSED_BF16) == mq.MQ_ERR_ALIGN
+
+
 def test_gemv_argument_errors(L):
     f = L.mq_gemv_bf16_decode
     assert f(None, P16, P16, 1, 4, 16, 0, None) == mq.MQ_ERR_INVALID
@@ -133,6 +163,8 @@ def test_valid_arguments_without_a_gpu_report_device_error(L):
     assert L.mq_gemm_nvfp4_prefill(_q(P16, P16, P16), None, _q(P16, P16, P16), P16, 4, 4, 16, 0,
                                    None) == mq.MQ_ERR_DEVICE
     assert L.mq_gemv_bf16_decode(P16, P16, P16, 1, 4, 16, 0, None) == mq.MQ_ERR_DEVICE
+    w = (P16, P16, P16)
+    assert _grouped(L, _q(P16, P16, P16), None, [w, w, w], [P16, P16, P16], [4, 8, 12]) == mq.MQ_ERR_DEVICE
     assert mq.last_error()
 
 

@@ -198,3 +198,69 @@ def test_bf16_output_is_nearest_even_rounding_of_f32_output(M, N, K):
     c32 = _gemm(qa, qw, M, N, f32=True).cpu().numpy()
     c16 = _gemm(qa, qw, M, N).view(torch.int16).cpu().numpy().view(np.uint16)
     assert np.array_equal(c16, workloads.f32_to_bf16_bits(c32))
+
+
+def _grouped(qa, x, ws, M, f32=False):
+    import torch
+    mq = _mq()
+    dt = torch.float32 if f32 else torch.bfloat16
+    cs = [torch.empty((M, w.shape[0]), dtype=dt, device="cuda") for w in ws]
+    flags = mq.MQ_OUT_F32 if f32 else 0
+    if x is not None:
+        flags |= mq.MQ_A_FUSED_BF16
+    mq.mq_gemm_nvfp4_prefill_grouped(qa, x, ws, cs, flags)
+    torch.cuda.synchronize()
+    return cs
+
+
+@pytest.mark.parametrize("M,Ns,K,seed", [
+    (300, (100, 260, 64), 512, 0),          # ragged groups, K % 128 == 0
+    (130, (512, 33), 4112, 1),               # ragged K
+    (257, (1024, 1024, 256, 16), 1024, 2),   # four groups
+    (64, (700,), 256, 3),                    # one group
+])
+def test_grouped_bit_identical_to_single_calls(M, Ns, K, seed):
+    # each output of the grouped launch must equal the single-weight call bit
+    # for bit (every element is accumulated in the same order whatever the
+    # tile shape); one group is also checked against the oracle
+    announce("gemm grouped vs single", M, Ns, K, seed)
+    import torch
+    mq = _mq()
+    xa = workloads.random_bf16((M, K), seed, 1.0, "lognormal_mixed")
+    xws = [workloads.random_bf16((n, K), seed + 20 + i, 0.02) for i, n in enumerate(Ns)]
+    x = to_dev_bf16(xa)
+    qa = mq.quantize(x)
+    ws = [mq.quantize(to_dev_bf16(xw)) for xw in xws]
+    for f32 in (False, True):
+        view = torch.int32 if f32 else torch.int16
+        cs = _grouped(qa, None, ws, M, f32)
+        for w, c in zip(ws, cs):
+            assert torch.equal(c.view(view), _gemm(qa, w, M, w.shape[0], f32=f32).view(view))
+        fs = _grouped(mq.NVFP4(None, None, torch.zeros(mq.REC_BYTES // 4, dtype=torch.int32, device="cuda")),
+                      x, ws, M, f32)
+        for c, f in zip(cs, fs):
+            assert torch.equal(c.view(view), f.view(view))
+    ref = oracle.gemm_nvfp4_ref(oracle.quantize_nvfp4(xa), oracle.quantize_nvfp4(xws[-1]))
+    _assert_rule_t(_out(cs[-1]), ref, False)
+
+
+def test_cfg2_grouped_gate_up_sampled():
+    # the launch the 8B-shape benchmark uses for the MLP input projections
+    announce("gemm cfg2 grouped gate+up")
+    import torch
+    mq = _mq()
+    xa = workloads.activation(2, "x_gu")
+    M, K = xa.shape
+    xws = [workloads.weight(2, p) for p in ("gate", "up")]
+    qa = mq.quantize(to_dev_bf16(xa))
+    ws = [mq.quantize(to_dev_bf16(xw)) for xw in xws]
+    cs = _grouped(qa, None, ws, M)
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([rng.choice(M, 192, replace=False), [0, M - 1]]))
+    oa = oracle.quantize_nvfp4(xa, rows=rows)
+    for xw, c in zip(xws, cs):
+        N = xw.shape[0]
+        cols = np.unique(np.concatenate([rng.choice(N, 384, replace=False), [0, N - 1]]))
+        ref = oracle.gemm_nvfp4_ref(oa, oracle.quantize_nvfp4(xw, rows=cols))
+        got = bf16_dev_to_f64(c[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+        _assert_rule_t(got, ref, True)
