@@ -17,7 +17,7 @@
 //
 // Data flow per workgroup (256 threads = 4 waves in a 2x2 grid, one wave per
 // SIMD; tile BM x BN; K advanced 128 elements = 8 groups per stage):
-//   HBM --direct-to-LDS loads (no registers)--> LDS ring of three stages
+//   HBM --direct-to-LDS loads (no registers)--> LDS ring of four stages
 //   (packed codes + scale bytes); the fused prologue and shapes with
 //   K % 128 != 0 go through registers instead
 //   LDS --16-byte reads--> registers: four dwords = codes of four K16 steps
@@ -39,11 +39,19 @@ constexpr int kRowStride = 64;     // LDS bytes per code row and stage
 constexpr int kScaleStride = 8;    // LDS bytes per scale row (8 groups)
 
 // Code rows in LDS hold four 16-byte chunks, chunk c of row r at position
-// c ^ swz(r).  Sixteen consecutive rows reading the same chunk then cover
-// every bank position of a 64-byte-row layout once per four rows (and once per
-// two rows for groups of eight), so the pipe's 16-byte reads are conflict
-// free, while whole rows stay contiguous for the direct-to-LDS copies.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// c ^ swz(r).  Four consecutive 64-byte rows already span the banks; the
+// swizzle moves rows r, r+4, r+8, r+12 (same banks) to different chunk
+// positions.  The pipe's 16-byte reads of 32 rows are then free of bank
+// conflicts on gfx950 (measured with SQ_LDS_BANK_CONFLICT; the row-pair
+// swizzle ((r>>1)^(r>>3))&3 doubled the LDS cycles), and whole rows stay
+// contiguous for the direct-to-LDS copies.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+
+// Scale bytes of a stage: 8 per row (groups g0..g7).  In LDS each block of
+// 32 rows is [dword 0 of rows 0..31 | dword 1 of rows 0..31] (256 bytes), so
+// the pipe's dword reads (row i, dword h) of 32 rows hit 32 consecutive
+// dwords per half-wave.
+__device__ __forceinline__ int scale_off(int row, int h) { return (row >> 5) * 256 + h * 128 + (row & 31) * 4; }
 
 // One launch computes C_g = A . W_g^T for up to kMaxGroup weights sharing A;
 // the column tiles of the groups follow each other (group g owns column
@@ -95,7 +103,8 @@ struct Smem {
   static constexpr int kAs = kW + BN * kRowStride;
   static constexpr int kWs = kAs + BM * kScaleStride;
   static constexpr int kStage = kWs + BN * kScaleStride;
-  static constexpr int kTotal = 3 * kStage;  // ring of three stages
+  static constexpr int kSlots = 4;            // ring of four stages
+  static constexpr int kTotal = kSlots * kStage;
 };
 
 
@@ -180,9 +189,10 @@ struct ScaleLoader {
     for (int j = 0; j < kPer; ++j) {
       const int r = threadIdx.x + kThreads * j;
       if (kFull || r < kRows) {
-        uint8_t* p = r < kA ? stage + Smem<BM, BN>::kAs + r * kScaleStride
-                            : stage + Smem<BM, BN>::kWs + (r - kA) * kScaleStride;
-        *(u32x2_t*)p = v[j];
+        uint8_t* p = r < kA ? stage + Smem<BM, BN>::kAs + scale_off(r, 0)
+                            : stage + Smem<BM, BN>::kWs + scale_off(r - kA, 0);
+        *(uint32_t*)p = v[j][0];
+        *(uint32_t*)(p + 128) = v[j][1];
       }
     }
   }
@@ -227,7 +237,7 @@ struct FusedALoader {
       uint32_t S = quantize_group16(w, s_t, lo, hi);
       const int chunk = (grp >> 1) ^ swz(row);
       *(u32x2_t*)(stage + Smem<BM, BN>::kA + row * kRowStride + chunk * 16 + (grp & 1) * 8) = u32x2_t{lo, hi};
-      stage[Smem<BM, BN>::kAs + row * kScaleStride + grp] = (uint8_t)S;
+      stage[Smem<BM, BN>::kAs + scale_off(row, grp >> 2) + (grp & 3)] = (uint8_t)S;
     }
   }
 };
@@ -236,8 +246,8 @@ struct FusedALoader {
 // buffer_load ... lds instruction fills a contiguous stretch of LDS, lane l
 // writing bytes [l*size, (l+1)*size) of it: 16 code rows (64 bytes each) per
 // 16-byte instruction, 32 scale rows (8 bytes) per 4-byte instruction.  The
-// chunk swizzle is applied by the choice of the global chunk each lane
-// copies.  The rows of a stage are A's then W's (WITH_A) or W's alone (fused
+// code swizzle and the scale block layout are applied by the choice of the
+// global piece each lane copies.  The rows of a stage are A's then W's (WITH_A) or W's alone (fused
 // prologue), contiguous in LDS.  Each operand is addressed through a buffer
 // resource covering exactly its tile's rows: the lane offset (one VGPR) is
 // fixed, the stage offset is a scalar, and an access outside the tile would
@@ -257,7 +267,8 @@ struct DmaLoader {
   static constexpr int kScale = kRows / 32 / 4;   // scale copies per wave
   static_assert(kCode * 64 == kRows && kScale * 128 == kRows, "tile rows");
   uint32_t coff[kCode], soff[kScale];
-  __amdgpu_buffer_rsrc_t ra, rw, rsa, rsw;
+  const uint8_t *a_c, *w_c, *a_s, *w_s;   // first row of each tile
+  int a_cb, w_cb, a_sb, w_sb;             // its valid bytes
   int wave;
 
   // Requires BM * K / 2 < 2^31 (checked by the host).
@@ -268,11 +279,15 @@ struct DmaLoader {
     const int ldc = K / 2, ng = K / kGroup;
     const int ma = min(BM, M - m0), nw = min(BN, N - n0);  // valid rows of the tiles
     if (WITH_A) {
-      ra = tile_rsrc(a_codes + (int64_t)m0 * ldc, (int64_t)ma * ldc);
-      rsa = tile_rsrc(a_scales + (int64_t)m0 * ng, (int64_t)ma * ng);
+      a_c = a_codes + (int64_t)m0 * ldc;
+      a_s = a_scales + (int64_t)m0 * ng;
+      a_cb = ma * ldc;
+      a_sb = ma * ng;
     }
-    rw = tile_rsrc(w_codes + (int64_t)n0 * ldc, (int64_t)nw * ldc);
-    rsw = tile_rsrc(w_scales + (int64_t)n0 * ng, (int64_t)nw * ng);
+    w_c = w_codes + (int64_t)n0 * ldc;
+    w_s = w_scales + (int64_t)n0 * ng;
+    w_cb = nw * ldc;
+    w_sb = nw * ng;
 #pragma unroll
     for (int j = 0; j < kCode; ++j) {
       const int r = 16 * (wave + 4 * j) + (lane >> 2);
@@ -281,13 +296,17 @@ struct DmaLoader {
     }
 #pragma unroll
     for (int j = 0; j < kScale; ++j) {
-      const int r = 32 * (wave + 4 * j) + (lane >> 1);
+      const int r = 32 * (wave + 4 * j) + (lane & 31);  // LDS dword lane = scale_off(r, lane >> 5)
       const int row = r < kRA ? min(r, ma - 1) : min(r - kRA, nw - 1);
-      soff[j] = (uint32_t)(row * ng + ((lane & 1) << 2));
+      soff[j] = (uint32_t)(row * ng + ((lane >> 5) << 2));
     }
   }
-  __device__ __forceinline__ void codes(uint8_t* stage, int kt) const {
+  // Stage kt into `stage`; with live false (a stage past the end) the
+  // resources cover no bytes, so the copies move no data (they write zeros).
+  __device__ __forceinline__ void codes(uint8_t* stage, int kt, bool live) const {
     uint8_t* lds = stage + (WITH_A ? Smem<BM, BN>::kA : Smem<BM, BN>::kW);
+    const __amdgpu_buffer_rsrc_t ra = tile_rsrc(WITH_A ? a_c : w_c, live ? (WITH_A ? a_cb : w_cb) : 0);
+    const __amdgpu_buffer_rsrc_t rw = tile_rsrc(w_c, live ? w_cb : 0);
 #pragma unroll
     for (int j = 0; j < kCode; ++j) {
       const int t = wave + 4 * j;
@@ -295,12 +314,14 @@ struct DmaLoader {
                                                (int)coff[j], kt * kRowBytes, 0, 0);
     }
   }
-  __device__ __forceinline__ void scales(uint8_t* stage, int kt) const {
+  __device__ __forceinline__ void scales(uint8_t* stage, int kt, bool live) const {
     uint8_t* lds = stage + (WITH_A ? Smem<BM, BN>::kAs : Smem<BM, BN>::kWs);
+    const __amdgpu_buffer_rsrc_t ra = tile_rsrc(WITH_A ? a_s : w_s, live ? (WITH_A ? a_sb : w_sb) : 0);
+    const __amdgpu_buffer_rsrc_t rw = tile_rsrc(w_s, live ? w_sb : 0);
 #pragma unroll
     for (int j = 0; j < kScale; ++j) {
       const int t = wave + 4 * j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(WITH_A && 32 * t < kRA ? rsa : rsw, (lds_void_t*)(lds + 256 * t), 4,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(WITH_A && 32 * t < kRA ? ra : rw, (lds_void_t*)(lds + 256 * t), 4,
                                                (int)soff[j], kt * 8, 0, 0);
     }
   }
@@ -362,8 +383,8 @@ struct WavePipe {
       a_off[q] = Smem<BM, BN>::kA + (wave_m + li) * kRowStride + (((2 * lh + q) ^ x) << 4);
       w_off[q] = Smem<BM, BN>::kW + (wave_n + li) * kRowStride + (((2 * lh + q) ^ x) << 4);
     }
-    as_off = Smem<BM, BN>::kAs + (wave_m + li) * kScaleStride + 4 * lh;
-    ws_off = Smem<BM, BN>::kWs + (wave_n + li) * kScaleStride + 4 * lh;
+    as_off = Smem<BM, BN>::kAs + scale_off(wave_m + li, lh);
+    ws_off = Smem<BM, BN>::kWs + scale_off(wave_n + li, lh);
   }
   // codes of steps 4Q..4Q+3
   template <int Q>
@@ -608,29 +629,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
   if constexpr (FAST) dma.init(args.a_codes, args.a_scales, grp.w_codes, grp.w_scales, M, N, K, m0, n0);
 
   auto load_stage = [&](uint8_t* stage, int kt) {
+    const int kc = kt < nk ? kt : nk - 1;
     if constexpr (FAST) {
-      dma.codes(stage, kt);
-      dma.scales(stage, kt);
+      dma.codes(stage, kc, kt < nk);
+      dma.scales(stage, kc, kt < nk);
     }
     if constexpr (FUSED) {
-      fa.load((const uint16_t*)args.a_bf16, m0, M, K, kt);
+      fa.load((const uint16_t*)args.a_bf16, m0, M, K, kc);
       fa.template quantize_store<BN>(stage, s_ta);
     } else if constexpr (!FAST) {
-      la.load(args.a_codes, m0, M, K, kt);
+      la.load(args.a_codes, m0, M, K, kc);
       la.store(stage + SM::kA);
     }
     if constexpr (!FAST) {
-      lw.load(grp.w_codes, n0, N, K, kt);
+      lw.load(grp.w_codes, n0, N, K, kc);
       lw.store(stage + SM::kW);
-      ls.load(args.a_scales, grp.w_scales, m0, n0, M, N, K, kt);
+      ls.load(args.a_scales, grp.w_scales, m0, n0, M, N, K, kc);
       ls.store(stage);
     }
   };
+  // direct copies issued per wave and stage (vmcnt units)
+  constexpr int kDma = FAST ? DmaLoader<BM, BN, !FUSED>::kCode + DmaLoader<BM, BN, !FUSED>::kScale : 0;
+  static_assert(kDma < 64, "vmcnt range");
+  constexpr int kWaitStage = 0x0070 | (kDma & 15) | ((kDma >> 4) << 14);  // vmcnt(kDma) lgkmcnt(0)
 
-  // prologue: stages 0 and 1 into LDS, the pipe primed with stage 0
+  // prologue: stages 0, 1 and 2 into LDS; stages 0 and 1 complete, the pipe
+  // primed with stage 0
   load_stage(smem, 0);
-  load_stage(smem + SM::kStage, nk > 1 ? 1 : 0);
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): direct-to-LDS copies included
+  load_stage(smem + SM::kStage, 1);
+  load_stage(smem + 2 * SM::kStage, 2);
+  __builtin_amdgcn_s_waitcnt(kWaitStage);
   __syncthreads();
   WavePipe<BM, BN> pipe;
   pipe.init(wave_m, wave_n, li, lh);
@@ -640,24 +668,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
   pipe.sigmas();
   pipe.template dequant<0, 0>();
 
-  // Ring of three LDS stages: stage kt is computed from slot kt%3 (its
-  // operands were read into registers during the previous stage), slot
-  // (kt+1)%3 is read for the next stage and slot (kt+2)%3 receives the stage
-  // after next.  Past the last stage the loads and reads are clamped to
-  // valid data and their results ignored, so the loop body has no branches.
+  // Ring of four LDS stages.  During stage kt: slot kt%4 is no longer read
+  // (its operands went to registers in the previous stage), slot (kt+1)%4 is
+  // read for the next stage, slot (kt+2)%4 is landing (copies issued in the
+  // previous stage) and slot (kt+3)%4 receives stage kt+3.  A copy thus has
+  // two stages to complete.  Past the last stage the register-path loads are
+  // clamped to valid data, the direct copies move nothing, and the reads'
+  // results are ignored, so the loop body has no branches.
   uint8_t* cur = smem;
   uint8_t* nxt = smem + SM::kStage;
-  uint8_t* slot = smem + 2 * SM::kStage;
+  uint8_t* nx2 = smem + 2 * SM::kStage;
+  uint8_t* slot = smem + 3 * SM::kStage;
   for (int kt = 0; kt < nk; ++kt) {
-    const int kf = kt + 2 < nk ? kt + 2 : nk - 1;
+    const bool live = kt + 3 < nk;
+    const int kf = live ? kt + 3 : nk - 1;
     auto fill = [&](int step) {
       if constexpr (FAST) {
-        if (step == 0) dma.codes(slot, kf);
-        if (step == 1) dma.scales(slot, kf);
+        // the fused A loads go first: waiting for them then does not wait
+        // for this stage's copies (vmcnt counts in issue order)
         if constexpr (FUSED) {
           if (step == 0) fa.load((const uint16_t*)args.a_bf16, m0, M, K, kf);
           if (step == 2) fa.template quantize_store<BN>(slot, s_ta);
         }
+        if (step == 0) dma.codes(slot, kf, live);
+        if (step == 1) dma.scales(slot, kf, live);
       } else {
         if (step == 0) {
           if (FUSED) fa.load((const uint16_t*)args.a_bf16, m0, M, K, kf);
@@ -682,17 +716,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
     run_step<5>(pipe, acc, nxt, fill);
     run_step<6>(pipe, acc, nxt, fill);
     run_step<7>(pipe, acc, nxt, fill);
-    // End of stage: the fill of the stage after next must be complete in LDS
-    // before any wave reads it: all direct copies (vmcnt) and all LDS writes.
-    // LDS operations complete in order and after the last fill write each
+    // End of stage: slot (kt+2)%4 must be complete in LDS before any wave
+    // reads it (next stage).  Its direct copies were issued in the previous
+    // stage, so all but this stage's kDma copies must have landed (vmcnt
+    // counts in issue order); register-path fills are written in this stage,
+    // and LDS operations complete in order: after the last fill write each
     // wave issued exactly TM + TN reads (the next stage's second chunk, from
-    // a slot nobody writes now), so those may stay in flight across the
-    // barrier.  (s_waitcnt: vmcnt 0, expcnt at its maximum.)
-    __builtin_amdgcn_s_waitcnt(0x0070 | ((TM + TN) << 8));
+    // a slot nobody writes now), which may stay in flight across the barrier.
+    __builtin_amdgcn_s_waitcnt((kWaitStage & ~0x0F00) | ((TM + TN) << 8));
     __builtin_amdgcn_s_barrier();
     uint8_t* done = cur;
     cur = nxt;
-    nxt = slot;
+    nxt = nx2;
+    nx2 = slot;
     slot = done;
   }
   epilogue<BM, BN, OUT_F32>(acc, smem, grp.c, M, N, m0, n0, wave, lane, scale);
