@@ -35,23 +35,19 @@ namespace mq {
 constexpr int kThreads = 256;
 constexpr int kBK = 128;            // K elements per stage
 constexpr int kRowBytes = kBK / 2;  // packed code bytes per row per stage
-constexpr int kRowStride = 64;     // LDS bytes per code row and stage
-constexpr int kScaleStride = 8;    // LDS bytes per scale row (8 groups)
+// An LDS ring slot holds two consecutive stages (a "double stage", 256 K
+// elements): per row 128 bytes of codes (one full cache line of the row-major
+// operand) and 16 bytes of scales, so the direct-to-LDS copies fetch whole
+// lines.
+constexpr int kRowStride = 2 * kRowBytes;  // 128: LDS bytes per code row of a slot
+constexpr int kScaleStride = 16;           // LDS bytes per scale row of a slot
 
-// Code rows in LDS hold four 16-byte chunks, chunk c of row r at position
-// c ^ swz(r).  Four consecutive 64-byte rows already span the banks; the
-// swizzle moves rows r, r+4, r+8, r+12 (same banks) to different chunk
-// positions.  The pipe's 16-byte reads of 32 rows are then free of bank
-// conflicts on gfx950 (measured with SQ_LDS_BANK_CONFLICT; the row-pair
-// swizzle ((r>>1)^(r>>3))&3 doubled the LDS cycles), and whole rows stay
-// contiguous for the direct-to-LDS copies.
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
-
-// Scale bytes of a stage: 8 per row (groups g0..g7).  In LDS each block of
-// 32 rows is [dword 0 of rows 0..31 | dword 1 of rows 0..31] (256 bytes), so
-// the pipe's dword reads (row i, dword h) of 32 rows hit 32 consecutive
-// dwords per half-wave.
-__device__ __forceinline__ int scale_off(int row, int h) { return (row >> 5) * 256 + h * 128 + (row & 31) * 4; }
+// Code rows in LDS hold eight 16-byte chunks (chunk 4p + c = chunk c of the
+// slot's stage p), chunk L of row r at position L ^ swz(r).  Two 128-byte rows
+// span the banks; the swizzle spreads rows r, r+2, ..., r+14 over all eight
+// positions, which a probe measured free of SQ_LDS_BANK_CONFLICT for the
+// pipe's 16-byte reads of 32 rows.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // One launch computes C_g = A . W_g^T for up to kMaxGroup weights sharing A;
 // the column tiles of the groups follow each other (group g owns column
@@ -102,9 +98,8 @@ struct Smem {
   static constexpr int kW = kA + BM * kRowStride;
   static constexpr int kAs = kW + BN * kRowStride;
   static constexpr int kWs = kAs + BM * kScaleStride;
-  static constexpr int kStage = kWs + BN * kScaleStride;
-  static constexpr int kSlots = 4;            // ring of four stages
-  static constexpr int kTotal = kSlots * kStage;
+  static constexpr int kSlot = kWs + BN * kScaleStride;
+  static constexpr int kTotal = 2 * kSlot;  // two slots = four stages
 };
 
 
@@ -138,13 +133,14 @@ struct PackedLoader {
       }
     }
   }
-  __device__ __forceinline__ void store(uint8_t* lds) const {
+  // into stage half p of a slot's code rows
+  __device__ __forceinline__ void store(uint8_t* lds, int p) const {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < kChunks; ++j) {
       const int c = tid + kThreads * j;
       const int row = c >> 2, col = c & 3;
-      *(u32x4_t*)(lds + row * kRowStride + ((col ^ swz(row)) << 4)) = code[j];
+      *(u32x4_t*)(lds + row * kRowStride + (((4 * p + col) ^ swz(row)) << 4)) = code[j];
     }
   }
 };
@@ -184,15 +180,15 @@ struct ScaleLoader {
       }
     }
   }
-  __device__ __forceinline__ void store(uint8_t* stage) const {
+  // into stage half h of a slot's scale rows
+  __device__ __forceinline__ void store(uint8_t* slot, int h) const {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int r = threadIdx.x + kThreads * j;
       if (kFull || r < kRows) {
-        uint8_t* p = r < kA ? stage + Smem<BM, BN>::kAs + scale_off(r, 0)
-                            : stage + Smem<BM, BN>::kWs + scale_off(r - kA, 0);
-        *(uint32_t*)p = v[j][0];
-        *(uint32_t*)(p + 128) = v[j][1];
+        uint8_t* p = r < kA ? slot + Smem<BM, BN>::kAs + r * kScaleStride
+                            : slot + Smem<BM, BN>::kWs + (r - kA) * kScaleStride;
+        *(u32x2_t*)(p + 8 * h) = v[j];
       }
     }
   }
@@ -224,9 +220,10 @@ struct FusedALoader {
       }
     }
   }
-  // Quantize the loaded groups into the stage's A codes and scale bytes.
+  // Quantize the loaded groups into stage half p of a slot's A codes and
+  // scale bytes.
   template <int BN>
-  __device__ __forceinline__ void quantize_store(uint8_t* stage, float s_t) const {
+  __device__ __forceinline__ void quantize_store(uint8_t* stage, int p, float s_t) const {
 #pragma unroll
     for (int j = 0; j < kGroupsPer; ++j) {
       const int gi = threadIdx.x + kThreads * j;
@@ -235,37 +232,41 @@ struct FusedALoader {
                        raw[j][1][0], raw[j][1][1], raw[j][1][2], raw[j][1][3]};
       uint32_t lo, hi;
       uint32_t S = quantize_group16(w, s_t, lo, hi);
-      const int chunk = (grp >> 1) ^ swz(row);
+      const int chunk = (4 * p + (grp >> 1)) ^ swz(row);
       *(u32x2_t*)(stage + Smem<BM, BN>::kA + row * kRowStride + chunk * 16 + (grp & 1) * 8) = u32x2_t{lo, hi};
-      stage[Smem<BM, BN>::kAs + scale_off(row, grp >> 2) + (grp & 3)] = (uint8_t)S;
+      stage[Smem<BM, BN>::kAs + row * kScaleStride + 8 * p + grp] = (uint8_t)S;
     }
   }
 };
 
-// Direct global->LDS copies of one stage (FAST shapes, K % 128 == 0).  One
-// buffer_load ... lds instruction fills a contiguous stretch of LDS, lane l
-// writing bytes [l*size, (l+1)*size) of it: 16 code rows (64 bytes each) per
-// 16-byte instruction, 32 scale rows (8 bytes) per 4-byte instruction.  The
-// code swizzle and the scale block layout are applied by the choice of the
-// global piece each lane copies.  The rows of a stage are A's then W's (WITH_A) or W's alone (fused
-// prologue), contiguous in LDS.  Each operand is addressed through a buffer
-// resource covering exactly its tile's rows: the lane offset (one VGPR) is
-// fixed, the stage offset is a scalar, and an access outside the tile would
-// read zeros rather than other memory.
+// Direct global->LDS copies of one double stage (FAST shapes, K % 256 == 0).
+// One buffer_load ... lds instruction fills a contiguous kilobyte of LDS,
+// lane l writing bytes [16l, 16l + 16): 8 code rows of 128 bytes (8 lanes
+// per row, one full line each) or 64 scale rows of 16 bytes.  The chunk
+// swizzle is applied by the choice of the global chunk each lane copies.
+// Tiles whose row count is not a multiple of 256 copy scales in 4-byte
+// pieces instead (4 lanes per row, 16 rows per instruction), which keeps the
+// instruction count per wave whole.  The rows of a slot are A's then W's
+// (WITH_A) or W's alone (fused prologue), contiguous in LDS.  Each operand is
+// addressed through a buffer resource covering exactly its tile's valid rows:
+// the lane offsets are fixed, the double-stage offset is a scalar, and rows
+// past the matrix read zeros rather than other memory.
 typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, kBufferWord3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kBufferWord3);
 }
 
 template <int BM, int BN, bool WITH_A>
 struct DmaLoader {
   static constexpr int kRA = WITH_A ? BM : 0;
   static constexpr int kRows = kRA + BN;
-  static constexpr int kCode = kRows / 16 / 4;    // code copies per wave
-  static constexpr int kScale = kRows / 32 / 4;   // scale copies per wave
-  static_assert(kCode * 64 == kRows && kScale * 128 == kRows, "tile rows");
+  static constexpr int kCode = kRows / 8 / 4;             // code copies per wave
+  static constexpr int kScaleBytes = kRows % 256 == 0 ? 16 : 4;
+  static constexpr int kScaleRowsPer = 64 * kScaleBytes / kScaleStride;  // rows per scale copy
+  static constexpr int kScale = kRows / kScaleRowsPer / 4;  // scale copies per wave
+  static_assert(kCode * 32 == kRows && kScale * 4 * kScaleRowsPer == kRows, "tile rows");
   uint32_t coff[kCode], soff[kScale];
   const uint8_t *a_c, *w_c, *a_s, *w_s;   // first row of each tile
   int a_cb, w_cb, a_sb, w_sb;             // its valid bytes
@@ -288,41 +289,50 @@ struct DmaLoader {
     w_s = w_scales + (int64_t)n0 * ng;
     w_cb = nw * ldc;
     w_sb = nw * ng;
+    // rows past the valid ones fall outside the resource and read zeros
 #pragma unroll
     for (int j = 0; j < kCode; ++j) {
-      const int r = 16 * (wave + 4 * j) + (lane >> 2);
-      const int row = r < kRA ? min(r, ma - 1) : min(r - kRA, nw - 1);  // clamped rows are discarded later
-      coff[j] = (uint32_t)(row * ldc + (((lane & 3) ^ swz(r)) << 4));
+      const int r = 8 * (wave + 4 * j) + (lane >> 3);
+      const int row = r < kRA ? r : r - kRA;
+      coff[j] = (uint32_t)(row * ldc + (((lane & 7) ^ swz(r)) << 4));
     }
 #pragma unroll
     for (int j = 0; j < kScale; ++j) {
-      const int r = 32 * (wave + 4 * j) + (lane & 31);  // LDS dword lane = scale_off(r, lane >> 5)
-      const int row = r < kRA ? min(r, ma - 1) : min(r - kRA, nw - 1);
-      soff[j] = (uint32_t)(row * ng + ((lane >> 5) << 2));
+      const int t = wave + 4 * j;
+      const int r = kScaleBytes == 16 ? 64 * t + lane : 16 * t + (lane >> 2);
+      const int row = r < kRA ? r : r - kRA;
+      soff[j] = (uint32_t)(row * ng + (kScaleBytes == 16 ? 0 : (lane & 3) << 2));
     }
   }
-  // Stage kt into `stage`; with live false (a stage past the end) the
+  // Double stage ds into `slot`; with live false (past the end) the
   // resources cover no bytes, so the copies move no data (they write zeros).
-  __device__ __forceinline__ void codes(uint8_t* stage, int kt, bool live) const {
-    uint8_t* lds = stage + (WITH_A ? Smem<BM, BN>::kA : Smem<BM, BN>::kW);
+  // Copies j with j % nparts == part are issued (the stage spreads them).
+  __device__ __forceinline__ void codes(uint8_t* slot, int ds, bool live, int part, int nparts) const {
+    uint8_t* lds = slot + (WITH_A ? Smem<BM, BN>::kA : Smem<BM, BN>::kW);
     const __amdgpu_buffer_rsrc_t ra = tile_rsrc(WITH_A ? a_c : w_c, live ? (WITH_A ? a_cb : w_cb) : 0);
     const __amdgpu_buffer_rsrc_t rw = tile_rsrc(w_c, live ? w_cb : 0);
 #pragma unroll
     for (int j = 0; j < kCode; ++j) {
+      if (j % nparts != part) continue;
       const int t = wave + 4 * j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(WITH_A && 16 * t < kRA ? ra : rw, (lds_void_t*)(lds + 1024 * t), 16,
-                                               (int)coff[j], kt * kRowBytes, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(WITH_A && 8 * t < kRA ? ra : rw, (lds_void_t*)(lds + 1024 * t), 16,
+                                               (int)coff[j], ds * kRowStride, 0, 0);
     }
   }
-  __device__ __forceinline__ void scales(uint8_t* stage, int kt, bool live) const {
-    uint8_t* lds = stage + (WITH_A ? Smem<BM, BN>::kAs : Smem<BM, BN>::kWs);
+  __device__ __forceinline__ void scales(uint8_t* slot, int ds, bool live) const {
+    uint8_t* lds = slot + (WITH_A ? Smem<BM, BN>::kAs : Smem<BM, BN>::kWs);
     const __amdgpu_buffer_rsrc_t ra = tile_rsrc(WITH_A ? a_s : w_s, live ? (WITH_A ? a_sb : w_sb) : 0);
     const __amdgpu_buffer_rsrc_t rw = tile_rsrc(w_s, live ? w_sb : 0);
 #pragma unroll
     for (int j = 0; j < kScale; ++j) {
       const int t = wave + 4 * j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(WITH_A && 32 * t < kRA ? ra : rw, (lds_void_t*)(lds + 256 * t), 4,
-                                               (int)soff[j], kt * 8, 0, 0);
+      const __amdgpu_buffer_rsrc_t r = WITH_A && kScaleRowsPer * t < kRA ? ra : rw;
+      if constexpr (kScaleBytes == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds + 1024 * t), 16, (int)soff[j],
+                                                 ds * kScaleStride, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds + 256 * t), 4, (int)soff[j],
+                                                 ds * kScaleStride, 0, 0);
     }
   }
 };
@@ -363,9 +373,10 @@ __device__ __forceinline__ half2_t sigma_pair(uint32_t scale_dword, uint32_t sel
 // eight codes at byte 32h + 4s of its fragment row (K elements 64h + 8s ..
 // +7, group 4h + s/2): the two lane halves split the stage's K range, so a
 // step's 16 K elements are 8 from each half, the same for A and W.  Codes
-// come from LDS four steps at a time (logical chunk 2h + q for steps
+// come from LDS four steps at a time (chunk 2h + q of the stage for steps
 // 4q..4q+3), each chunk into its own buffer; the lane's four scales are
-// dword h of the row's eight scale bytes.
+// dword h of the stage's eight scale bytes of the row.  A stage is half P of
+// an LDS slot.
 template <int BM, int BN>
 struct WavePipe {
   static constexpr int TM = BM / 64, TN = BN / 64;
@@ -373,32 +384,35 @@ struct WavePipe {
   uint32_t sa[TM], sw[TN];        // the lane's four scale bytes per fragment
   half2_t pa[2][TM], pw[2][TN];   // sigma pairs, sub-chunks 0 and 1
   half8_t oa[2][TM], ow[2][TN];   // dequantized operands, double-buffered
-  int a_off[2], w_off[2], as_off, ws_off;
+  int a_off[2][2], w_off[2][2], as_off, ws_off;  // [stage half][chunk buffer]
 
   __device__ __forceinline__ void init(int wave_m, int wave_n, int li, int lh) {
     // fragment rows differ by multiples of 32, which leave swz unchanged
     const int x = swz(li);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      a_off[q] = Smem<BM, BN>::kA + (wave_m + li) * kRowStride + (((2 * lh + q) ^ x) << 4);
-      w_off[q] = Smem<BM, BN>::kW + (wave_n + li) * kRowStride + (((2 * lh + q) ^ x) << 4);
-    }
-    as_off = Smem<BM, BN>::kAs + scale_off(wave_m + li, lh);
-    ws_off = Smem<BM, BN>::kWs + scale_off(wave_n + li, lh);
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        a_off[p][q] = Smem<BM, BN>::kA + (wave_m + li) * kRowStride + (((4 * p + 2 * lh + q) ^ x) << 4);
+        w_off[p][q] = Smem<BM, BN>::kW + (wave_n + li) * kRowStride + (((4 * p + 2 * lh + q) ^ x) << 4);
+      }
+    as_off = Smem<BM, BN>::kAs + (wave_m + li) * kScaleStride + 4 * lh;
+    ws_off = Smem<BM, BN>::kWs + (wave_n + li) * kScaleStride + 4 * lh;
   }
-  // codes of steps 4Q..4Q+3
-  template <int Q>
-  __device__ __forceinline__ void read_chunk(const uint8_t* stage) {
+  // codes of steps 4Q..4Q+3 of stage half P of a slot
+  template <int P, int Q>
+  __device__ __forceinline__ void read_chunk(const uint8_t* slot) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) ca[Q][i] = *(const u32x4_t*)(stage + a_off[Q] + i * 32 * kRowStride);
+    for (int i = 0; i < TM; ++i) ca[Q][i] = *(const u32x4_t*)(slot + a_off[P][Q] + i * 32 * kRowStride);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) cw[Q][j] = *(const u32x4_t*)(stage + w_off[Q] + j * 32 * kRowStride);
+    for (int j = 0; j < TN; ++j) cw[Q][j] = *(const u32x4_t*)(slot + w_off[P][Q] + j * 32 * kRowStride);
   }
-  __device__ __forceinline__ void read_scales(const uint8_t* stage) {
+  template <int P>
+  __device__ __forceinline__ void read_scales(const uint8_t* slot) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sa[i] = *(const uint32_t*)(stage + as_off + i * 32 * kScaleStride);
+    for (int i = 0; i < TM; ++i) sa[i] = *(const uint32_t*)(slot + as_off + 8 * P + i * 32 * kScaleStride);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) sw[j] = *(const uint32_t*)(stage + ws_off + j * 32 * kScaleStride);
+    for (int j = 0; j < TN; ++j) sw[j] = *(const uint32_t*)(slot + ws_off + 8 * P + j * 32 * kScaleStride);
   }
   __device__ __forceinline__ void sigmas() {
 #pragma unroll
@@ -446,17 +460,17 @@ __device__ __forceinline__ void interleave() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Step S of a stage: LDS reads for the next stage (first chunk in step 3,
-// scales in step 4, second chunk in step 7, each after the buffer's last use
-// in this stage), dequantization of step S+1 (or of the next stage's step 0),
-// the MFMAs of step S, and step S's part of the fill of the stage after next.
-template <int S, int BM, int BN, typename Fill>
+// Step S of a stage: LDS reads for the next stage (half PN of slot nxt:
+// first chunk in step 3, scales in step 4, second chunk in step 7, each after
+// the buffer's last use in this stage), dequantization of step S+1 (or of the
+// next stage's step 0), the MFMAs of step S, and step S's part of the fills.
+template <int S, int PN, int BM, int BN, typename Fill>
 __device__ __forceinline__ void run_step(WavePipe<BM, BN>& p, f32x16_t (&acc)[BM / 64][BN / 64],
                                          const uint8_t* nxt, Fill& fill) {
   constexpr int TM = BM / 64, TN = BN / 64, NM = TM * TN, ND = 8 * (TM + TN);
-  if (S == 3) p.template read_chunk<0>(nxt);
-  if (S == 4) p.read_scales(nxt);
-  if (S == 7) p.template read_chunk<1>(nxt);
+  if (S == 3) p.template read_chunk<PN, 0>(nxt);
+  if (S == 4) p.template read_scales<PN>(nxt);
+  if (S == 7) p.template read_chunk<PN, 1>(nxt);
   if (S == 7) p.sigmas();  // the next stage's; this stage's were last used in step 6
   if (S < 7) p.template dequant<(S + 1) & 7, (S + 1) & 1>();
   else p.template dequant<0, 0>();
@@ -628,108 +642,133 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
   ScaleLoader<BM, BN, FAST, !FUSED> ls;
   if constexpr (FAST) dma.init(args.a_codes, args.a_scales, grp.w_codes, grp.w_scales, M, N, K, m0, n0);
 
-  auto load_stage = [&](uint8_t* stage, int kt) {
-    const int kc = kt < nk ? kt : nk - 1;
-    if constexpr (FAST) {
-      dma.codes(stage, kc, kt < nk);
-      dma.scales(stage, kc, kt < nk);
-    }
-    if constexpr (FUSED) {
-      fa.load((const uint16_t*)args.a_bf16, m0, M, K, kc);
-      fa.template quantize_store<BN>(stage, s_ta);
-    } else if constexpr (!FAST) {
-      la.load(args.a_codes, m0, M, K, kc);
-      la.store(stage + SM::kA);
-    }
+  // Register-path fill of stage k into half (k & 1) of a slot.  FAST (only
+  // the fused A tile goes this way) clamps k to the last stage; the ragged
+  // loaders' bounds checks zero a stage past the end instead, which lets an
+  // odd stage count finish on a zero half.
+  auto reg_load = [&](int k) __attribute__((always_inline)) {
+    const int kc = FAST ? min(k, nk - 1) : k;
+    if constexpr (FUSED) fa.load((const uint16_t*)args.a_bf16, m0, M, K, kc);
+    else if constexpr (!FAST) la.load(args.a_codes, m0, M, K, kc);
+  };
+  auto reg_store = [&](uint8_t* slot, int k) __attribute__((always_inline)) {
+    if constexpr (FUSED) fa.template quantize_store<BN>(slot, k & 1, s_ta);
+    else if constexpr (!FAST) la.store(slot + SM::kA, k & 1);
+  };
+  auto load_stage_reg = [&](uint8_t* slot, int k) __attribute__((always_inline)) {
+    reg_load(k);
+    reg_store(slot, k);
     if constexpr (!FAST) {
-      lw.load(grp.w_codes, n0, N, K, kc);
-      lw.store(stage + SM::kW);
-      ls.load(args.a_scales, grp.w_scales, m0, n0, M, N, K, kc);
-      ls.store(stage);
+      lw.load(grp.w_codes, n0, N, K, k);
+      lw.store(slot + SM::kW, k & 1);
+      ls.load(args.a_scales, grp.w_scales, m0, n0, M, N, K, k);
+      ls.store(slot, k & 1);
     }
   };
-  // direct copies issued per wave and stage (vmcnt units)
-  constexpr int kDma = FAST ? DmaLoader<BM, BN, !FUSED>::kCode + DmaLoader<BM, BN, !FUSED>::kScale : 0;
-  static_assert(kDma < 64, "vmcnt range");
-  constexpr int kWaitStage = 0x0070 | (kDma & 15) | ((kDma >> 4) << 14);  // vmcnt(kDma) lgkmcnt(0)
+  const int nd = (nk + 1) / 2;  // double stages (FAST shapes have nk even)
 
-  // prologue: stages 0, 1 and 2 into LDS; stages 0 and 1 complete, the pipe
-  // primed with stage 0
-  load_stage(smem, 0);
-  load_stage(smem + SM::kStage, 1);
-  load_stage(smem + 2 * SM::kStage, 2);
-  __builtin_amdgcn_s_waitcnt(kWaitStage);
+  // prologue: double stages 0 and 1 into the two slots (stage 3, the second
+  // half of slot 1, comes from the register path in stage 0), then the pipe
+  // is primed with stage 0
+  if constexpr (FAST) {
+    dma.codes(smem, 0, true, 0, 1);
+    dma.scales(smem, 0, true);
+    dma.codes(smem + SM::kSlot, 1, nd > 1, 0, 1);
+    dma.scales(smem + SM::kSlot, 1, nd > 1);
+  }
+  if constexpr (FUSED || !FAST) {
+    load_stage_reg(smem, 0);
+    load_stage_reg(smem, 1);
+    load_stage_reg(smem + SM::kSlot, 2);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): direct-to-LDS copies included
   __syncthreads();
   WavePipe<BM, BN> pipe;
   pipe.init(wave_m, wave_n, li, lh);
-  pipe.template read_chunk<0>(smem);
-  pipe.template read_chunk<1>(smem);
-  pipe.read_scales(smem);
+  pipe.template read_chunk<0, 0>(smem);
+  pipe.template read_chunk<0, 1>(smem);
+  pipe.template read_scales<0>(smem);
   pipe.sigmas();
   pipe.template dequant<0, 0>();
 
-  // Ring of four LDS stages.  During stage kt: slot kt%4 is no longer read
-  // (its operands went to registers in the previous stage), slot (kt+1)%4 is
-  // read for the next stage, slot (kt+2)%4 is landing (copies issued in the
-  // previous stage) and slot (kt+3)%4 receives stage kt+3.  A copy thus has
-  // two stages to complete.  Past the last stage the register-path loads are
-  // clamped to valid data, the direct copies move nothing, and the reads'
-  // results are ignored, so the loop body has no branches.
+  // Two LDS slots of two stages each.  In double stage d (slot cur; slot nxt
+  // holds d+1):
+  //  - even stage 2d pre-reads stage 2d+1 (cur, half 1); the register path
+  //    fills stage 2d+3 (nxt, half 1).  It ends with every wave's copies and
+  //    LDS operations complete and a barrier: afterwards slot nxt is whole
+  //    and nobody reads slot cur any more.
+  //  - odd stage 2d+1 pre-reads stage 2d+2 (nxt, half 0) and fills slot cur
+  //    with double stage d+2: direct copies (two stages to land, before the
+  //    next even barrier) and, on the register path, stage 2d+4 (half 0).
+  //    No barrier: the next writes to slot nxt come after the next one.
+  // Past the end the copies move nothing and register loads are clamped or
+  // zeroed; the reads' results are then ignored, so the loop has no branches.
   uint8_t* cur = smem;
-  uint8_t* nxt = smem + SM::kStage;
-  uint8_t* nx2 = smem + 2 * SM::kStage;
-  uint8_t* slot = smem + 3 * SM::kStage;
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool live = kt + 3 < nk;
-    const int kf = live ? kt + 3 : nk - 1;
-    auto fill = [&](int step) {
-      if constexpr (FAST) {
-        // the fused A loads go first: waiting for them then does not wait
-        // for this stage's copies (vmcnt counts in issue order)
-        if constexpr (FUSED) {
-          if (step == 0) fa.load((const uint16_t*)args.a_bf16, m0, M, K, kf);
-          if (step == 2) fa.template quantize_store<BN>(slot, s_ta);
+  uint8_t* nxt = smem + SM::kSlot;
+  for (int d = 0; d < nd; ++d) {
+    const int k0 = 2 * d;
+    auto fill_even = [&](int step) __attribute__((always_inline)) {
+      if constexpr (FUSED || !FAST) {
+        const int k = k0 + 3;
+        if (step == 0) reg_load(k);
+        if (step == 2) {
+          reg_store(nxt, k);
+          if constexpr (!FAST) lw.load(grp.w_codes, n0, N, K, k);
         }
-        if (step == 0) dma.codes(slot, kf, live);
-        if (step == 1) dma.scales(slot, kf, live);
-      } else {
-        if (step == 0) {
-          if (FUSED) fa.load((const uint16_t*)args.a_bf16, m0, M, K, kf);
-          else la.load(args.a_codes, m0, M, K, kf);
-        } else if (step == 2) {
-          if (FUSED) fa.template quantize_store<BN>(slot, s_ta);
-          else la.store(slot + SM::kA);
-          lw.load(grp.w_codes, n0, N, K, kf);
-        } else if (step == 4) {
-          lw.store(slot + SM::kW);
-          ls.load(args.a_scales, grp.w_scales, m0, n0, M, N, K, kf);
-        } else if (step == 6) {
-          ls.store(slot);
+        if constexpr (!FAST) {
+          if (step == 4) {
+            lw.store(nxt + SM::kW, 1);
+            ls.load(args.a_scales, grp.w_scales, m0, n0, M, N, K, k);
+          }
+          if (step == 6) ls.store(nxt, 1);
         }
       }
     };
-    run_step<0>(pipe, acc, nxt, fill);
-    run_step<1>(pipe, acc, nxt, fill);
-    run_step<2>(pipe, acc, nxt, fill);
-    run_step<3>(pipe, acc, nxt, fill);
-    run_step<4>(pipe, acc, nxt, fill);
-    run_step<5>(pipe, acc, nxt, fill);
-    run_step<6>(pipe, acc, nxt, fill);
-    run_step<7>(pipe, acc, nxt, fill);
-    // End of stage: slot (kt+2)%4 must be complete in LDS before any wave
-    // reads it (next stage).  Its direct copies were issued in the previous
-    // stage, so all but this stage's kDma copies must have landed (vmcnt
-    // counts in issue order); register-path fills are written in this stage,
-    // and LDS operations complete in order: after the last fill write each
-    // wave issued exactly TM + TN reads (the next stage's second chunk, from
-    // a slot nobody writes now), which may stay in flight across the barrier.
-    __builtin_amdgcn_s_waitcnt((kWaitStage & ~0x0F00) | ((TM + TN) << 8));
+    auto fill_odd = [&](int step) __attribute__((always_inline)) {
+      if constexpr (FUSED || !FAST) {
+        // register loads first: waiting for them then does not wait for
+        // this stage's direct copies (vmcnt counts in issue order)
+        const int k = k0 + 4;
+        if (step == 0) reg_load(k);
+        if (step == 2) {
+          reg_store(cur, k);
+          if constexpr (!FAST) lw.load(grp.w_codes, n0, N, K, k);
+        }
+        if constexpr (!FAST) {
+          if (step == 4) {
+            lw.store(cur + SM::kW, 0);
+            ls.load(args.a_scales, grp.w_scales, m0, n0, M, N, K, k);
+          }
+          if (step == 6) ls.store(cur, 0);
+        }
+      }
+      if constexpr (FAST) {
+        const bool live = d + 2 < nd;
+        if (step < 4) dma.codes(cur, d + 2, live, step, 4);
+        if (step == 4) dma.scales(cur, d + 2, live);
+      }
+    };
+    run_step<0, 1>(pipe, acc, cur, fill_even);
+    run_step<1, 1>(pipe, acc, cur, fill_even);
+    run_step<2, 1>(pipe, acc, cur, fill_even);
+    run_step<3, 1>(pipe, acc, cur, fill_even);
+    run_step<4, 1>(pipe, acc, cur, fill_even);
+    run_step<5, 1>(pipe, acc, cur, fill_even);
+    run_step<6, 1>(pipe, acc, cur, fill_even);
+    run_step<7, 1>(pipe, acc, cur, fill_even);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    uint8_t* done = cur;
+    run_step<0, 0>(pipe, acc, nxt, fill_odd);
+    run_step<1, 0>(pipe, acc, nxt, fill_odd);
+    run_step<2, 0>(pipe, acc, nxt, fill_odd);
+    run_step<3, 0>(pipe, acc, nxt, fill_odd);
+    run_step<4, 0>(pipe, acc, nxt, fill_odd);
+    run_step<5, 0>(pipe, acc, nxt, fill_odd);
+    run_step<6, 0>(pipe, acc, nxt, fill_odd);
+    run_step<7, 0>(pipe, acc, nxt, fill_odd);
+    uint8_t* t = cur;
     cur = nxt;
-    nxt = nx2;
-    nx2 = slot;
-    slot = done;
+    nxt = t;
   }
   epilogue<BM, BN, OUT_F32>(acc, smem, grp.c, M, N, m0, n0, wave, lane, scale);
 }
@@ -760,13 +799,15 @@ static hipError_t launch_cfg(const GemmArgs& a0, int dev, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The fast variant needs whole stages (K % 128 == 0) and buffer offsets of a
-// 256-row tile below 2^31 (256 * K/2 < 2^31).
-static bool fast_shape(int64_t K) { return K % kBK == 0 && K < (int64_t(1) << 24); }
+// The fast variant needs whole double stages (K % 256 == 0) and buffer
+// offsets of a 256-row tile below 2^31 (256 * K/2 < 2^31).
+static bool fast_shape(int64_t K) { return K % (2 * kBK) == 0 && K < (int64_t(1) << 24); }
 
 template <int BM, int BN, bool FUSED>
 static hipError_t dispatch_flags(const GemmArgs& a, bool out_f32, int d, hipStream_t s) {
-  const bool fast = fast_shape(a.K);
+  // the 16-byte scale copies want 16-byte aligned scale rows
+  bool fast = fast_shape(a.K) && (a.a_bf16 || ((uintptr_t)a.a_scales & 15) == 0);
+  for (int g = 0; g < a.ngroup; ++g) fast = fast && ((uintptr_t)a.w_scales[g] & 15) == 0;
   if (fast) return out_f32 ? launch_cfg<BM, BN, true, true, FUSED>(a, d, s) : launch_cfg<BM, BN, true, false, FUSED>(a, d, s);
   return out_f32 ? launch_cfg<BM, BN, false, true, FUSED>(a, d, s) : launch_cfg<BM, BN, false, false, FUSED>(a, d, s);
 }
