@@ -6,27 +6,160 @@
 // workers) runs on the original BF16 weights.  With M <= 32 rows of X the
 // work is bound by streaming W from HBM (2 bytes per weight, M flops/byte),
 // so the kernel is organised around W's bytes:
-//   - a workgroup owns 16 rows of W and all of K; its NW waves split K in
-//     interleaved 128-element chunks, so the whole chip streams W with many
-//     16-byte loads in flight;
-//   - each lane reads 64 contiguous bytes of one W row per chunk and feeds
-//     them to v_mfma_f32_16x16x32_bf16 (W rows as the 16-row operand, X^T
-//     as the 16-column operand; up to two column tiles for M <= 32).  The
-//     MFMA is used for its fp32 accumulation of exact bf16 products, not for
-//     its rate: the kernel stays HBM-bound;
-//   - the K order inside a chunk is permuted identically for W and X;
+//   - a workgroup owns 16 rows of W and all of K; its four waves take the
+//     K chunks (128 elements = 256 bytes per row) in turn;
+//   - each wave has a ring of LDS buffers, one chunk each: the chunk's 16 W
+//     rows and the matching X pieces (16 rows per column tile) arrive by
+//     buffer_load ... lds, every instruction copying four rows of 256 bytes
+//     (whole cache lines), kGvBuf - 1 chunks ahead of use; rows past N or M
+//     and elements past K read zeros through the buffer resources;
+//   - the wave reads the chunk back in MFMA layout (16-byte piece L of row r
+//     sits at position L ^ (r & 15), so 16 rows hit distinct banks) and
+//     feeds v_mfma_f32_16x16x32_bf16 with W rows as the 16-row operand and
+//     X^T as the 16-column operand (up to two column tiles for M <= 32); the
+//     MFMA is used for its fp32 accumulation of exact bf16 products, not its
+//     rate;
+//   - the K order inside a chunk is the same for W and X;
 //   - the per-wave partial tiles are summed through LDS in a fixed order
-//     (deterministic), scaled to bf16 with round-to-nearest-even and stored.
+//     (deterministic), rounded to bf16 (nearest-even) and stored.
 #include "mq_device.h"
 #include "mq_internal.h"
 
 namespace mq {
 
-constexpr int kGvChunk = 128;  // K elements per wave per chunk
+constexpr int kGvChunk = 128;                    // K elements per chunk
+constexpr int kGvRowBytes = 2 * kGvChunk;        // bytes per row and chunk
+constexpr int kGvWaves = 4;                      // waves per workgroup (split K)
+constexpr int kGvBuf = 3;                        // LDS chunk buffers per wave
+constexpr int kGvTile = 16 * kGvRowBytes;        // 4 KB: 16 rows of one chunk
+constexpr int kGvBufferWord3 = 0x00020000;       // raw buffer, 32-bit data format
+typedef __attribute__((address_space(3))) void gv_lds_t;
+
+// 16 bytes from LDS, complete on return.  Written as one asm block (the read
+// and its wait together) because the compiler, seeing an ordinary LDS load
+// after the direct-to-LDS copies, waits for every copy in flight (vmcnt(0))
+// and so would drain the prefetch at each chunk; the copies this read needs
+// have been waited for explicitly.
+__device__ __forceinline__ uint4 lds_read16(const uint8_t* p) {
+  u32x4_t r;
+  const uint32_t a = (uint32_t)(uintptr_t)p;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(a) : "memory");
+  return __builtin_bit_cast(uint4, r);
+}
+
+template <int MT>
+constexpr int gv_lds_bytes() { return kGvWaves * kGvBuf * (1 + MT) * kGvTile; }
+
+template <int MT>
+__global__ __launch_bounds__(kGvWaves * 64) void gemv_bf16_kernel(const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ w,
+                                                                uint16_t* __restrict__ y, int M, int N, int K) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr int kBufBytes = (1 + MT) * kGvTile;  // W tile, then MT X tiles
+  constexpr int kCopies = 4 * (1 + MT);          // copy instructions per chunk
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int i = lane & 15, h = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  // the host guarantees 32 * K * 2 < 2^31
+  const uint16_t* wtile = w + (int64_t)n0 * K;
+  const int wbytes = min(16, N - n0) * K * 2, xbytes = M * K * 2;
+  // copy j of a chunk covers rows 4(j%4) .. +3 of its tile (tile j/4: W, then
+  // the X column tiles); lane l: row r = 4(j%4) + l/16, LDS piece l%16 holds
+  // logical piece (l%16) ^ r, i.e. K elements k0 + 8((l%16) ^ r) .. +7.  K is
+  // a multiple of the chunk, so no piece lies past K.
+  uint32_t off[kCopies];
+#pragma unroll
+  for (int j = 0; j < kCopies; ++j) {
+    const int r = 4 * (j % 4) + (lane >> 4), tile = j / 4;
+    const int row = tile == 0 ? r : 16 * (tile - 1) + r;  // row of W (tile) or of X
+    off[j] = (uint32_t)(row * K + 8 * ((lane & 15) ^ r)) * 2u;
+  }
+  uint8_t* ring = lds + wave * kGvBuf * kBufBytes;
+  const int nchunks = (K + kGvChunk - 1) / kGvChunk;
+  const int mine = nchunks > wave ? (nchunks - wave + kGvWaves - 1) / kGvWaves : 0;  // this wave's chunks
+  // This wave's t-th chunk into buffer dst.  Past the share the resources
+  // cover no bytes (zeros, no memory traffic).
+  auto copy = [&](int t, uint8_t* dst) __attribute__((always_inline)) {
+    const bool live = t < mine;
+    const int k0 = (wave + kGvWaves * t) * kGvChunk;
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc((void*)wtile, 0, live ? wbytes : 0, kGvBufferWord3);
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, live ? xbytes : 0, kGvBufferWord3);
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(j < 4 ? rw : rx, (gv_lds_t*)(dst + 1024 * j), 16, (int)off[j],
+                                               live ? k0 * 2 : 0, 0, 0);
+  };
+
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int u = 0; u < MT; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Copies run two chunks ahead through three buffers that rotate; before
+  // chunk t is read, every copy but the newest chunk's two groups must have
+  // landed (vmcnt counts in issue order).  The buffer refilled at step t was
+  // read at step t - 1, and those reads completed before their MFMAs.
+  // Chunks past this wave's share compute on zeros.
+  static_assert(kGvBuf == 3, "three rotating buffers");
+  uint8_t* cur = ring;
+  uint8_t* nx1 = ring + kBufBytes;
+  uint8_t* nx2 = ring + 2 * kBufBytes;
+  copy(0, cur);
+  copy(1, nx1);
+  constexpr int kWait = 2 * kCopies;
+  static_assert(kWait < 64, "vmcnt range");
+  for (int t = 0; t < mine; ++t) {
+    copy(t + 2, nx2);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (kWait & 15) | ((kWait >> 4) << 14));  // vmcnt(kWait)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pos = ((4 * q + h) ^ i) << 4;
+      const uint4 wv = lds_read16(cur + i * kGvRowBytes + pos);
+#pragma unroll
+      for (int u = 0; u < MT; ++u) {
+        const uint4 xv = lds_read16(cur + (1 + u) * kGvTile + i * kGvRowBytes + pos);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv),
+                                                        __builtin_bit_cast(bf16x8_t, xv), acc[u], 0, 0, 0);
+      }
+    }
+    uint8_t* done = cur;
+    cur = nx1;
+    nx1 = nx2;
+    nx2 = done;
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): no copy still writes the ring
+  __syncthreads();
+  f32x4_t* red = (f32x4_t*)lds;  // [wave][MT][64]
+#pragma unroll
+  for (int u = 0; u < MT; ++u) red[(wave * MT + u) * 64 + lane] = acc[u];
+  __syncthreads();
+  // wave u finishes column tile u
+  if (wave < MT) {
+    const int u = wave;
+    f32x4_t s = red[u * 64 + lane];
+    for (int v = 1; v < kGvWaves; ++v) s += red[(v * MT + u) * 64 + lane];
+    const int m = (lane & 15) + 16 * u;
+    if (m < M) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = n0 + 4 * (lane >> 4) + r;
+        if (n < N) {
+          uint32_t b = __float_as_uint(s[r]);
+          y[(int64_t)m * N + n] = (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+        }
+      }
+    }
+  }
+}
+
+// Ragged K (K % 128 != 0): 16 W rows per workgroup, up to kGvMaxWaves waves
+// splitting K, loads straight into registers (the four lanes of a row read 64
+// contiguous bytes per instruction), every piece bounds-checked.
 constexpr int kGvMaxWaves = 16;
 
 template <int MT>
-__global__ __launch_bounds__(kGvMaxWaves * 64) void gemv_bf16_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(kGvMaxWaves * 64) void gemv_bf16_ragged_kernel(const uint16_t* __restrict__ x,
                                                                    const uint16_t* __restrict__ w,
                                                                    uint16_t* __restrict__ y, int M, int N,
                                                                    int K) {
@@ -37,14 +170,14 @@ __global__ __launch_bounds__(kGvMaxWaves * 64) void gemv_bf16_kernel(const uint1
   const int n0 = blockIdx.x * 16;
   int nrow = n0 + i;
   nrow = nrow < N ? nrow : N - 1;
-  const uint16_t* wrow = w + (int64_t)nrow * K + 32 * h;
+  const uint16_t* wrow = w + (int64_t)nrow * K + 8 * h;
   const uint16_t* xrow[MT];
   bool xok[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int m = i + 16 * t;
     xok[t] = m < M;
-    xrow[t] = x + (int64_t)(xok[t] ? m : 0) * K + 32 * h;
+    xrow[t] = x + (int64_t)(xok[t] ? m : 0) * K + 8 * h;
   }
   f32x4_t acc[MT];
 #pragma unroll
@@ -61,11 +194,11 @@ __global__ __launch_bounds__(kGvMaxWaves * 64) void gemv_bf16_kernel(const uint1
       const int k0 = (c + u * nw) * kGvChunk;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const bool in = k0 + 32 * h + 8 * q < K;
-        wv[u][q] = in ? ld_stream(wrow + k0 + 8 * q) : zero;
+        const bool in = k0 + 8 * h + 32 * q < K;
+        wv[u][q] = in ? ld_stream(wrow + k0 + 32 * q) : zero;
 #pragma unroll
         for (int t = 0; t < MT; ++t)
-          xv[u][t][q] = (in && xok[t]) ? *(const uint4*)(xrow[t] + k0 + 8 * q) : zero;
+          xv[u][t][q] = (in && xok[t]) ? *(const uint4*)(xrow[t] + k0 + 32 * q) : zero;
       }
     }
 #pragma unroll
@@ -82,11 +215,11 @@ __global__ __launch_bounds__(kGvMaxWaves * 64) void gemv_bf16_kernel(const uint1
     const int k0 = c * kGvChunk;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const bool in = k0 + 32 * h + 8 * q < K;
-      uint4 wq = in ? ld_stream(wrow + k0 + 8 * q) : zero;
+      const bool in = k0 + 8 * h + 32 * q < K;
+      uint4 wq = in ? ld_stream(wrow + k0 + 32 * q) : zero;
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        uint4 xq = (in && xok[t]) ? *(const uint4*)(xrow[t] + k0 + 8 * q) : zero;
+        uint4 xq = (in && xok[t]) ? *(const uint4*)(xrow[t] + k0 + 32 * q) : zero;
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wq),
                                                         __builtin_bit_cast(bf16x8_t, xq), acc[t], 0, 0, 0);
       }
@@ -113,8 +246,24 @@ __global__ __launch_bounds__(kGvMaxWaves * 64) void gemv_bf16_kernel(const uint1
   }
 }
 
-hipError_t launch_gemv(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
-                       const DeviceInfo& dev, hipStream_t stream) {
+template <int MT>
+static hipError_t launch_mt(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K, int dev,
+                            hipStream_t stream) {
+  auto kern = gemv_bf16_kernel<MT>;
+  constexpr int lds = gv_lds_bytes<MT>();
+  static bool attr_done[64] = {};  // benign race: the call is idempotent
+  if (dev < 0 || dev >= 64 || !attr_done[dev]) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) attr_done[dev] = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)((N + 15) / 16)), dim3(kGvWaves * 64), lds, stream, (const uint16_t*)x,
+                     (const uint16_t*)w, (uint16_t*)y, (int)M, (int)N, (int)K);
+  return hipGetLastError();
+}
+
+static hipError_t launch_ragged(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
+                                const DeviceInfo& dev, hipStream_t stream) {
   const int nwg = (int)((N + 15) / 16);
   const int nchunks = (int)((K + kGvChunk - 1) / kGvChunk);
   // aim for about eight waves per CU over the whole grid
@@ -123,13 +272,21 @@ hipError_t launch_gemv(const void* x, const void* w, void* y, int64_t M, int64_t
   nw = nw > kGvMaxWaves ? kGvMaxWaves : nw;
   nw = nw > nchunks ? (nchunks < 1 ? 1 : nchunks) : nw;
   if (M <= 16) {
-    hipLaunchKernelGGL(gemv_bf16_kernel<1>, dim3(nwg), dim3(nw * 64), 0, stream, (const uint16_t*)x,
+    hipLaunchKernelGGL(gemv_bf16_ragged_kernel<1>, dim3(nwg), dim3(nw * 64), 0, stream, (const uint16_t*)x,
                        (const uint16_t*)w, (uint16_t*)y, (int)M, (int)N, (int)K);
   } else {
-    hipLaunchKernelGGL(gemv_bf16_kernel<2>, dim3(nwg), dim3(nw * 64), 0, stream, (const uint16_t*)x,
+    hipLaunchKernelGGL(gemv_bf16_ragged_kernel<2>, dim3(nwg), dim3(nw * 64), 0, stream, (const uint16_t*)x,
                        (const uint16_t*)w, (uint16_t*)y, (int)M, (int)N, (int)K);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemv(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
+                       const DeviceInfo& dev, hipStream_t stream) {
+  // the ring kernel needs whole chunks and buffer offsets of 32 rows below 2^31
+  if (K % kGvChunk != 0 || K >= (int64_t(1) << 25)) return launch_ragged(x, w, y, M, N, K, dev, stream);
+  if (M <= 16) return launch_mt<1>(x, w, y, M, N, K, dev.device, stream);
+  return launch_mt<2>(x, w, y, M, N, K, dev.device, stream);
 }
 
 }  // namespace mq

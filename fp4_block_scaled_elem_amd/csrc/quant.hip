@@ -155,7 +155,9 @@ static int grid_for(int64_t items, int threads, int max_blocks) {
 hipError_t launch_amax(const void* x_bf16, int64_t nelem, mq_scale_rec* rec, const DeviceInfo& dev,
                        hipStream_t stream) {
   const int64_t n16 = nelem / 8;
-  int blocks = grid_for((n16 + 3) / 4, kQThreads, dev.num_cu * 4);
+  // two workgroups per CU: enough loads in flight for HBM, and few partial
+  // maxima for every quantize workgroup to reduce (measured faster than four)
+  int blocks = grid_for((n16 + 3) / 4, kQThreads, dev.num_cu * 2);
   if (blocks > MQ_AMAX_PARTS) blocks = MQ_AMAX_PARTS;
   hipLaunchKernelGGL(amax_kernel, dim3(blocks), dim3(kQThreads), 0, stream,
                      (const uint4*)x_bf16, n16, rec);
