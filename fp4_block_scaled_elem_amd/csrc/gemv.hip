@@ -8,17 +8,18 @@
 // so the kernel is organised around W's bytes:
 //   - a workgroup owns 16 rows of W and all of K; its four waves take the
 //     K chunks (128 elements = 256 bytes per row) in turn;
-//   - each wave has a ring of LDS buffers, one chunk each: the chunk's 16 W
-//     rows and the matching X pieces (16 rows per column tile) arrive by
+//   - each wave has two LDS buffers, one chunk each: the chunk's 16 W rows
+//     and the matching X pieces (16 rows per column tile) arrive by
 //     buffer_load ... lds, every instruction copying four rows of 256 bytes
-//     (whole cache lines), kGvBuf - 1 chunks ahead of use; rows past N or M
-//     and elements past K read zeros through the buffer resources;
+//     (whole cache lines), one chunk ahead of use; rows past N or M read
+//     zeros through the buffer resources (K is a multiple of the chunk; other
+//     K take a register-path kernel);
 //   - the wave reads the chunk back in MFMA layout (16-byte piece L of row r
 //     sits at position L ^ (r & 15), so 16 rows hit distinct banks) and
 //     feeds v_mfma_f32_16x16x32_bf16 with W rows as the 16-row operand and
-//     X^T as the 16-column operand (up to two column tiles for M <= 32); the
-//     MFMA is used for its fp32 accumulation of exact bf16 products, not its
-//     rate;
+//     X^T as the 16-column operand (up to two column tiles for M <= 32); all
+//     reads of a chunk go out together and are waited for once; the MFMA is
+//     used for its fp32 accumulation of exact bf16 products, not its rate;
 //   - the K order inside a chunk is the same for W and X;
 //   - the per-wave partial tiles are summed through LDS in a fixed order
 //     (deterministic), rounded to bf16 (nearest-even) and stored.
@@ -30,26 +31,65 @@ namespace mq {
 constexpr int kGvChunk = 128;                    // K elements per chunk
 constexpr int kGvRowBytes = 2 * kGvChunk;        // bytes per row and chunk
 constexpr int kGvWaves = 4;                      // waves per workgroup (split K)
-constexpr int kGvBuf = 3;                        // LDS chunk buffers per wave
 constexpr int kGvTile = 16 * kGvRowBytes;        // 4 KB: 16 rows of one chunk
 constexpr int kGvBufferWord3 = 0x00020000;       // raw buffer, 32-bit data format
 typedef __attribute__((address_space(3))) void gv_lds_t;
 
-// 16 bytes from LDS, complete on return.  Written as one asm block (the read
-// and its wait together) because the compiler, seeing an ordinary LDS load
-// after the direct-to-LDS copies, waits for every copy in flight (vmcnt(0))
-// and so would drain the prefetch at each chunk; the copies this read needs
-// have been waited for explicitly.
-__device__ __forceinline__ uint4 lds_read16(const uint8_t* p) {
-  u32x4_t r;
-  const uint32_t a = (uint32_t)(uintptr_t)p;
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(a) : "memory");
-  return __builtin_bit_cast(uint4, r);
+// All pieces of one chunk that a lane needs, in one asm block that also waits
+// for them: for q = 0..3 the W piece at a[q] and the MT X pieces one tile
+// (4 KB) apart after it.  The outputs are early-clobber, so no read can land
+// on an address still to be used.  Ordinary loads would not do: after the
+// direct-to-LDS copies the compiler puts a vmcnt(0) before any LDS load,
+// which would drain the prefetch at every chunk; the copies a chunk needs
+// are waited for explicitly.
+template <int MT>
+__device__ __forceinline__ void lds_read_chunk(const uint32_t (&a)[4], uint4 (&wv)[4], uint4 (&xv)[4][MT]) {
+  u32x4_t w0, w1, w2, w3, x0, x1, x2, x3;
+  if constexpr (MT == 1) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %4, %8 offset:4096\n\t"
+        "ds_read_b128 %1, %9\n\tds_read_b128 %5, %9 offset:4096\n\t"
+        "ds_read_b128 %2, %10\n\tds_read_b128 %6, %10 offset:4096\n\t"
+        "ds_read_b128 %3, %11\n\tds_read_b128 %7, %11 offset:4096\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3), "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+    xv[0][0] = __builtin_bit_cast(uint4, x0);
+    xv[1][0] = __builtin_bit_cast(uint4, x1);
+    xv[2][0] = __builtin_bit_cast(uint4, x2);
+    xv[3][0] = __builtin_bit_cast(uint4, x3);
+  } else {
+    u32x4_t y0, y1, y2, y3;
+    asm volatile(
+        "ds_read_b128 %0, %12\n\tds_read_b128 %4, %12 offset:4096\n\tds_read_b128 %8, %12 offset:8192\n\t"
+        "ds_read_b128 %1, %13\n\tds_read_b128 %5, %13 offset:4096\n\tds_read_b128 %9, %13 offset:8192\n\t"
+        "ds_read_b128 %2, %14\n\tds_read_b128 %6, %14 offset:4096\n\tds_read_b128 %10, %14 offset:8192\n\t"
+        "ds_read_b128 %3, %15\n\tds_read_b128 %7, %15 offset:4096\n\tds_read_b128 %11, %15 offset:8192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3), "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(y0),
+          "=&v"(y1), "=&v"(y2), "=&v"(y3)
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+    xv[0][0] = __builtin_bit_cast(uint4, x0);
+    xv[1][0] = __builtin_bit_cast(uint4, x1);
+    xv[2][0] = __builtin_bit_cast(uint4, x2);
+    xv[3][0] = __builtin_bit_cast(uint4, x3);
+    xv[0][MT - 1] = __builtin_bit_cast(uint4, y0);
+    xv[1][MT - 1] = __builtin_bit_cast(uint4, y1);
+    xv[2][MT - 1] = __builtin_bit_cast(uint4, y2);
+    xv[3][MT - 1] = __builtin_bit_cast(uint4, y3);
+  }
+  wv[0] = __builtin_bit_cast(uint4, w0);
+  wv[1] = __builtin_bit_cast(uint4, w1);
+  wv[2] = __builtin_bit_cast(uint4, w2);
+  wv[3] = __builtin_bit_cast(uint4, w3);
 }
 
 template <int MT>
-constexpr int gv_lds_bytes() { return kGvWaves * kGvBuf * (1 + MT) * kGvTile; }
+constexpr int gv_lds_bytes() { return kGvWaves * 2 * (1 + MT) * kGvTile; }
 
+// MT column tiles of X (16 rows each) against 16 rows of W per workgroup.
 template <int MT>
 __global__ __launch_bounds__(kGvWaves * 64) void gemv_bf16_kernel(const uint16_t* __restrict__ x,
                                                                 const uint16_t* __restrict__ w,
@@ -63,18 +103,19 @@ __global__ __launch_bounds__(kGvWaves * 64) void gemv_bf16_kernel(const uint16_t
   // the host guarantees 32 * K * 2 < 2^31
   const uint16_t* wtile = w + (int64_t)n0 * K;
   const int wbytes = min(16, N - n0) * K * 2, xbytes = M * K * 2;
-  // copy j of a chunk covers rows 4(j%4) .. +3 of its tile (tile j/4: W, then
-  // the X column tiles); lane l: row r = 4(j%4) + l/16, LDS piece l%16 holds
-  // logical piece (l%16) ^ r, i.e. K elements k0 + 8((l%16) ^ r) .. +7.  K is
-  // a multiple of the chunk, so no piece lies past K.
+  // copy j of a chunk covers rows 4(j%4) .. +3 of tile j/4 (W, then the X
+  // column tiles); lane l: row
+  // r = 4(j%4) + l/16, LDS piece l%16 holds logical piece (l%16) ^ r, i.e.
+  // K elements k0 + 8((l%16) ^ r) .. +7.  K is a multiple of the chunk, so no
+  // piece lies past K.
   uint32_t off[kCopies];
 #pragma unroll
   for (int j = 0; j < kCopies; ++j) {
     const int r = 4 * (j % 4) + (lane >> 4), tile = j / 4;
-    const int row = tile == 0 ? r : 16 * (tile - 1) + r;  // row of W (tile) or of X
+    const int row = tile == 0 ? r : 16 * (tile - 1) + r;  // row of W or of X
     off[j] = (uint32_t)(row * K + 8 * ((lane & 15) ^ r)) * 2u;
   }
-  uint8_t* ring = lds + wave * kGvBuf * kBufBytes;
+  uint8_t* ring = lds + wave * 2 * kBufBytes;
   const int nchunks = (K + kGvChunk - 1) / kGvChunk;
   const int mine = nchunks > wave ? (nchunks - wave + kGvWaves - 1) / kGvWaves : 0;  // this wave's chunks
   // This wave's t-th chunk into buffer dst.  Past the share the resources
@@ -96,37 +137,33 @@ __global__ __launch_bounds__(kGvWaves * 64) void gemv_bf16_kernel(const uint16_t
 #pragma unroll
   for (int u = 0; u < MT; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Copies run two chunks ahead through three buffers that rotate; before
-  // chunk t is read, every copy but the newest chunk's two groups must have
-  // landed (vmcnt counts in issue order).  The buffer refilled at step t was
-  // read at step t - 1, and those reads completed before their MFMAs.
-  // Chunks past this wave's share compute on zeros.
-  static_assert(kGvBuf == 3, "three rotating buffers");
+  // Copies run one chunk ahead through two buffers that alternate; before
+  // chunk t is read, every copy but the next chunk's must have landed (vmcnt
+  // counts in issue order).  The buffer refilled at step t was read at step
+  // t - 1, and those reads completed inside their asm block.  Chunks past
+  // this wave's share compute on zeros.
   uint8_t* cur = ring;
-  uint8_t* nx1 = ring + kBufBytes;
-  uint8_t* nx2 = ring + 2 * kBufBytes;
+  uint8_t* nxt = ring + kBufBytes;
   copy(0, cur);
-  copy(1, nx1);
-  constexpr int kWait = 2 * kCopies;
+  constexpr int kWait = kCopies;
   static_assert(kWait < 64, "vmcnt range");
   for (int t = 0; t < mine; ++t) {
-    copy(t + 2, nx2);
+    copy(t + 1, nxt);
     __builtin_amdgcn_s_waitcnt(0x0F70 | (kWait & 15) | ((kWait >> 4) << 14));  // vmcnt(kWait)
+    uint32_t ad[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int pos = ((4 * q + h) ^ i) << 4;
-      const uint4 wv = lds_read16(cur + i * kGvRowBytes + pos);
+    for (int q = 0; q < 4; ++q) ad[q] = (uint32_t)(uintptr_t)(cur + i * kGvRowBytes + (((4 * q + h) ^ i) << 4));
+    uint4 wv[4], xv[4][MT];
+    lds_read_chunk<MT>(ad, wv, xv);
 #pragma unroll
-      for (int u = 0; u < MT; ++u) {
-        const uint4 xv = lds_read16(cur + (1 + u) * kGvTile + i * kGvRowBytes + pos);
-        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv),
-                                                        __builtin_bit_cast(bf16x8_t, xv), acc[u], 0, 0, 0);
-      }
-    }
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int u = 0; u < MT; ++u)
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv[q]),
+                                                        __builtin_bit_cast(bf16x8_t, xv[q][u]), acc[u], 0, 0, 0);
     uint8_t* done = cur;
-    cur = nx1;
-    nx1 = nx2;
-    nx2 = done;
+    cur = nxt;
+    nxt = done;
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): no copy still writes the ring
   __syncthreads();
@@ -247,8 +284,8 @@ __global__ __launch_bounds__(kGvMaxWaves * 64) void gemv_bf16_ragged_kernel(cons
 }
 
 template <int MT>
-static hipError_t launch_mt(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K, int dev,
-                            hipStream_t stream) {
+static hipError_t launch_ring(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K, int dev,
+                              hipStream_t stream) {
   auto kern = gemv_bf16_kernel<MT>;
   constexpr int lds = gv_lds_bytes<MT>();
   static bool attr_done[64] = {};  // benign race: the call is idempotent
@@ -257,8 +294,8 @@ static hipError_t launch_mt(const void* x, const void* w, void* y, int64_t M, in
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < 64) attr_done[dev] = true;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)((N + 15) / 16)), dim3(kGvWaves * 64), lds, stream, (const uint16_t*)x,
-                     (const uint16_t*)w, (uint16_t*)y, (int)M, (int)N, (int)K);
+  hipLaunchKernelGGL(kern, dim3((unsigned)((N + 15) / 16)), dim3(kGvWaves * 64), lds, stream,
+                     (const uint16_t*)x, (const uint16_t*)w, (uint16_t*)y, (int)M, (int)N, (int)K);
   return hipGetLastError();
 }
 
@@ -285,8 +322,8 @@ hipError_t launch_gemv(const void* x, const void* w, void* y, int64_t M, int64_t
                        const DeviceInfo& dev, hipStream_t stream) {
   // the ring kernel needs whole chunks and buffer offsets of 32 rows below 2^31
   if (K % kGvChunk != 0 || K >= (int64_t(1) << 25)) return launch_ragged(x, w, y, M, N, K, dev, stream);
-  if (M <= 16) return launch_mt<1>(x, w, y, M, N, K, dev.device, stream);
-  return launch_mt<2>(x, w, y, M, N, K, dev.device, stream);
+  if (M <= 16) return launch_ring<1>(x, w, y, M, N, K, dev.device, stream);
+  return launch_ring<2>(x, w, y, M, N, K, dev.device, stream);
 }
 
 }  // namespace mq

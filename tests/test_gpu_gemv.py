@@ -36,8 +36,13 @@ def test_cfg4_decode(M, proj):
     _check(workloads.activation(4, act, M=M), workloads.weight(4, proj))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (3, 17, 48), (17, 1000, 4112), (32, 33, 160),
-                                   (5, 4096, 16), (31, 64, 8192)])
+@pytest.mark.parametrize("M,N,K", [
+    # K % 128 != 0: the register-path kernel
+    (1, 1, 16), (3, 17, 48), (17, 1000, 4112), (32, 33, 160), (5, 4096, 16),
+    # K % 128 == 0: the LDS-ring kernel, with ragged N and M, one chunk (three
+    # waves without work), and chunk counts that do not divide by four
+    (31, 64, 8192), (1, 1, 128), (17, 1000, 1024), (32, 4100, 256), (2, 33, 384), (16, 17, 640),
+])
 def test_ragged(M, N, K):
     announce("gemv ragged", M, N, K)
     _check(workloads.random_bf16((M, K), M + N, 1.0), workloads.random_bf16((N, K), K, 0.02))
