@@ -50,7 +50,12 @@ def parse():
                    help="grouped: k+v and gate+up as one launch each; separate: one launch per projection")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=8192, help="activation rows in the CPU sample")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the per-kernel rates measured after the timed region (quantizer and decode GEMV)")
+    p.add_argument("--cpu-rows", type=int, default=4096, help="activation rows in the CPU sample (at most M)")
+    p.add_argument("--cpu-wrows", type=int, default=4096, help="weight rows per projection in the CPU sample")
+    p.add_argument("--decode-only", action="store_true",
+                   help="only measure the BF16 decode GEMV at the decode shapes (one JSON line, not the step metric)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB) three "
                         "times, as the reference for scaling HBM byte counters")
@@ -149,6 +154,92 @@ def _pairs_ms(evs):
     return sum(evs[i].elapsed_time(evs[i + 1]) for i in range(0, len(evs), 2))
 
 
+def _median_us(fn, reps=50, warm=20, batch=10):
+    """Median and min over `reps` HIP-event timings of the per-call duration
+    of `batch` back-to-back calls (fn(i) with i counting calls, so inputs can
+    rotate); a lone call would be dominated by launch latency."""
+    import statistics
+    import torch
+    i = 0
+    for _ in range(warm):
+        fn(i)
+        i += 1
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(batch):
+            fn(i)
+            i += 1
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / batch)
+    return statistics.median(ts), min(ts)
+
+
+def per_launch(cfg, plan, acts, qw, qa, fa, out, events, steps):
+    """TFLOP/s of each launch of the step, from the timed region's events."""
+    import workloads
+    res = {}
+    n = len(plan)
+    for idx, (a, g) in enumerate(plan):
+        ms = sum(events["g"][2 * (s * n + idx)].elapsed_time(events["g"][2 * (s * n + idx) + 1])
+                 for s in range(steps)) / steps
+        flops = sum(2 * cfg.M[0] * cfg.layer.proj_nk(p)[0] * cfg.layer.proj_nk(p)[1] for p in g)
+        res["+".join(g)] = {"us": round(ms * 1e3, 2), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+    return res
+
+
+def act_quant_rates(acts):
+    """The standalone quantizer per activation tensor: achieved GB/s for the
+    single-read algorithmic bytes (2 + 0.5625 per element) and for the bytes
+    the two passes move (the amax pass reads the input again).  Inputs and
+    outputs rotate over copies so the working set exceeds the 256 MB
+    Infinity Cache."""
+    import fp4_block_scaled_elem_amd as mq
+    res = {}
+    for a, x0 in acts.items():
+        n = x0.numel()
+        ncopy = max(2, -(-600 * 2 ** 20 // (n * 2)))
+        xs = [x0.clone() for _ in range(ncopy)]
+        qs = [mq.NVFP4.empty(*x0.shape) for _ in range(ncopy)]
+        med, mn = _median_us(lambda r: mq.mq_quantize_nvfp4(xs[r % ncopy], qs[r % ncopy]))
+        del xs, qs
+        res[a] = {"shape": list(x0.shape), "us_median": round(med, 2), "us_min": round(mn, 2),
+                  "GBps_1pass": round(n * 2.5625 / med / 1e3, 1), "GBps_2pass": round(n * 4.5625 / med / 1e3, 1),
+                  "pct_hbm_2pass": round(100 * n * 4.5625 / med / 1e3 / PEAK_HBM_GBS, 1)}
+    return res
+
+
+def decode_gemv_rates(reps=50):
+    """The BF16 decode GEMV at the decode configuration's shapes (M in
+    {1, 4, 16, 32} x the 8B layer's (N, K) pairs), weights rotated over copies
+    so that the working set exceeds the 256 MB Infinity Cache; achieved GB/s
+    over 2NK + 2MK + 2MN bytes, and torch's BF16 linear at the same shapes."""
+    import torch
+    import torch.nn.functional as F
+    import fp4_block_scaled_elem_amd as mq
+    import workloads
+    lay = workloads.LLAMA8B
+    res = {}
+    for p in ("q", "k", "gate", "down"):
+        N, K = lay.proj_nk(p)
+        ncopy = max(2, -(-600 * 2 ** 20 // (2 * N * K)))
+        gen = torch.Generator(device="cuda").manual_seed(1000 + N + K)
+        ws = [(torch.randn((N, K), generator=gen, device="cuda") * 0.02).to(torch.bfloat16) for _ in range(ncopy)]
+        for M in (1, 4, 16, 32):
+            x = torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            med, mn = _median_us(lambda r: mq.mq_gemv_bf16_decode(x, ws[r % ncopy], y), reps=reps)
+            tmed, _ = _median_us(lambda r: F.linear(x, ws[r % ncopy]), reps=reps)
+            b = 2 * N * K + 2 * M * K + 2 * M * N
+            res[f"{p}_M{M}"] = {"N": N, "K": K, "M": M, "us_median": round(med, 2), "us_min": round(mn, 2),
+                                "GBps": round(b / med / 1e3, 1), "pct_hbm": round(100 * b / med / 1e3 / PEAK_HBM_GBS, 1),
+                                "torch_us": round(tmed, 2)}
+        del ws
+    return res
+
+
 def bf16_reference(cfg, acts, wdev, iters=10):
     """torch's BF16 GEMM (hipBLASLt) at the same shapes, TFLOP/s."""
     import torch
@@ -168,11 +259,11 @@ def bf16_reference(cfg, acts, wdev, iters=10):
     return flops / dt / 1e12
 
 
-def cpu_baseline(cfg_id, acts_host, rows):
+def cpu_baseline(cfg_id, acts_host, rows, wrows):
     """The oracle as it stands, on a bounded sample of the same workload:
     the first ``rows`` tokens of each activation (quantized as a tensor of
-    their own) times 1024 weight rows of every projection (weights quantized
-    beforehand, untimed, as on the GPU)."""
+    their own) times the first ``wrows`` weight rows of every projection
+    (weights quantized beforehand, untimed, as on the GPU)."""
     import numpy as np
     import oracle
     import workloads
@@ -185,7 +276,7 @@ def cpu_baseline(cfg_id, acts_host, rows):
     wq = {}
     for p in cfg.projs:
         wb = workloads.weight(cfg_id, p)
-        wq[p] = oracle.quantize_nvfp4(wb[:1024])
+        wq[p] = oracle.quantize_nvfp4(wb[:wrows])
     flops, dt = 0, 0.0
     for a in workloads.ACTS:
         xs = acts_host[a][:rows]
@@ -198,7 +289,7 @@ def cpu_baseline(cfg_id, acts_host, rows):
             flops += 2 * c.shape[0] * c.shape[1] * xs.shape[1]
         dt += time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
-            "sample": (f"first {rows} tokens of each activation x 1024 weight rows of each of "
+            "sample": (f"first {min(rows, cfg.M[0])} tokens of each activation x first {wrows} weight rows of each of "
                        f"{len(cfg.projs)} projections ({flops / 1e9:.1f} GFLOP, {dt:.1f} s; NumPy "
                        f"elementwise steps single-threaded, float64 matmul on {blas} BLAS threads)")}
 
@@ -231,6 +322,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.decode_only:
+        print(json.dumps({"decode_gemv": decode_gemv_rates()}), flush=True)
+        return
     cfg, acts_host, acts, wdev, qw, qa, fa, out = setup(args.config)
     flops = cfg.flops()
     plan = launch_plan(cfg, args.launches)
@@ -256,8 +350,11 @@ def main():
     n_gemm = len(plan)
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
 
+    launches = per_launch(cfg, plan, acts, qw, qa, fa, out, events, args.steps)
+    quant = None if (args.no_extras or cfg.fused_act_quant) else act_quant_rates(acts)
+    gemv = None if args.no_extras else decode_gemv_rates()
     bf16 = None if args.no_bf16 else bf16_reference(cfg, acts, wdev)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args.config, acts_host, args.cpu_rows)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.config, acts_host, args.cpu_rows, args.cpu_wrows)
 
     rec = {
         "metric": METRIC,
@@ -283,6 +380,9 @@ def main():
                      "frac": round(gemm_tflops / PEAK_F16_MFMA_TFLOPS, 4), "traffic": gemm_traffic(cfg.name),
                      "launches_per_step": n_gemm, "avg_launch_ms": round(gemm_ms / n_gemm, 4)},
         "split_ms": {"gemm": round(gemm_ms, 4), "act_quant_and_gaps": round(rest_ms, 4)},
+        "per_launch": launches,
+        "act_quant": quant,
+        "decode_gemv": gemv,
         "bf16_torch_tflops": None if bf16 is None else round(bf16, 2),
         "ratio_vs_bf16_torch": None if bf16 is None else round(value / bf16, 3),
         "cpu_baseline": cpu,

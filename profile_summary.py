@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Summarise rocprofv3 runs of bench.py into short text files under profiles/.
 
-    python profile_summary.py <run_dir> <workload-name>
+    python profile_summary.py <run_dir> <workload-name> [<calibration_dir>]
 
 <run_dir> holds, from one GPU session (each a rocprofv3 output directory):
   ktcsv/      --kernel-trace --stats --output-format csv
@@ -9,7 +9,8 @@
   write/      --pmc WRITE_SIZE        (rocpd database)
   cal_fetch/  --pmc FETCH_SIZE of `bench.py --copy-calibration`
   cal_write/  --pmc WRITE_SIZE of `bench.py --copy-calibration`
-and commands.txt with the exact commands that produced them.
+and commands.txt with the exact commands that produced them.  The two
+calibration runs may come from another directory (third argument).
 
 Writes profiles/<kernel>_<workload>.txt (per-kernel durations, HBM bytes
 per launch after scaling by the copy calibration) and
@@ -55,10 +56,11 @@ def pmc(db_dir: str):
 
 def main():
     run, workload = sys.argv[1], sys.argv[2]
+    cal = sys.argv[3] if len(sys.argv) > 3 else run
     stats = list(csv.DictReader(open(glob.glob(os.path.join(run, "ktcsv", "**", "*kernel_stats.csv"),
                                                recursive=True)[0])))
     fetch, write = pmc(os.path.join(run, "fetch")), pmc(os.path.join(run, "write"))
-    calf, calw = pmc(os.path.join(run, "cal_fetch")), pmc(os.path.join(run, "cal_write"))
+    calf, calw = pmc(os.path.join(cal, "cal_fetch")), pmc(os.path.join(cal, "cal_write"))
     cal_read = [v for (n, g, c), v in calf.items() if "neg_kernel" in n]
     cal_wr = [v for (n, g, c), v in calw.items() if "neg_kernel" in n]
     gib_kib = float(1 << 20)
@@ -98,13 +100,14 @@ def main():
     path = os.path.join(ROOT, "profiles", f"kernels_{workload}.txt")
     open(path, "w").write("\n".join(lines) + "\n")
     # traffic for the GEMM launches of one step, per launch (mean over launches)
-    g_read = [v for k, v in fb.items() if k[0].startswith("gemm_nvfp4_kernel")]
-    g_write = [v for k, v in wb.items() if k[0].startswith("gemm_nvfp4_kernel")]
     launches = collections.Counter()
     for (n, g, c), v in fetch.items():
         if n.startswith("gemm_nvfp4_kernel") and c == "FETCH_SIZE":
             launches[(n, g)] += len(v)
     tot = sum(launches.values())
+    if not tot:
+        print(path)
+        return
     mean_read = sum(fb[k] * launches[k] for k in launches) / tot
     mean_write = sum(wb.get(k, 0) * launches[k] for k in launches) / tot
     json.dump({"workload": workload, "gemm_source_sha256_16": source_hash(),
