@@ -223,7 +223,7 @@ struct FusedALoader {
   // Quantize the loaded groups into stage half p of a slot's A codes and
   // scale bytes.
   template <int BN>
-  __device__ __forceinline__ void quantize_store(uint8_t* stage, int p, float s_t) const {
+  __device__ __forceinline__ void quantize_store(uint8_t* stage, int p, const GroupScaleTab& tab) const {
 #pragma unroll
     for (int j = 0; j < kGroupsPer; ++j) {
       const int gi = threadIdx.x + kThreads * j;
@@ -231,7 +231,7 @@ struct FusedALoader {
       uint32_t w[8] = {raw[j][0][0], raw[j][0][1], raw[j][0][2], raw[j][0][3],
                        raw[j][1][0], raw[j][1][1], raw[j][1][2], raw[j][1][3]};
       uint32_t lo, hi;
-      uint32_t S = quantize_group16(w, s_t, lo, hi);
+      uint32_t S = quantize_group16(w, tab, lo, hi);
       const int chunk = (4 * p + (grp >> 1)) ^ swz(row);
       *(u32x2_t*)(stage + Smem<BM, BN>::kA + row * kRowStride + chunk * 16 + (grp & 1) * 8) = u32x2_t{lo, hi};
       stage[Smem<BM, BN>::kAs + row * kScaleStride + 8 * p + grp] = (uint8_t)S;
@@ -622,6 +622,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
     s_ta = args.a_rec->s_t;
   }
   const float scale = s_ta * grp.w_rec->s_t;
+  // fused prologue: the group-scale constants of A's tensor scale (the
+  // reciprocal table is complete after this barrier)
+  GroupScaleTab gtab{};
+  if constexpr (FUSED) {
+    __shared__ float recip_tab[128];
+    gtab = group_scale_tab(s_ta, recip_tab);
+    __syncthreads();
+  }
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -652,7 +660,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
     else if constexpr (!FAST) la.load(args.a_codes, m0, M, K, kc);
   };
   auto reg_store = [&](uint8_t* slot, int k) __attribute__((always_inline)) {
-    if constexpr (FUSED) fa.template quantize_store<BN>(slot, k & 1, s_ta);
+    if constexpr (FUSED) fa.template quantize_store<BN>(slot, k & 1, gtab);
     else if constexpr (!FAST) la.store(slot + SM::kA, k & 1);
   };
   auto load_stage_reg = [&](uint8_t* slot, int k) __attribute__((always_inline)) {

@@ -5,9 +5,11 @@
 // Technical Summary s.2, Hybrid Precision Strategy): a scale per 16-element
 // group plus a tensor-level scale, elements rounded to nearest.  Formats:
 // E2M1 elements, OCP E4M3 ("fn") group scales, binary32 tensor scale
-// s_t = amax / 2688.  Every floating-point step here is a single IEEE
-// binary32 operation (the library is built with -ffp-contract=off and with
-// correctly rounded division), so results are bit-reproducible.
+// s_t = amax / 2688.  Every floating-point result here is the correctly
+// rounded binary32 result of the operation it stands for (the library is
+// built with -ffp-contract=off and with correctly rounded division), so
+// results are bit-reproducible; where a cheaper instruction sequence gives
+// that same result, the comment beside it says why.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,6 +37,8 @@ __device__ __forceinline__ uint4 ld_stream(const void* p) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+
 // max over the two bf16 magnitudes of a word, as a 15-bit integer.  For
 // non-negative finite floats the bit pattern orders like the value.
 __device__ __forceinline__ uint32_t bf16x2_absmax_bits(uint32_t w) {
@@ -42,21 +46,33 @@ __device__ __forceinline__ uint32_t bf16x2_absmax_bits(uint32_t w) {
   return lo > hi ? lo : hi;
 }
 
+// max over the bf16 magnitudes of n words (packed 16-bit maxima, one
+// instruction per word, then one across the two halves).
+template <int N>
+__device__ __forceinline__ uint32_t bf16_absmax_bits(const uint32_t* w) {
+  u16x2_t m = __builtin_bit_cast(u16x2_t, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+  for (int i = 1; i < N; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, w[i] & 0x7FFF7FFFu));
+  const uint32_t lo = m[0], hi = m[1];
+  return lo > hi ? lo : hi;
+}
+
 // Nearest E4M3 byte to rho >= 0, ties to even, saturating at 448 (0x7E),
-// subnormals (multiples of 2^-9) kept.
+// subnormals (multiples of 2^-9) kept; NaN -> 0x7E.  Below 2^-5 the E4M3
+// values are the multiples of 2^-9 and the code of k * 2^-9 is k, so one
+// binary32 addition of 2^14 (whose ulp is 2^-9) rounds rho to that grid with
+// ties to even and leaves k in the low bits.  From 2^-6 up, rounding the
+// binary32 pattern to 3 fraction bits with ties to even is an integer add of
+// 0x7FFFF plus the kept LSB (a carry moves into the exponent), and the
+// rounded pattern's top bits minus 120 << 3 (binary32 vs E4M3 exponent bias)
+// are the code.  Both forms were checked against the plain case analysis on
+// every binary32 value in [0, 448).
 __device__ __forceinline__ uint32_t e4m3_from_f32(float rho) {
-  if (!(rho < 448.0f)) return 0x7Eu;         // also catches +inf
-  if (rho < 0.015625f) {                      // below 2^-6: fixed step 2^-9
-    float q = __builtin_rintf(rho * 512.0f);  // exact scaling, RNE
-    return (uint32_t)q;                       // 0..8; 8 is the code of 2^-6
-  }
-  uint32_t b = __float_as_uint(rho);
-  uint32_t e = (b >> 23) - 120u;              // biased E4M3 exponent, 1..15
-  uint32_t man = b & 0x7FFFFFu;
-  uint32_t keep = man >> 20;
-  uint32_t rest = man & 0xFFFFFu;
-  uint32_t up = (rest > 0x80000u) || (rest == 0x80000u && (keep & 1u));
-  return ((e << 3) | keep) + up;              // a carry moves into the exponent
+  const uint32_t fine = __float_as_uint(rho + 16384.0f) - 0x46800000u;
+  const uint32_t b = __float_as_uint(rho);
+  const uint32_t coarse = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - 960u;
+  const uint32_t S = rho < 0.03125f ? fine : coarse;
+  return rho < 448.0f ? S : 0x7Eu;
 }
 
 // Exact binary32 value of an E4M3 byte (0x00..0x7E).
@@ -106,30 +122,51 @@ __device__ __forceinline__ uint32_t encode8(const uint32_t w[4], float e) {
   return c;
 }
 
+// 1 / (value(S) * s_t) for one E4M3 byte S, 0 when that product is 0: the
+// reciprocal group scale, tabulated per workgroup for the tensor scale s_t.
+__device__ __forceinline__ float group_recip(uint32_t S, float s_t) {
+  const float d = e4m3_to_f32(S) * s_t;
+  return d > 0.0f ? 1.0f / d : 0.0f;
+}
+
+// Per-tensor constants of the group-scale computation: inv = RN64(1 / s_t)
+// and the table recip[S] = group_recip(S, s_t) for S = 0..127 (entry 127,
+// not an E4M3 finite value, is never selected for a valid s_t; it is filled
+// so that every index is defined).  Every thread of the block calls this;
+// the table is ready after the next barrier.
+struct GroupScaleTab {
+  double inv;
+  const float* recip;  // LDS
+};
+__device__ __forceinline__ GroupScaleTab group_scale_tab(float s_t, float* recip_lds) {
+  for (int i = threadIdx.x; i < 128; i += blockDim.x) recip_lds[i] = group_recip((uint32_t)i, s_t);
+  return GroupScaleTab{1.0 / (double)s_t, recip_lds};
+}
+
 // Group scale of a group whose absolute maximum has the bf16 magnitude bits
-// am: returns the E4M3 byte S and sets e = 1 / (value(S) * s_t) (0 when that
-// product is 0).  Each step is one IEEE binary32 operation.
-__device__ __forceinline__ uint32_t group_scale(uint32_t am, float s_t, float& e) {
-  float a = __uint_as_float(am << 16);
-  float rho = (a / 6.0f) / s_t;
-  uint32_t S = e4m3_from_f32(rho);
-  float d = e4m3_to_f32(S) * s_t;
-  e = d > 0.0f ? 1.0f / d : 0.0f;
+// am: returns the E4M3 byte S of rho = (a / 6) / s_t (both divisions
+// correctly rounded binary32) and sets e = 1 / (value(S) * s_t).
+// The divisions are exact-rounding products: for binary32 x and y != 0,
+// rounding the binary64 product x * RN64(1/y) to binary32 gives RN32(x / y),
+// since a binary32 quotient that is not representable lies at least about
+// 2^-48 of its size from every binary32 rounding midpoint, well beyond the
+// product's 2^-52 error, and the quotient is a midpoint only when y is a
+// power of two, where the product is exact.
+__device__ __forceinline__ uint32_t group_scale(uint32_t am, const GroupScaleTab& tab, float& e) {
+  const float a = __uint_as_float(am << 16);
+  const float q = (float)((double)a * (1.0 / 6.0));
+  const float rho = (float)((double)q * tab.inv);
+  const uint32_t S = e4m3_from_f32(rho);
+  e = tab.recip[S & 0x7Fu];  // S <= 0x7E for a finite positive s_t
   return S;
 }
 
 // Quantize one group of 16 bf16 values (8 words).  Writes 8 code bytes (two
 // words, even element in the low nibble) and returns the E4M3 scale byte.
-__device__ __forceinline__ uint32_t quantize_group16(const uint32_t w[8], float s_t,
+__device__ __forceinline__ uint32_t quantize_group16(const uint32_t w[8], const GroupScaleTab& tab,
                                                      uint32_t& codes_lo, uint32_t& codes_hi) {
-  uint32_t am = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t m = bf16x2_absmax_bits(w[i]);
-    am = am > m ? am : m;
-  }
   float e;
-  uint32_t S = group_scale(am, s_t, e);
+  const uint32_t S = group_scale(bf16_absmax_bits<8>(w), tab, e);
   codes_lo = encode8(w, e);
   codes_hi = encode8(w + 4, e);
   return S;

@@ -13,7 +13,8 @@
 //      lane owns 8 consecutive elements (one 16-byte load, fully coalesced);
 //      the two lanes of a group exchange their half maxima with one
 //      cross-lane swap; the element codes come from the hardware fp4
-//      conversion of x * e.
+//      conversion of x * e, the reciprocal group scale e from a table of the
+//      128 possible values built by each workgroup.
 // Both passes are HBM-bound: 2 bytes read per element for the amax, 2 read
 // plus 0.5625 written per element for the encode.
 #include "mq_device.h"
@@ -33,11 +34,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 __device__ __forceinline__ uint32_t uint4_absmax(uint4 v) {
-  uint32_t a = bf16x2_absmax_bits(v.x), b = bf16x2_absmax_bits(v.y);
-  uint32_t c = bf16x2_absmax_bits(v.z), d = bf16x2_absmax_bits(v.w);
-  a = a > b ? a : b;
-  c = c > d ? c : d;
-  return a > c ? a : c;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  return bf16_absmax_bits<4>(w);
 }
 
 // Block-wide max of a per-thread value; every thread gets the result.
@@ -99,6 +97,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
                                                              uint8_t* __restrict__ scales,
                                                              mq_scale_rec* __restrict__ rec, int given) {
   __shared__ uint32_t sh[kQThreads / 64];
+  __shared__ float recip[128];
   float s_t;
   if (given) {
     s_t = rec->s_t;
@@ -110,6 +109,8 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
       rec->amax_bits = amax;
     }
   }
+  const GroupScaleTab tab = group_scale_tab(s_t, recip);
+  __syncthreads();
   // nhalf and stride are even and a pair starts on an even index, so both
   // lanes of a group enter and leave every loop iteration together
   const int64_t stride = (int64_t)gridDim.x * kQThreads;
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
       const uint32_t other = __shfl_xor(am, 1, 64);
       am = am > other ? am : other;
       float e;
-      const uint32_t S = group_scale(am, s_t, e);
+      const uint32_t S = group_scale(am, tab, e);
       const int64_t hu = h + u * stride;
       codes[hu] = encode8(w, e);
       if ((hu & 1) == 0) scales[hu >> 1] = (uint8_t)S;
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
     const uint32_t other = __shfl_xor(am, 1, 64);
     am = am > other ? am : other;
     float e;
-    const uint32_t S = group_scale(am, s_t, e);
+    const uint32_t S = group_scale(am, tab, e);
     codes[h] = encode8(w, e);
     if ((h & 1) == 0) scales[h >> 1] = (uint8_t)S;
   }
