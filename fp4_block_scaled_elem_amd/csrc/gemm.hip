@@ -197,15 +197,20 @@ struct ScaleLoader {
 // bf16 activations quantized on the fly (fused prologue): BM rows x 128
 // elements per stage = BM*8 groups, each thread owning whole groups.  The
 // arithmetic is quantize_group16, bit-identical to the standalone quantizer.
+// Tiles of more than 128 rows take a stage in kParts parts (loaded and
+// quantized at different pipeline steps) so that at most four groups of raw
+// bf16 data are held in registers.
 template <int BM, bool FAST>
 struct FusedALoader {
-  static constexpr int kGroupsPer = BM * 8 / kThreads;
+  static constexpr int kGroupsAll = BM * 8 / kThreads;
+  static constexpr int kParts = kGroupsAll > 4 ? kGroupsAll / 4 : 1;
+  static constexpr int kGroupsPer = kGroupsAll / kParts;
   u32x4_t raw[kGroupsPer][2];
 
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ a, int m0, int M, int K, int kt) {
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ a, int m0, int M, int K, int kt, int part) {
 #pragma unroll
     for (int j = 0; j < kGroupsPer; ++j) {
-      const int gi = threadIdx.x + kThreads * j;
+      const int gi = threadIdx.x + kThreads * (part * kGroupsPer + j);
       const int row = gi >> 3, grp = gi & 7;
       int r = m0 + row;
       r = r < M ? r : M - 1;
@@ -222,16 +227,16 @@ struct FusedALoader {
   }
   // Quantize the loaded groups into stage half p of a slot's A codes and
   // scale bytes.
-  template <int BN>
-  __device__ __forceinline__ void quantize_store(uint8_t* stage, int p, const GroupScaleTab& tab) const {
+  template <int BN, bool OVF>
+  __device__ __forceinline__ void quantize_store(uint8_t* stage, int p, const GroupScaleTab& tab, int part) const {
 #pragma unroll
     for (int j = 0; j < kGroupsPer; ++j) {
-      const int gi = threadIdx.x + kThreads * j;
+      const int gi = threadIdx.x + kThreads * (part * kGroupsPer + j);
       const int row = gi >> 3, grp = gi & 7;
       uint32_t w[8] = {raw[j][0][0], raw[j][0][1], raw[j][0][2], raw[j][0][3],
                        raw[j][1][0], raw[j][1][1], raw[j][1][2], raw[j][1][3]};
       uint32_t lo, hi;
-      uint32_t S = quantize_group16(w, tab, lo, hi);
+      uint32_t S = quantize_group16<OVF>(w, tab, lo, hi);
       const int chunk = (4 * p + (grp >> 1)) ^ swz(row);
       *(u32x2_t*)(stage + Smem<BM, BN>::kA + row * kRowStride + chunk * 16 + (grp & 1) * 8) = u32x2_t{lo, hi};
       stage[Smem<BM, BN>::kAs + row * kScaleStride + 8 * p + grp] = (uint8_t)S;
@@ -622,163 +627,188 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
     s_ta = args.a_rec->s_t;
   }
   const float scale = s_ta * grp.w_rec->s_t;
-  // fused prologue: the group-scale constants of A's tensor scale (the
-  // reciprocal table is complete after this barrier)
+  // fused prologue: the group-scale constants of A's tensor scale
   GroupScaleTab gtab{};
   if constexpr (FUSED) {
     __shared__ float recip_tab[128];
     gtab = group_scale_tab(s_ta, recip_tab);
-    __syncthreads();
   }
 
-  f32x16_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  // Main loop and epilogue.  The fused prologue's kernels carry two copies,
+  // with and without the quantizer's overflow fix-up, chosen once per
+  // workgroup: the common copy has no branches in its loop.
+  auto run = [&](auto ovf_c) __attribute__((always_inline)) {
+    constexpr bool OVF = decltype(ovf_c)::value;
+    f32x16_t acc[TM][TN];
+  #pragma unroll
+    for (int i = 0; i < TM; ++i)
+  #pragma unroll
+      for (int j = 0; j < TN; ++j)
+  #pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  using SM = Smem<BM, BN>;
-  // FAST shapes copy packed operands straight into LDS (A too unless it is
-  // quantized here); the fused A tile and all operands of ragged-K shapes go
-  // through registers.
-  DmaLoader<BM, BN, !FUSED> dma;
-  PackedLoader<BM, FAST> la;
-  FusedALoader<BM, FAST> fa;
-  PackedLoader<BN, FAST> lw;
-  ScaleLoader<BM, BN, FAST, !FUSED> ls;
-  if constexpr (FAST) dma.init(args.a_codes, args.a_scales, grp.w_codes, grp.w_scales, M, N, K, m0, n0);
+    using SM = Smem<BM, BN>;
+    // FAST shapes copy packed operands straight into LDS (A too unless it is
+    // quantized here); the fused A tile and all operands of ragged-K shapes go
+    // through registers.
+    DmaLoader<BM, BN, !FUSED> dma;
+    PackedLoader<BM, FAST> la;
+    FusedALoader<BM, FAST> fa;
+    PackedLoader<BN, FAST> lw;
+    ScaleLoader<BM, BN, FAST, !FUSED> ls;
+    if constexpr (FAST) dma.init(args.a_codes, args.a_scales, grp.w_codes, grp.w_scales, M, N, K, m0, n0);
 
-  // Register-path fill of stage k into half (k & 1) of a slot.  FAST (only
-  // the fused A tile goes this way) clamps k to the last stage; the ragged
-  // loaders' bounds checks zero a stage past the end instead, which lets an
-  // odd stage count finish on a zero half.
-  auto reg_load = [&](int k) __attribute__((always_inline)) {
-    const int kc = FAST ? min(k, nk - 1) : k;
-    if constexpr (FUSED) fa.load((const uint16_t*)args.a_bf16, m0, M, K, kc);
-    else if constexpr (!FAST) la.load(args.a_codes, m0, M, K, kc);
-  };
-  auto reg_store = [&](uint8_t* slot, int k) __attribute__((always_inline)) {
-    if constexpr (FUSED) fa.template quantize_store<BN>(slot, k & 1, gtab);
-    else if constexpr (!FAST) la.store(slot + SM::kA, k & 1);
-  };
-  auto load_stage_reg = [&](uint8_t* slot, int k) __attribute__((always_inline)) {
-    reg_load(k);
-    reg_store(slot, k);
-    if constexpr (!FAST) {
-      lw.load(grp.w_codes, n0, N, K, k);
-      lw.store(slot + SM::kW, k & 1);
-      ls.load(args.a_scales, grp.w_scales, m0, n0, M, N, K, k);
-      ls.store(slot, k & 1);
+    // Register-path fill of stage k into half (k & 1) of a slot.  FAST (only
+    // the fused A tile goes this way) clamps k to the last stage; the ragged
+    // loaders' bounds checks zero a stage past the end instead, which lets an
+    // odd stage count finish on a zero half.
+    // The A operand of a stage goes through registers in kParts parts (the
+    // fused prologue of a 256-row tile: two), part p loaded at pipeline step
+    // 2p and stored at step 2p + 2.
+    constexpr int kParts = FUSED ? FusedALoader<BM, FAST>::kParts : 1;
+    auto reg_load = [&](int k, int part) __attribute__((always_inline)) {
+      const int kc = FAST ? min(k, nk - 1) : k;
+      if constexpr (FUSED) fa.load((const uint16_t*)args.a_bf16, m0, M, K, kc, part);
+      else if constexpr (!FAST) la.load(args.a_codes, m0, M, K, kc);
+    };
+    auto reg_store = [&](uint8_t* slot, int k, int part) __attribute__((always_inline)) {
+      if constexpr (FUSED) fa.template quantize_store<BN, OVF>(slot, k & 1, gtab, part);
+      else if constexpr (!FAST) la.store(slot + SM::kA, k & 1);
+    };
+    // pipeline step of one A part's register traffic: store of part step/2 - 1,
+    // then load of part step/2
+    auto reg_step = [&](uint8_t* slot, int k, int step) __attribute__((always_inline)) {
+      if (step % 2 == 0 && step / 2 <= kParts) {
+        if (step > 0) reg_store(slot, k, step / 2 - 1);
+        if (step / 2 < kParts) reg_load(k, step / 2);
+      }
+    };
+    auto load_stage_reg = [&](uint8_t* slot, int k) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int part = 0; part < kParts; ++part) {
+        reg_load(k, part);
+        reg_store(slot, k, part);
+      }
+      if constexpr (!FAST) {
+        lw.load(grp.w_codes, n0, N, K, k);
+        lw.store(slot + SM::kW, k & 1);
+        ls.load(args.a_scales, grp.w_scales, m0, n0, M, N, K, k);
+        ls.store(slot, k & 1);
+      }
+    };
+    const int nd = (nk + 1) / 2;  // double stages (FAST shapes have nk even)
+
+    // prologue: double stages 0 and 1 into the two slots (stage 3, the second
+    // half of slot 1, comes from the register path in stage 0), then the pipe
+    // is primed with stage 0
+    if constexpr (FAST) {
+      dma.codes(smem, 0, true, 0, 1);
+      dma.scales(smem, 0, true);
+      dma.codes(smem + SM::kSlot, 1, nd > 1, 0, 1);
+      dma.scales(smem + SM::kSlot, 1, nd > 1);
     }
+    if constexpr (FUSED || !FAST) {
+      load_stage_reg(smem, 0);
+      load_stage_reg(smem, 1);
+      load_stage_reg(smem + SM::kSlot, 2);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): direct-to-LDS copies included
+    __syncthreads();
+    WavePipe<BM, BN> pipe;
+    pipe.init(wave_m, wave_n, li, lh);
+    pipe.template read_chunk<0, 0>(smem);
+    pipe.template read_chunk<0, 1>(smem);
+    pipe.template read_scales<0>(smem);
+    pipe.sigmas();
+    pipe.template dequant<0, 0>();
+
+    // Two LDS slots of two stages each.  In double stage d (slot cur; slot nxt
+    // holds d+1):
+    //  - even stage 2d pre-reads stage 2d+1 (cur, half 1); the register path
+    //    fills stage 2d+3 (nxt, half 1).  It ends with every wave's copies and
+    //    LDS operations complete and a barrier: afterwards slot nxt is whole
+    //    and nobody reads slot cur any more.
+    //  - odd stage 2d+1 pre-reads stage 2d+2 (nxt, half 0) and fills slot cur
+    //    with double stage d+2: direct copies (two stages to land, before the
+    //    next even barrier) and, on the register path, stage 2d+4 (half 0).
+    //    No barrier: the next writes to slot nxt come after the next one.
+    // Past the end the copies move nothing and register loads are clamped or
+    // zeroed; the reads' results are then ignored, so the loop has no branches.
+    uint8_t* cur = smem;
+    uint8_t* nxt = smem + SM::kSlot;
+    for (int d = 0; d < nd; ++d) {
+      const int k0 = 2 * d;
+      auto fill_even = [&](int step) __attribute__((always_inline)) {
+        if constexpr (FUSED || !FAST) {
+          const int k = k0 + 3;
+          reg_step(nxt, k, step);
+          if (step == 2) {
+            if constexpr (!FAST) lw.load(grp.w_codes, n0, N, K, k);
+          }
+          if constexpr (!FAST) {
+            if (step == 4) {
+              lw.store(nxt + SM::kW, 1);
+              ls.load(args.a_scales, grp.w_scales, m0, n0, M, N, K, k);
+            }
+            if (step == 6) ls.store(nxt, 1);
+          }
+        }
+      };
+      auto fill_odd = [&](int step) __attribute__((always_inline)) {
+        if constexpr (FUSED || !FAST) {
+          // register loads first: waiting for them then does not wait for
+          // this stage's direct copies (vmcnt counts in issue order)
+          const int k = k0 + 4;
+          reg_step(cur, k, step);
+          if (step == 2) {
+            if constexpr (!FAST) lw.load(grp.w_codes, n0, N, K, k);
+          }
+          if constexpr (!FAST) {
+            if (step == 4) {
+              lw.store(cur + SM::kW, 0);
+              ls.load(args.a_scales, grp.w_scales, m0, n0, M, N, K, k);
+            }
+            if (step == 6) ls.store(cur, 0);
+          }
+        }
+        if constexpr (FAST) {
+          const bool live = d + 2 < nd;
+          if (step < 4) dma.codes(cur, d + 2, live, step, 4);
+          if (step == 4) dma.scales(cur, d + 2, live);
+        }
+      };
+      run_step<0, 1>(pipe, acc, cur, fill_even);
+      run_step<1, 1>(pipe, acc, cur, fill_even);
+      run_step<2, 1>(pipe, acc, cur, fill_even);
+      run_step<3, 1>(pipe, acc, cur, fill_even);
+      run_step<4, 1>(pipe, acc, cur, fill_even);
+      run_step<5, 1>(pipe, acc, cur, fill_even);
+      run_step<6, 1>(pipe, acc, cur, fill_even);
+      run_step<7, 1>(pipe, acc, cur, fill_even);
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      run_step<0, 0>(pipe, acc, nxt, fill_odd);
+      run_step<1, 0>(pipe, acc, nxt, fill_odd);
+      run_step<2, 0>(pipe, acc, nxt, fill_odd);
+      run_step<3, 0>(pipe, acc, nxt, fill_odd);
+      run_step<4, 0>(pipe, acc, nxt, fill_odd);
+      run_step<5, 0>(pipe, acc, nxt, fill_odd);
+      run_step<6, 0>(pipe, acc, nxt, fill_odd);
+      run_step<7, 0>(pipe, acc, nxt, fill_odd);
+      uint8_t* t = cur;
+      cur = nxt;
+      nxt = t;
+    }
+    epilogue<BM, BN, OUT_F32>(acc, smem, grp.c, M, N, m0, n0, wave, lane, scale);
   };
-  const int nd = (nk + 1) / 2;  // double stages (FAST shapes have nk even)
-
-  // prologue: double stages 0 and 1 into the two slots (stage 3, the second
-  // half of slot 1, comes from the register path in stage 0), then the pipe
-  // is primed with stage 0
-  if constexpr (FAST) {
-    dma.codes(smem, 0, true, 0, 1);
-    dma.scales(smem, 0, true);
-    dma.codes(smem + SM::kSlot, 1, nd > 1, 0, 1);
-    dma.scales(smem + SM::kSlot, 1, nd > 1);
+  if constexpr (FUSED) {
+    if (gtab.ovf)
+      run(BoolC<true>{});
+    else
+      run(BoolC<false>{});
+  } else {
+    run(BoolC<false>{});
   }
-  if constexpr (FUSED || !FAST) {
-    load_stage_reg(smem, 0);
-    load_stage_reg(smem, 1);
-    load_stage_reg(smem + SM::kSlot, 2);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): direct-to-LDS copies included
-  __syncthreads();
-  WavePipe<BM, BN> pipe;
-  pipe.init(wave_m, wave_n, li, lh);
-  pipe.template read_chunk<0, 0>(smem);
-  pipe.template read_chunk<0, 1>(smem);
-  pipe.template read_scales<0>(smem);
-  pipe.sigmas();
-  pipe.template dequant<0, 0>();
-
-  // Two LDS slots of two stages each.  In double stage d (slot cur; slot nxt
-  // holds d+1):
-  //  - even stage 2d pre-reads stage 2d+1 (cur, half 1); the register path
-  //    fills stage 2d+3 (nxt, half 1).  It ends with every wave's copies and
-  //    LDS operations complete and a barrier: afterwards slot nxt is whole
-  //    and nobody reads slot cur any more.
-  //  - odd stage 2d+1 pre-reads stage 2d+2 (nxt, half 0) and fills slot cur
-  //    with double stage d+2: direct copies (two stages to land, before the
-  //    next even barrier) and, on the register path, stage 2d+4 (half 0).
-  //    No barrier: the next writes to slot nxt come after the next one.
-  // Past the end the copies move nothing and register loads are clamped or
-  // zeroed; the reads' results are then ignored, so the loop has no branches.
-  uint8_t* cur = smem;
-  uint8_t* nxt = smem + SM::kSlot;
-  for (int d = 0; d < nd; ++d) {
-    const int k0 = 2 * d;
-    auto fill_even = [&](int step) __attribute__((always_inline)) {
-      if constexpr (FUSED || !FAST) {
-        const int k = k0 + 3;
-        if (step == 0) reg_load(k);
-        if (step == 2) {
-          reg_store(nxt, k);
-          if constexpr (!FAST) lw.load(grp.w_codes, n0, N, K, k);
-        }
-        if constexpr (!FAST) {
-          if (step == 4) {
-            lw.store(nxt + SM::kW, 1);
-            ls.load(args.a_scales, grp.w_scales, m0, n0, M, N, K, k);
-          }
-          if (step == 6) ls.store(nxt, 1);
-        }
-      }
-    };
-    auto fill_odd = [&](int step) __attribute__((always_inline)) {
-      if constexpr (FUSED || !FAST) {
-        // register loads first: waiting for them then does not wait for
-        // this stage's direct copies (vmcnt counts in issue order)
-        const int k = k0 + 4;
-        if (step == 0) reg_load(k);
-        if (step == 2) {
-          reg_store(cur, k);
-          if constexpr (!FAST) lw.load(grp.w_codes, n0, N, K, k);
-        }
-        if constexpr (!FAST) {
-          if (step == 4) {
-            lw.store(cur + SM::kW, 0);
-            ls.load(args.a_scales, grp.w_scales, m0, n0, M, N, K, k);
-          }
-          if (step == 6) ls.store(cur, 0);
-        }
-      }
-      if constexpr (FAST) {
-        const bool live = d + 2 < nd;
-        if (step < 4) dma.codes(cur, d + 2, live, step, 4);
-        if (step == 4) dma.scales(cur, d + 2, live);
-      }
-    };
-    run_step<0, 1>(pipe, acc, cur, fill_even);
-    run_step<1, 1>(pipe, acc, cur, fill_even);
-    run_step<2, 1>(pipe, acc, cur, fill_even);
-    run_step<3, 1>(pipe, acc, cur, fill_even);
-    run_step<4, 1>(pipe, acc, cur, fill_even);
-    run_step<5, 1>(pipe, acc, cur, fill_even);
-    run_step<6, 1>(pipe, acc, cur, fill_even);
-    run_step<7, 1>(pipe, acc, cur, fill_even);
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    run_step<0, 0>(pipe, acc, nxt, fill_odd);
-    run_step<1, 0>(pipe, acc, nxt, fill_odd);
-    run_step<2, 0>(pipe, acc, nxt, fill_odd);
-    run_step<3, 0>(pipe, acc, nxt, fill_odd);
-    run_step<4, 0>(pipe, acc, nxt, fill_odd);
-    run_step<5, 0>(pipe, acc, nxt, fill_odd);
-    run_step<6, 0>(pipe, acc, nxt, fill_odd);
-    run_step<7, 0>(pipe, acc, nxt, fill_odd);
-    uint8_t* t = cur;
-    cur = nxt;
-    nxt = t;
-  }
-  epilogue<BM, BN, OUT_F32>(acc, smem, grp.c, M, N, m0, n0, wave, lane, scale);
 }
 
 // ------------------------------------------------------------------ host --

@@ -105,14 +105,17 @@ __device__ __forceinline__ float tensor_scale_from_amax(uint32_t amax_bits) {
 // every non-NaN binary32 y (checked exhaustively on gfx950 over all 2^32
 // patterns).  y is NaN only for x = +-0 with e = +inf (a group scale whose
 // reciprocal overflows); those elements get the sign-only code, as
-// e2m1_mag(NaN) = 0 prescribes.
+// e2m1_mag(NaN) = 0 prescribes.  That fix-up is compiled in only with OVF,
+// which callers select when the tensor scale is small enough for some
+// reciprocal to overflow (GroupScaleTab::ovf).
+template <bool OVF>
 __device__ __forceinline__ uint32_t encode8(const uint32_t w[4], float e) {
   uint32_t c = 0;
   c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, bf16_lo(w[0]) * e, bf16_hi(w[0]) * e, 1.0f, 0);
   c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, bf16_lo(w[1]) * e, bf16_hi(w[1]) * e, 1.0f, 1);
   c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, bf16_lo(w[2]) * e, bf16_hi(w[2]) * e, 1.0f, 2);
   c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, bf16_lo(w[3]) * e, bf16_hi(w[3]) * e, 1.0f, 3);
-  if (__builtin_expect(e > 3.0e38f, 0)) {
+  if (OVF && e > 3.0e38f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if ((w[i] & 0x7FFFu) == 0) c = (c & ~(0xFu << (8 * i))) | (((w[i] >> 15) & 1u) << (8 * i + 3));
@@ -129,18 +132,30 @@ __device__ __forceinline__ float group_recip(uint32_t S, float s_t) {
   return d > 0.0f ? 1.0f / d : 0.0f;
 }
 
-// Per-tensor constants of the group-scale computation: inv = RN64(1 / s_t)
-// and the table recip[S] = group_recip(S, s_t) for S = 0..127 (entry 127,
-// not an E4M3 finite value, is never selected for a valid s_t; it is filled
-// so that every index is defined).  Every thread of the block calls this;
-// the table is ready after the next barrier.
+// Per-tensor constants of the group-scale computation: inv = RN64(1 / s_t),
+// the table recip[S] = group_recip(S, s_t) for S = 0..127 (entry 127, not an
+// E4M3 finite value, is never selected for a valid s_t; it is filled so that
+// every index is defined), and ovf: whether some entry lies in the range
+// where encode8 needs its fix-up (an OR over the table: with a subnormal s_t
+// the smallest scales give d = 0 and a zero entry while larger ones still
+// overflow).  Every thread of the block must call this; it ends with a
+// barrier, after which the table is complete.
 struct GroupScaleTab {
   double inv;
   const float* recip;  // LDS
+  bool ovf;
 };
 __device__ __forceinline__ GroupScaleTab group_scale_tab(float s_t, float* recip_lds) {
-  for (int i = threadIdx.x; i < 128; i += blockDim.x) recip_lds[i] = group_recip((uint32_t)i, s_t);
-  return GroupScaleTab{1.0 / (double)s_t, recip_lds};
+  int big = 0;
+  for (int i = threadIdx.x; i < 128; i += blockDim.x) {
+    const float r = group_recip((uint32_t)i, s_t);
+    recip_lds[i] = r;
+    big |= r > 3.0e38f;
+  }
+  // uniform by construction; readfirstlane lets the compiler branch on it
+  // with a scalar test
+  const bool ovf = __builtin_amdgcn_readfirstlane(__syncthreads_or(big)) != 0;
+  return GroupScaleTab{1.0 / (double)s_t, recip_lds, ovf};
 }
 
 // Group scale of a group whose absolute maximum has the bf16 magnitude bits
@@ -163,14 +178,22 @@ __device__ __forceinline__ uint32_t group_scale(uint32_t am, const GroupScaleTab
 
 // Quantize one group of 16 bf16 values (8 words).  Writes 8 code bytes (two
 // words, even element in the low nibble) and returns the E4M3 scale byte.
+template <bool OVF>
 __device__ __forceinline__ uint32_t quantize_group16(const uint32_t w[8], const GroupScaleTab& tab,
                                                      uint32_t& codes_lo, uint32_t& codes_hi) {
   float e;
   const uint32_t S = group_scale(bf16_absmax_bits<8>(w), tab, e);
-  codes_lo = encode8(w, e);
-  codes_hi = encode8(w + 4, e);
+  codes_lo = encode8<OVF>(w, e);
+  codes_hi = encode8<OVF>(w + 4, e);
   return S;
 }
+
+// A compile-time bool passed to generic lambdas, which then instantiate one
+// copy of their body per value.
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
 
 // E4M3 byte -> binary16 bits (exact: every E4M3 value is a normal binary16).
 // Normal E4M3 (exponent field >= 1): same mantissa bits, exponent bias 15

@@ -110,40 +110,47 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
     }
   }
   const GroupScaleTab tab = group_scale_tab(s_t, recip);
-  __syncthreads();
   // nhalf and stride are even and a pair starts on an even index, so both
-  // lanes of a group enter and leave every loop iteration together
+  // lanes of a group enter and leave every loop iteration together.  The
+  // loops come in two copies, with and without encode8's overflow fix-up.
   const int64_t stride = (int64_t)gridDim.x * kQThreads;
-  constexpr int U = 4;
-  int64_t h = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
-  for (; h + (U - 1) * stride < nhalf; h += U * stride) {
-    uint4 v[U];
+  auto run = [&](auto ovf_c) __attribute__((always_inline)) {
+    constexpr bool OVF = decltype(ovf_c)::value;
+    constexpr int U = 4;
+    int64_t h = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
+    for (; h + (U - 1) * stride < nhalf; h += U * stride) {
+      uint4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = ld_stream(&x[h + u * stride]);
+      for (int u = 0; u < U; ++u) v[u] = ld_stream(&x[h + u * stride]);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      uint32_t am = uint4_absmax(v[u]);
+      for (int u = 0; u < U; ++u) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        uint32_t am = uint4_absmax(v[u]);
+        const uint32_t other = __shfl_xor(am, 1, 64);
+        am = am > other ? am : other;
+        float e;
+        const uint32_t S = group_scale(am, tab, e);
+        const int64_t hu = h + u * stride;
+        codes[hu] = encode8<OVF>(w, e);
+        if ((hu & 1) == 0) scales[hu >> 1] = (uint8_t)S;
+      }
+    }
+    for (; h < nhalf; h += stride) {
+      const uint4 v = ld_stream(&x[h]);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t am = uint4_absmax(v);
       const uint32_t other = __shfl_xor(am, 1, 64);
       am = am > other ? am : other;
       float e;
       const uint32_t S = group_scale(am, tab, e);
-      const int64_t hu = h + u * stride;
-      codes[hu] = encode8(w, e);
-      if ((hu & 1) == 0) scales[hu >> 1] = (uint8_t)S;
+      codes[h] = encode8<OVF>(w, e);
+      if ((h & 1) == 0) scales[h >> 1] = (uint8_t)S;
     }
-  }
-  for (; h < nhalf; h += stride) {
-    const uint4 v = ld_stream(&x[h]);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t am = uint4_absmax(v);
-    const uint32_t other = __shfl_xor(am, 1, 64);
-    am = am > other ? am : other;
-    float e;
-    const uint32_t S = group_scale(am, tab, e);
-    codes[h] = encode8(w, e);
-    if ((h & 1) == 0) scales[h >> 1] = (uint8_t)S;
-  }
+  };
+  if (tab.ovf)
+    run(BoolC<true>{});
+  else
+    run(BoolC<false>{});
 }
 
 static int grid_for(int64_t items, int threads, int max_blocks) {

@@ -121,6 +121,38 @@ def test_fused_prologue_bit_identical_to_unfused(M, N, K, seed):
     _assert_rule_t(_out(c_unf), ref, False)
 
 
+@pytest.mark.parametrize("K", [256, 272])
+def test_fused_prologue_reciprocal_overflow(K):
+    # activations of bf16 subnormals only: s_tA is so small that every
+    # reciprocal group scale overflows to +inf, where zero elements keep a
+    # sign-only code and the others saturate (the quantizer's fix-up path,
+    # compiled separately from the common one); large weights keep the
+    # output scale s_tA*s_tW normal, so a wrong code shows in the output
+    announce("gemm fused reciprocal overflow", K)
+    import torch
+    mq = _mq()
+    M, N = 64, 128
+    rng = np.random.default_rng(31 + K)
+    xa = np.zeros((M, K), np.uint16)
+    xa[rng.random((M, K)) < 0.3] = 0x8000                       # -0
+    nz = rng.random((M, K)) < 0.2
+    xa[nz] = rng.integers(1, 8, int(nz.sum())).astype(np.uint16) | \
+        np.where(rng.random(int(nz.sum())) < 0.5, 0x8000, 0).astype(np.uint16)
+    xw = workloads.random_bf16((N, K), 33, 1.0e37)
+    x = to_dev_bf16(xa)
+    qw = mq.quantize(to_dev_bf16(xw))
+    qa = mq.quantize(x)
+    oa = oracle.quantize_nvfp4(xa)
+    assert np.array_equal(qa.codes.cpu().numpy().reshape(oa.codes.shape), oa.codes)
+    c_unf = _gemm(qa, qw, M, N, f32=True)
+    c_fus, a = _fused(x, qw, M, N, f32=True)
+    assert torch.equal(c_unf.view(torch.int32), c_fus.view(torch.int32))
+    assert a.s_t() == qa.s_t()
+    ref = oracle.gemm_nvfp4_ref(oa, oracle.quantize_nvfp4(xw))
+    assert np.abs(ref).max() > 0
+    _assert_rule_t(_out(c_fus), ref, False)
+
+
 def test_fused_given_scale():
     announce("gemm fused given scale")
     import torch
