@@ -631,7 +631,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
   GroupScaleTab gtab{};
   if constexpr (FUSED) {
     __shared__ float recip_tab[128];
-    gtab = group_scale_tab(s_ta, recip_tab);
+    gtab = group_scale_tab<kThreads>(s_ta, recip_tab);
   }
 
   // Main loop and epilogue.  The fused prologue's kernels carry two copies,

@@ -138,16 +138,18 @@ __device__ __forceinline__ float group_recip(uint32_t S, float s_t) {
 // every index is defined), and ovf: whether some entry lies in the range
 // where encode8 needs its fix-up (an OR over the table: with a subnormal s_t
 // the smallest scales give d = 0 and a zero entry while larger ones still
-// overflow).  Every thread of the block must call this; it ends with a
+// overflow).  Every thread of the block (kBlock threads, a compile-time
+// constant: blockDim would be a memory load) must call this; it ends with a
 // barrier, after which the table is complete.
 struct GroupScaleTab {
   double inv;
   const float* recip;  // LDS
   bool ovf;
 };
+template <int kBlock>
 __device__ __forceinline__ GroupScaleTab group_scale_tab(float s_t, float* recip_lds) {
   int big = 0;
-  for (int i = threadIdx.x; i < 128; i += blockDim.x) {
+  for (int i = threadIdx.x; i < 128; i += kBlock) {
     const float r = group_recip((uint32_t)i, s_t);
     recip_lds[i] = r;
     big |= r > 3.0e38f;

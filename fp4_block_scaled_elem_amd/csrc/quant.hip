@@ -45,7 +45,7 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* sh) {
   if (lane == 0) sh[wave] = v;
   __syncthreads();
   uint32_t r = 0;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r = r > sh[i] ? r : sh[i];
+  for (int i = 0; i < kQThreads / 64; ++i) r = r > sh[i] ? r : sh[i];
   __syncthreads();
   return r;
 }
@@ -82,8 +82,42 @@ __global__ __launch_bounds__(kQThreads) void amax_kernel(const uint4* __restrict
 __device__ __forceinline__ uint32_t reduce_parts(const mq_scale_rec* __restrict__ rec, uint32_t* sh) {
   const uint32_t n = rec->nparts;
   uint32_t m = 0;
-  for (uint32_t j = threadIdx.x; j < n; j += blockDim.x) {
+  for (uint32_t j = threadIdx.x; j < n; j += kQThreads) {
     uint32_t v = rec->part[j];
+    m = m > v ? m : v;
+  }
+  return block_max_u32(m, sh);
+}
+
+// The scale record as the encode pass reads it: the given s_t, the number of
+// partial maxima and the first two per thread (up to 2 * kQThreads partials
+// without a loop), loaded before the input data, since a wait for a load
+// also waits for every load issued before it.
+struct RecHead {
+  float s_t;
+  uint32_t n, p[2];
+};
+__device__ __forceinline__ RecHead load_rec_head(const mq_scale_rec* __restrict__ rec) {
+  RecHead r;
+  r.s_t = rec->s_t;
+  r.n = rec->nparts;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int j = threadIdx.x + i * kQThreads;
+    r.p[i] = j < MQ_AMAX_PARTS ? rec->part[j] : 0u;
+  }
+  return r;
+}
+__device__ __forceinline__ uint32_t reduce_rec_head(const RecHead& r, const mq_scale_rec* __restrict__ rec,
+                                                    uint32_t* sh) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t j = threadIdx.x + i * kQThreads;
+    if (j < r.n) m = m > r.p[i] ? m : r.p[i];
+  }
+  for (uint32_t j = threadIdx.x + 2 * kQThreads; j < r.n; j += kQThreads) {
+    const uint32_t v = rec->part[j];
     m = m > v ? m : v;
   }
   return block_max_u32(m, sh);
@@ -98,34 +132,44 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
                                                              mq_scale_rec* __restrict__ rec, int given) {
   __shared__ uint32_t sh[kQThreads / 64];
   __shared__ float recip[128];
+  constexpr int U = 4;
+  const int64_t stride = (int64_t)gridDim.x * kQThreads;
+  int64_t h = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
+  // The first iteration's loads go out before the tensor scale is known:
+  // their latency overlaps the reduction of the partial maxima and the
+  // table build (the barriers there wait for LDS traffic only).
+  // These loads are unconditional (indices clamped into the input, which
+  // holds at least two half-groups), so that the wait for the record's
+  // loads can leave them in flight on every path.
+  const RecHead head = load_rec_head(rec);
+  uint4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t i = h + u * stride;
+    v[u] = ld_stream(&x[i < nhalf ? i : nhalf - 1]);
+  }
   float s_t;
   if (given) {
-    s_t = rec->s_t;
+    s_t = head.s_t;
   } else {
-    uint32_t amax = reduce_parts(rec, sh);
+    uint32_t amax = reduce_rec_head(head, rec, sh);
     s_t = tensor_scale_from_amax(amax);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
       rec->s_t = s_t;
       rec->amax_bits = amax;
     }
   }
-  const GroupScaleTab tab = group_scale_tab(s_t, recip);
+  const GroupScaleTab tab = group_scale_tab<kQThreads>(s_t, recip);
   // nhalf and stride are even and a pair starts on an even index, so both
   // lanes of a group enter and leave every loop iteration together.  The
   // loops come in two copies, with and without encode8's overflow fix-up.
-  const int64_t stride = (int64_t)gridDim.x * kQThreads;
   auto run = [&](auto ovf_c) __attribute__((always_inline)) {
     constexpr bool OVF = decltype(ovf_c)::value;
-    constexpr int U = 4;
-    int64_t h = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
-    for (; h + (U - 1) * stride < nhalf; h += U * stride) {
-      uint4 v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = ld_stream(&x[h + u * stride]);
+    auto encode_iter = [&](const uint4 (&vv)[U]) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-        uint32_t am = uint4_absmax(v[u]);
+        const uint32_t w[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+        uint32_t am = uint4_absmax(vv[u]);
         const uint32_t other = __shfl_xor(am, 1, 64);
         am = am > other ? am : other;
         float e;
@@ -134,11 +178,21 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
         codes[hu] = encode8<OVF>(w, e);
         if ((hu & 1) == 0) scales[hu >> 1] = (uint8_t)S;
       }
+    };
+    if (h + (U - 1) * stride < nhalf) {  // first iteration: data already loaded
+      encode_iter(v);
+      h += U * stride;
+    }
+    for (; h + (U - 1) * stride < nhalf; h += U * stride) {
+      uint4 nv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) nv[u] = ld_stream(&x[h + u * stride]);
+      encode_iter(nv);
     }
     for (; h < nhalf; h += stride) {
-      const uint4 v = ld_stream(&x[h]);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint32_t am = uint4_absmax(v);
+      const uint4 t = ld_stream(&x[h]);
+      const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+      uint32_t am = uint4_absmax(t);
       const uint32_t other = __shfl_xor(am, 1, 64);
       am = am > other ? am : other;
       float e;
