@@ -48,6 +48,17 @@ def test_ragged(M, N, K):
     _check(workloads.random_bf16((M, K), M + N, 1.0), workloads.random_bf16((N, K), K, 0.02))
 
 
+@pytest.mark.parametrize("M", list(range(1, 33)))
+def test_every_row_count(M):
+    # every M in 1..32: the ring kernel copies only the X row groups below M
+    # (one copy per four rows) and takes 32 W rows per workgroup above 16;
+    # N = 48 and 17 leave the last workgroup's second W tile partly or
+    # almost entirely past N
+    N = 48 if M % 2 else 17
+    announce("gemv rows", M, N)
+    _check(workloads.random_bf16((M, 512), 100 + M, 1.0), workloads.random_bf16((N, 512), 200 + M, 0.02))
+
+
 def test_one_hot_rows_are_exact():
     announce("gemv one-hot")
     M, N, K = 20, 300, 1024
