@@ -244,6 +244,46 @@ def decode_gemv_rates(reps=50):
     return res
 
 
+def phase_linear_rates(reps=50):
+    """The phase-aware linear (mq_linear_forward) on the 8B q projection's
+    weight (4096 x 4096, both formats resident): a decode step at M = 1 and
+    32 routes to the BF16 GEMV, a 4096-token prefill to quantize + NVFP4
+    GEMM; each timed next to the direct calls it routes to (the dispatch is
+    host logic).  Weights rotate over copies past the Infinity Cache for the
+    decode rows; the prefill is compute-bound."""
+    import torch
+    import fp4_block_scaled_elem_amd as mq
+    import workloads
+    N, K = workloads.LLAMA8B.proj_nk("q")
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    ncopy = max(2, -(-600 * 2 ** 20 // (2 * N * K)))
+    lins = [mq.Linear((torch.randn((N, K), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)).prepare()
+            for _ in range(ncopy)]
+    res = {}
+    for M in (1, 32, 4096):
+        x = torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        a = mq.NVFP4.empty(M, K)
+        path = lins[0].path(M)
+        if path == mq.MQ_PATH_DECODE_BF16:
+            direct = lambda r: mq.mq_gemv_bf16_decode(x, lins[r % ncopy].w_bf16, y)
+        else:
+            def direct(r):
+                mq.mq_quantize_nvfp4(x, a)
+                mq.mq_gemm_nvfp4_prefill(a, None, lins[r % ncopy].w_nvfp4, y)
+        med, _ = _median_us(lambda r: lins[r % ncopy].forward(x, out=y, a_work=a), reps=reps)
+        dmed, _ = _median_us(direct, reps=reps)
+        entry = {"path": "decode_bf16" if path == mq.MQ_PATH_DECODE_BF16 else "prefill_nvfp4",
+                 "us_median": round(med, 2), "direct_us_median": round(dmed, 2)}
+        if path == mq.MQ_PATH_DECODE_BF16:
+            entry["GBps"] = round((2 * N * K + 2 * M * K + 2 * M * N) / med / 1e3, 1)
+        else:
+            entry["tflops"] = round(2 * M * N * K / med / 1e6, 1)
+        res[f"M{M}"] = entry
+    del lins
+    return res
+
+
 def bf16_reference(cfg, acts, wdev, iters=10):
     """torch's BF16 GEMM (hipBLASLt) at the same shapes, TFLOP/s."""
     import torch
@@ -364,6 +404,7 @@ def main():
     launches = per_launch(cfg, plan, acts, qw, qa, fa, out, events, args.steps)
     quant = None if (args.no_extras or cfg.fused_act_quant) else act_quant_rates(acts)
     gemv = None if args.no_extras else decode_gemv_rates()
+    phase = None if args.no_extras else phase_linear_rates()
     bf16 = None if args.no_bf16 else bf16_reference(cfg, acts, wdev)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.config, acts_host, args.cpu_rows, args.cpu_wrows)
 
@@ -395,6 +436,7 @@ def main():
         "per_launch": launches,
         "act_quant": quant,
         "decode_gemv": gemv,
+        "phase_linear": phase,
         "bf16_torch_tflops": None if bf16 is None else round(bf16, 2),
         "ratio_vs_bf16_torch": None if bf16 is None else round(value / bf16, 3),
         "cpu_baseline": cpu,

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI in include/mq.h):
     mq_gemm_nvfp4_prefill(a: NVFP4, a_bf16, w: NVFP4, c, flags=0, stream=None)
     mq_gemm_nvfp4_prefill_grouped(a: NVFP4, a_bf16, ws: [NVFP4], cs: [tensor], flags=0, stream=None)
     mq_gemv_bf16_decode(x_bf16, w_bf16, y_bf16, flags=0, stream=None)
+    mq_linear_path / mq_linear_prepare / mq_linear_forward (through ``Linear``)
 
 and small conveniences built on them (``quantize``, ``prefill_linear``,
 ``decode_linear``).
@@ -36,12 +37,17 @@ MQ_SCALE_GIVEN = 1
 MQ_OUT_BF16 = 0
 MQ_OUT_F32 = 2
 MQ_A_FUSED_BF16 = 4
+MQ_PHASE_PREFILL = 8
+MQ_PHASE_DECODE = 16
+MQ_PATH_DECODE_BF16 = 1
+MQ_PATH_PREFILL_NVFP4 = 2
 MQ_AMAX_PARTS = 1020
 MQ_MAX_GROUP = 4
 REC_BYTES = 16 + 4 * MQ_AMAX_PARTS  # sizeof(mq_scale_rec) = 4096
 
 EXPORTS = ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemm_nvfp4_prefill_grouped",
-           "mq_gemv_bf16_decode", "mq_status_str", "mq_last_error", "mq_version")
+           "mq_gemv_bf16_decode", "mq_linear_path", "mq_linear_prepare", "mq_linear_forward",
+           "mq_status_str", "mq_last_error", "mq_version")
 
 
 class LibraryNotBuilt(ImportError):
@@ -56,6 +62,11 @@ class MQError(RuntimeError):
 
 class _NVFP4C(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("rec", ctypes.c_void_p)]
+
+
+class _LinearC(ctypes.Structure):
+    _fields_ = [("w_bf16", ctypes.c_void_p), ("w_nvfp4", _NVFP4C), ("N", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("prefill_min_rows", ctypes.c_int64)]
 
 
 _lib = None
@@ -81,6 +92,13 @@ def lib():
     L.mq_gemm_nvfp4_prefill_grouped.restype = ctypes.c_int32
     L.mq_gemv_bf16_decode.argtypes = [vp, vp, vp, i64, i64, i64, u32, vp]
     L.mq_gemv_bf16_decode.restype = ctypes.c_int32
+    LP = ctypes.POINTER(_LinearC)
+    L.mq_linear_path.argtypes = [LP, i64, u32]
+    L.mq_linear_path.restype = ctypes.c_int32
+    L.mq_linear_prepare.argtypes = [LP, vp]
+    L.mq_linear_prepare.restype = ctypes.c_int32
+    L.mq_linear_forward.argtypes = [LP, vp, i64, P, vp, u32, vp]
+    L.mq_linear_forward.restype = ctypes.c_int32
     L.mq_status_str.argtypes = [ctypes.c_int32]
     L.mq_status_str.restype = ctypes.c_char_p
     L.mq_last_error.argtypes = []
@@ -228,6 +246,57 @@ def mq_gemv_bf16_decode(x_bf16, w_bf16, y_bf16, flags: int = 0, stream=None):
         raise ValueError("shape mismatch")
     _check(lib().mq_gemv_bf16_decode(_dev_ptr(x_bf16, "x"), _dev_ptr(w_bf16, "w"), _dev_ptr(y_bf16, "y"),
                                      M, N, K, flags, _stream_ptr(stream)), "mq_gemv_bf16_decode")
+
+
+class Linear:
+    """One weight W [N][K] in both formats: the original bf16 tensor (decode
+    path) and its NVFP4 copy (prefill path), filled by ``prepare``.  Each
+    ``forward`` goes through mq_linear_forward, which routes the call by its
+    phase flag, or by its row count when it names none (M >= prefill_min_rows
+    is prefill)."""
+
+    def __init__(self, w_bf16, prefill_min_rows: int = 33):
+        import torch
+        if w_bf16.dtype != torch.bfloat16 or w_bf16.dim() != 2:
+            raise ValueError("w_bf16 must be a 2-D bfloat16 tensor")
+        self.w_bf16 = w_bf16
+        self.N, self.K = w_bf16.shape
+        self.w_nvfp4 = NVFP4.empty(self.N, self.K, device=w_bf16.device)
+        self.prefill_min_rows = prefill_min_rows
+
+    def _c(self):
+        return _LinearC(_dev_ptr(self.w_bf16, "w_bf16").value, self.w_nvfp4._c(), self.N, self.K,
+                        self.prefill_min_rows)
+
+    def path(self, M: int, flags: int = 0) -> int:
+        """MQ_PATH_DECODE_BF16, MQ_PATH_PREFILL_NVFP4, or 0 (rejected)."""
+        lc = self._c()
+        return lib().mq_linear_path(ctypes.byref(lc), M, flags)
+
+    def prepare(self, stream=None):
+        lc = self._c()
+        _check(lib().mq_linear_prepare(ctypes.byref(lc), _stream_ptr(stream)), "mq_linear_prepare")
+        return self
+
+    def forward(self, x_bf16, out=None, flags: int = 0, a_work: NVFP4 | None = None, stream=None):
+        import torch
+        if x_bf16.dtype != torch.bfloat16 or x_bf16.dim() != 2 or x_bf16.shape[1] != self.K:
+            raise ValueError(f"x must be bfloat16 [M][{self.K}]")
+        M = x_bf16.shape[0]
+        y = out if out is not None else torch.empty((M, self.N), dtype=torch.bfloat16, device=x_bf16.device)
+        if y.dtype != torch.bfloat16 or tuple(y.shape) != (M, self.N):
+            raise ValueError(f"out must be bfloat16 [{M}][{self.N}]")
+        if a_work is None and self.path(M, flags) == MQ_PATH_PREFILL_NVFP4:
+            if flags & MQ_A_FUSED_BF16:
+                a_work = NVFP4(None, None, torch.zeros(REC_BYTES // 4, dtype=torch.int32, device=x_bf16.device))
+            else:
+                a_work = NVFP4.empty(M, self.K, device=x_bf16.device)
+        lc = self._c()
+        ac = a_work._c() if a_work is not None else None
+        _check(lib().mq_linear_forward(ctypes.byref(lc), _dev_ptr(x_bf16, "x"), M,
+                                       ctypes.byref(ac) if ac is not None else None, _dev_ptr(y, "out"),
+                                       flags, _stream_ptr(stream)), "mq_linear_forward")
+        return y
 
 
 # ---------------------------------------------------------------- helpers --

@@ -183,4 +183,76 @@ mq_status mq_gemv_bf16_decode(const void* x_bf16, const void* w_bf16, void* y_bf
   return launched(mq::launch_gemv(x_bf16, w_bf16, y_bf16, M, N, K, dev, (hipStream_t)hip_stream), "gemv");
 }
 
+// ------------------------------------------------------- phase-aware linear --
+
+int32_t mq_linear_path(const mq_linear* L, int64_t M, uint32_t flags) {
+  if (!L || M < 1) return 0;
+  if (L->prefill_min_rows < 1 || L->prefill_min_rows > 33) return 0;
+  const uint32_t phase = flags & (MQ_PHASE_PREFILL | MQ_PHASE_DECODE);
+  if (phase == (MQ_PHASE_PREFILL | MQ_PHASE_DECODE)) return 0;
+  const bool prefill = phase == MQ_PHASE_PREFILL || (phase == 0 && M >= L->prefill_min_rows);
+  if (prefill) return MQ_PATH_PREFILL_NVFP4;
+  return M <= 32 ? MQ_PATH_DECODE_BF16 : 0;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks of the weight side of a linear, shared by prepare and forward.
+mq_status check_linear(const mq_linear* L) {
+  if (!L) return fail(MQ_ERR_INVALID, "L must not be NULL");
+  if (!L->w_bf16 || !L->w_nvfp4.codes || !L->w_nvfp4.scales || !L->w_nvfp4.rec)
+    return fail(MQ_ERR_INVALID, "L->w_bf16 and L->w_nvfp4 codes, scales and rec must not be NULL");
+  if (mq_status s = check_dims(L->N, L->K, "N", "K")) return s;
+  if (L->K % 16) return fail(MQ_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)L->K);
+  if (!aligned(L->w_bf16, 16) || !aligned(L->w_nvfp4.codes, 16) || !aligned(L->w_nvfp4.scales, 8) ||
+      !aligned(L->w_nvfp4.rec, 16))
+    return fail(MQ_ERR_ALIGN, "w_bf16 and codes need 16-byte, scales 8-byte, rec 16-byte alignment");
+  return MQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mq_status mq_linear_prepare(const mq_linear* L, void* hip_stream) {
+  if (mq_status s = check_linear(L)) return s;
+  return mq_quantize_nvfp4(L->w_bf16, L->N, L->K, &L->w_nvfp4, MQ_SCALE_DYNAMIC, hip_stream);
+}
+
+mq_status mq_linear_forward(const mq_linear* L, const void* x_bf16, int64_t M, const mq_nvfp4* a_work,
+                            void* y_bf16, uint32_t flags, void* hip_stream) {
+  const uint32_t known = MQ_PHASE_PREFILL | MQ_PHASE_DECODE | MQ_A_FUSED_BF16;
+  if (flags & ~known) return fail(MQ_ERR_INVALID, "unknown flags 0x%x", flags);
+  if ((flags & MQ_PHASE_PREFILL) && (flags & MQ_PHASE_DECODE))
+    return fail(MQ_ERR_INVALID, "MQ_PHASE_PREFILL and MQ_PHASE_DECODE are exclusive");
+  if (mq_status s = check_linear(L)) return s;
+  if (L->prefill_min_rows < 1 || L->prefill_min_rows > 33)
+    return fail(MQ_ERR_INVALID, "prefill_min_rows=%lld must be in 1..33", (long long)L->prefill_min_rows);
+  if (!x_bf16 || !y_bf16) return fail(MQ_ERR_INVALID, "x and y must not be NULL");
+  if (M < 1 || M > kMaxDim) return fail(MQ_ERR_SHAPE, "M=%lld out of range", (long long)M);
+  const int32_t path = mq_linear_path(L, M, flags);
+  if (path == 0) return fail(MQ_ERR_SHAPE, "M=%lld: a decode call takes 1..32 rows", (long long)M);
+  if (!aligned(x_bf16, 16)) return fail(MQ_ERR_ALIGN, "x needs 16-byte alignment");
+  if (path == MQ_PATH_DECODE_BF16) {
+    if (!aligned(y_bf16, 2)) return fail(MQ_ERR_ALIGN, "y needs 2-byte alignment");
+    return mq_gemv_bf16_decode(x_bf16, L->w_bf16, y_bf16, M, L->N, L->K, 0, hip_stream);
+  }
+  // prefill: every check of both launches before the first is queued
+  const bool fused = flags & MQ_A_FUSED_BF16;
+  if (!a_work || !a_work->rec) return fail(MQ_ERR_INVALID, "a prefill call needs a_work with rec");
+  if (!fused && (!a_work->codes || !a_work->scales))
+    return fail(MQ_ERR_INVALID, "a_work->codes and a_work->scales must not be NULL");
+  if (!aligned(a_work->rec, 16) || (!fused && (!aligned(a_work->codes, 16) || !aligned(a_work->scales, 8))))
+    return fail(MQ_ERR_ALIGN, "a_work: codes need 16-byte, scales 8-byte, rec 16-byte alignment");
+  if (!aligned(y_bf16, 16)) return fail(MQ_ERR_ALIGN, "y needs 16-byte alignment on the prefill path");
+  if (M * L->K > ((int64_t)1 << 40) || M * L->N > ((int64_t)1 << 40))
+    return fail(MQ_ERR_SHAPE, "M=%lld exceeds the supported size", (long long)M);
+  if (fused)
+    return mq_gemm_nvfp4_prefill(a_work, x_bf16, &L->w_nvfp4, y_bf16, M, L->N, L->K, MQ_A_FUSED_BF16, hip_stream);
+  if (mq_status s = mq_quantize_nvfp4(x_bf16, M, L->K, a_work, MQ_SCALE_DYNAMIC, hip_stream)) return s;
+  return mq_gemm_nvfp4_prefill(a_work, nullptr, &L->w_nvfp4, y_bf16, M, L->N, L->K, 0, hip_stream);
+}
+
 }  // extern "C"

@@ -17,6 +17,10 @@
  *                          the same for several weights that share A, in one
  *                          launch
  *   mq_gemv_bf16_decode    Y = X . W^T on bf16 X [M][K] and W [N][K]
+ *   mq_linear_prepare / mq_linear_forward / mq_linear_path
+ *                          one weight kept in both formats (original BF16
+ *                          and an NVFP4 copy), each call routed to the
+ *                          prefill (NVFP4) or decode (BF16) path
  *
  * Formats (readings where the pages are silent):
  *   element   OCP E2M1 4-bit code = sign<<3 | magnitude index, magnitudes
@@ -104,6 +108,8 @@ typedef struct mq_nvfp4 {
 #define MQ_OUT_BF16      0u  /* GEMM output bf16 (default)                      */
 #define MQ_OUT_F32       2u  /* GEMM output binary32 (pre-rounding value)       */
 #define MQ_A_FUSED_BF16  4u  /* GEMM: A given as bf16, quantized in-kernel      */
+#define MQ_PHASE_PREFILL 8u  /* linear: this call is a prefill (NVFP4 path)     */
+#define MQ_PHASE_DECODE 16u  /* linear: this call is a decode step (BF16 path)  */
 
 /*
  * mq_quantize_nvfp4 - quantize a bf16 matrix to NVFP4.
@@ -189,6 +195,74 @@ mq_status mq_gemm_nvfp4_prefill_grouped(const mq_nvfp4* a, const void* a_bf16,
 mq_status mq_gemv_bf16_decode(const void* x_bf16, const void* w_bf16,
                               void* y_bf16, int64_t M, int64_t N, int64_t K,
                               uint32_t flags, void* hip_stream);
+
+/*
+ * Phase-aware linear layer.  The method keeps each weight matrix in two
+ * formats and picks one per inference phase (gist.science English explainer,
+ * s.2 Hybrid Precision Strategy: prefill in NVFP4 for weights and
+ * activations, decode on the original BF16 weights; s.2 System-Level
+ * Deployment: the two phases run on separate prefill and decode workers).
+ * mq_linear holds both formats of one weight W [N][K]; a call names its
+ * phase in its flags, or leaves it to the row count (decode steps carry one
+ * row per sequence of the batch, prefills the prompt's tokens): calls with
+ * M >= prefill_min_rows are taken as prefill.  The row threshold is this
+ * library's reading; the pages name the phases, not a size.
+ */
+typedef struct mq_linear {
+  const void* w_bf16;        /* DEVICE bf16 [N][K], 16-byte aligned: the
+                                original weights (decode path)              */
+  mq_nvfp4 w_nvfp4;          /* DEVICE NVFP4 copy of w_bf16 [N][K] (prefill
+                                path), written by mq_linear_prepare          */
+  int64_t N, K;              /* N >= 1; K >= 16, K % 16 == 0                */
+  int64_t prefill_min_rows;  /* 1..33: rows at which a call without a phase
+                                flag counts as prefill (33: every batch the
+                                decode path supports stays on it)           */
+} mq_linear;
+
+#define MQ_PATH_DECODE_BF16   1  /* mq_gemv_bf16_decode on w_bf16              */
+#define MQ_PATH_PREFILL_NVFP4 2  /* quantize X, mq_gemm_nvfp4_prefill on w_nvfp4 */
+
+/*
+ * mq_linear_path - the path a call with M rows and these flags takes:
+ *   MQ_PHASE_PREFILL -> MQ_PATH_PREFILL_NVFP4; MQ_PHASE_DECODE ->
+ *   MQ_PATH_DECODE_BF16 (M <= 32); neither -> by prefill_min_rows.
+ *   Returns 0 for arguments mq_linear_forward would reject on that ground
+ *   (L NULL, M < 1, both phase flags, a decode call with M > 32,
+ *   prefill_min_rows outside 1..33).  Host only: no device work.
+ */
+int32_t mq_linear_path(const mq_linear* L, int64_t M, uint32_t flags);
+
+/*
+ * mq_linear_prepare - the offline step: quantize L->w_bf16 into L->w_nvfp4
+ *   with its own tensor scale over the whole matrix (mq_quantize_nvfp4,
+ *   dynamic).  Queued on hip_stream like every call; the NVFP4 copy is
+ *   valid for calls queued after it on the same stream.
+ */
+mq_status mq_linear_prepare(const mq_linear* L, void* hip_stream);
+
+/*
+ * mq_linear_forward - Y[M][N] = X[M][K] . W^T through the call's phase.
+ *   Decode (MQ_PATH_DECODE_BF16): mq_gemv_bf16_decode(x, L->w_bf16, y);
+ *   M <= 32; a_work is not used (may be NULL); MQ_A_FUSED_BF16 is ignored.
+ *   Prefill (MQ_PATH_PREFILL_NVFP4): X is quantized on the fly into a_work
+ *   (mq_quantize_nvfp4, dynamic scale), then mq_gemm_nvfp4_prefill with
+ *   L->w_nvfp4, bf16 output; with MQ_A_FUSED_BF16 the quantization runs in
+ *   the GEMM's prologue instead (a_work->rec is still used; codes and scales
+ *   may be NULL).
+ *   Each path's output is bit-identical to the direct calls it names.
+ * L        HOST pointer; L->w_nvfp4 must hold mq_linear_prepare's result
+ *          before a prefill call runs.
+ * x_bf16   DEVICE bf16 [M][K], 16-byte aligned.
+ * a_work   HOST pointer to caller-owned NVFP4 buffers for X [M][K] (codes
+ *          16-byte, scales 8-byte, rec 16-byte aligned); prefill only.
+ * y_bf16   DEVICE bf16 [M][N]; 16-byte aligned for prefill, 2 for decode.
+ * flags    0, MQ_PHASE_PREFILL or MQ_PHASE_DECODE, optionally
+ *          | MQ_A_FUSED_BF16.
+ * All arguments of the chosen path are checked before anything is queued.
+ */
+mq_status mq_linear_forward(const mq_linear* L, const void* x_bf16, int64_t M,
+                            const mq_nvfp4* a_work, void* y_bf16,
+                            uint32_t flags, void* hip_stream);
 
 /* Static string naming a status code. */
 const char* mq_status_str(mq_status s);

@@ -36,7 +36,7 @@ def L():
 def test_header_declares_the_entry_points():
     fns = _header_functions()
     for f in ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemm_nvfp4_prefill_grouped",
-              "mq_gemv_bf16_decode"):
+              "mq_gemv_bf16_decode", "mq_linear_path", "mq_linear_prepare", "mq_linear_forward"):
         assert f in fns
 
 
@@ -149,6 +149,63 @@ def test_gemv_argument_errors(L):
     assert f(P16, P16, P1, 1, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
 
 
+def _lin(w=P16, codes=P16, scales=P16, rec=P16, N=4, K=16, pmin=33):
+    return ctypes.byref(mq._LinearC(w, mq._NVFP4C(codes, scales, rec), N, K, pmin))
+
+
+def test_linear_path_routing(L):
+    # the phase flag decides; without one the row count does (M >= pmin is
+    # prefill); a decode call takes at most 32 rows
+    f = L.mq_linear_path
+    D, P = mq.MQ_PATH_DECODE_BF16, mq.MQ_PATH_PREFILL_NVFP4
+    for M in (1, 2, 16, 31, 32):
+        assert f(_lin(), M, 0) == D
+    for M in (33, 64, 4096, 1 << 20):
+        assert f(_lin(), M, 0) == P
+    assert f(_lin(pmin=1), 1, 0) == P
+    assert f(_lin(pmin=17), 16, 0) == D and f(_lin(pmin=17), 17, 0) == P
+    assert f(_lin(), 1, mq.MQ_PHASE_PREFILL) == P
+    assert f(_lin(), 4096, mq.MQ_PHASE_PREFILL | mq.MQ_A_FUSED_BF16) == P
+    assert f(_lin(), 32, mq.MQ_PHASE_DECODE) == D
+    assert f(_lin(pmin=1), 5, mq.MQ_PHASE_DECODE) == D
+    assert f(_lin(), 33, mq.MQ_PHASE_DECODE) == 0
+    assert f(_lin(), 1, mq.MQ_PHASE_PREFILL | mq.MQ_PHASE_DECODE) == 0
+    assert f(_lin(), 0, 0) == 0
+    assert f(_lin(pmin=0), 1, 0) == 0 and f(_lin(pmin=34), 1, 0) == 0
+    assert f(None, 1, 0) == 0
+
+
+def test_linear_argument_errors(L):
+    fw, fp = L.mq_linear_forward, L.mq_linear_prepare
+    a = _q(P16, P16, P16)
+    assert fp(None, None) == mq.MQ_ERR_INVALID
+    assert fp(_lin(w=None), None) == mq.MQ_ERR_INVALID
+    assert fp(_lin(rec=None), None) == mq.MQ_ERR_INVALID
+    assert fp(_lin(K=24), None) == mq.MQ_ERR_SHAPE
+    assert fp(_lin(N=0), None) == mq.MQ_ERR_SHAPE
+    assert fp(_lin(w=P8), None) == mq.MQ_ERR_ALIGN
+    assert fp(_lin(scales=P1), None) == mq.MQ_ERR_ALIGN
+    assert fw(_lin(), P16, 1, None, P16, 64, None) == mq.MQ_ERR_INVALID                   # unknown flag
+    assert fw(_lin(), P16, 1, None, P16, mq.MQ_PHASE_PREFILL | mq.MQ_PHASE_DECODE, None) == mq.MQ_ERR_INVALID
+    assert fw(None, P16, 1, None, P16, 0, None) == mq.MQ_ERR_INVALID
+    assert fw(_lin(pmin=34), P16, 1, None, P16, 0, None) == mq.MQ_ERR_INVALID
+    assert fw(_lin(), None, 1, None, P16, 0, None) == mq.MQ_ERR_INVALID
+    assert fw(_lin(), P16, 1, None, None, 0, None) == mq.MQ_ERR_INVALID
+    assert fw(_lin(), P16, 0, None, P16, 0, None) == mq.MQ_ERR_SHAPE
+    assert fw(_lin(), P16, 40, a, P16, mq.MQ_PHASE_DECODE, None) == mq.MQ_ERR_SHAPE
+    assert "decode" in mq.last_error()
+    assert fw(_lin(), P8, 1, None, P16, 0, None) == mq.MQ_ERR_ALIGN
+    assert fw(_lin(), P16, 1, None, P1, 0, None) == mq.MQ_ERR_ALIGN                        # decode: y 2-byte
+    # prefill calls need a_work (its rec always; codes and scales unless fused)
+    assert fw(_lin(), P16, 64, None, P16, 0, None) == mq.MQ_ERR_INVALID
+    assert fw(_lin(), P16, 64, _q(P16, P16, None), P16, 0, None) == mq.MQ_ERR_INVALID
+    assert fw(_lin(), P16, 64, _q(None, P16, P16), P16, 0, None) == mq.MQ_ERR_INVALID
+    assert fw(_lin(), P16, 64, _q(P16, P1, P16), P16, 0, None) == mq.MQ_ERR_ALIGN
+    assert fw(_lin(), P16, 64, a, P8, 0, None) == mq.MQ_ERR_ALIGN                          # prefill: y 16-byte
+    assert fw(_lin(), P16, 1, a, P8, mq.MQ_PHASE_PREFILL, None) == mq.MQ_ERR_ALIGN
+    assert fw(_lin(N=1 << 30), P16, 1 << 11, a, P16, 0, None) == mq.MQ_ERR_SHAPE
+
+
 def _no_gpu():
     try:
         import torch
@@ -165,6 +222,11 @@ def test_valid_arguments_without_a_gpu_report_device_error(L):
     assert L.mq_gemv_bf16_decode(P16, P16, P16, 1, 4, 16, 0, None) == mq.MQ_ERR_DEVICE
     w = (P16, P16, P16)
     assert _grouped(L, _q(P16, P16, P16), None, [w, w, w], [P16, P16, P16], [4, 8, 12]) == mq.MQ_ERR_DEVICE
+    assert L.mq_linear_prepare(_lin(), None) == mq.MQ_ERR_DEVICE
+    assert L.mq_linear_forward(_lin(), P16, 1, None, P1 + 1, 0, None) == mq.MQ_ERR_DEVICE
+    assert L.mq_linear_forward(_lin(), P16, 64, _q(P16, P16, P16), P16, 0, None) == mq.MQ_ERR_DEVICE
+    assert L.mq_linear_forward(_lin(), P16, 64, _q(None, None, P16), P16, mq.MQ_A_FUSED_BF16,
+                               None) == mq.MQ_ERR_DEVICE
     assert mq.last_error()
 
 
