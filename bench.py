@@ -244,6 +244,42 @@ def decode_gemv_rates(reps=50):
     return res
 
 
+def decode_nvfp4_rates(bf16_rates=None, reps=50):
+    """The uniform-NVFP4 decode GEMV (X and W both NVFP4) at the decode
+    configuration's shapes, M in {1, 16, 32}; weights rotated over copies
+    past the 256 MB Infinity Cache.  GB/s over the algorithmic bytes
+    0.5625 (N K + M K) + 2 M N, and the time relative to the BF16 decode GEMV
+    at the same shape (bf16_rates: decode_gemv_rates' result).  X is
+    quantized once outside the timed calls (its M x K elements are small)."""
+    import torch
+    import fp4_block_scaled_elem_amd as mq
+    import workloads
+    lay = workloads.LLAMA8B
+    res = {}
+    for p in ("q", "k", "gate", "down"):
+        N, K = lay.proj_nk(p)
+        wbytes = N * K * 9 // 16
+        ncopy = max(2, -(-600 * 2 ** 20 // wbytes))
+        gen = torch.Generator(device="cuda").manual_seed(2000 + N + K)
+        ws = []
+        for _ in range(ncopy):
+            ws.append(mq.quantize((torch.randn((N, K), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)))
+        for M in (1, 16, 32):
+            xq = mq.quantize(torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16))
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            med, mn = _median_us(lambda r: mq.mq_gemv_nvfp4_decode(xq, ws[r % ncopy], y), reps=reps)
+            b = (N * K + M * K) * 9 // 16 + 2 * M * N
+            e = {"N": N, "K": K, "M": M, "us_median": round(med, 2), "us_min": round(mn, 2),
+                 "GBps": round(b / med / 1e3, 1), "pct_hbm": round(100 * b / med / 1e3 / PEAK_HBM_GBS, 1)}
+            ref = (bf16_rates or {}).get(f"{p}_M{M}")
+            if ref:
+                e["bf16_gemv_us"] = ref["us_median"]
+                e["speedup_vs_bf16"] = round(ref["us_median"] / med, 2)
+            res[f"{p}_M{M}"] = e
+        del ws
+    return res
+
+
 def phase_linear_rates(reps=50):
     """The phase-aware linear (mq_linear_forward) on the 8B q projection's
     weight (4096 x 4096, both formats resident): a decode step at M = 1 and
@@ -367,7 +403,8 @@ def main():
         copy_calibration()
         return
     if args.decode_only:
-        print(json.dumps({"decode_gemv": decode_gemv_rates()}), flush=True)
+        gemv = decode_gemv_rates()
+        print(json.dumps({"decode_gemv": gemv, "decode_nvfp4_gemv": decode_nvfp4_rates(gemv)}), flush=True)
         return
     cfg, acts_host, acts, wdev, qw, qa, fa, out = setup(args.config)
     flops = cfg.flops()
@@ -404,6 +441,7 @@ def main():
     launches = per_launch(cfg, plan, acts, qw, qa, fa, out, events, args.steps)
     quant = None if (args.no_extras or cfg.fused_act_quant) else act_quant_rates(acts)
     gemv = None if args.no_extras else decode_gemv_rates()
+    gemv_fp4 = None if args.no_extras else decode_nvfp4_rates(gemv)
     phase = None if args.no_extras else phase_linear_rates()
     bf16 = None if args.no_bf16 else bf16_reference(cfg, acts, wdev)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.config, acts_host, args.cpu_rows, args.cpu_wrows)
@@ -436,6 +474,7 @@ def main():
         "per_launch": launches,
         "act_quant": quant,
         "decode_gemv": gemv,
+        "decode_nvfp4_gemv": gemv_fp4,
         "phase_linear": phase,
         "bf16_torch_tflops": None if bf16 is None else round(bf16, 2),
         "ratio_vs_bf16_torch": None if bf16 is None else round(value / bf16, 3),

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI in include/mq.h):
     mq_gemm_nvfp4_prefill(a: NVFP4, a_bf16, w: NVFP4, c, flags=0, stream=None)
     mq_gemm_nvfp4_prefill_grouped(a: NVFP4, a_bf16, ws: [NVFP4], cs: [tensor], flags=0, stream=None)
     mq_gemv_bf16_decode(x_bf16, w_bf16, y_bf16, flags=0, stream=None)
+    mq_gemv_nvfp4_decode(x: NVFP4, w: NVFP4, y_bf16, flags=0, stream=None)
     mq_linear_path / mq_linear_prepare / mq_linear_forward (through ``Linear``)
 
 and small conveniences built on them (``quantize``, ``prefill_linear``,
@@ -46,7 +47,7 @@ MQ_MAX_GROUP = 4
 REC_BYTES = 16 + 4 * MQ_AMAX_PARTS  # sizeof(mq_scale_rec) = 4096
 
 EXPORTS = ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemm_nvfp4_prefill_grouped",
-           "mq_gemv_bf16_decode", "mq_linear_path", "mq_linear_prepare", "mq_linear_forward",
+           "mq_gemv_bf16_decode", "mq_gemv_nvfp4_decode", "mq_linear_path", "mq_linear_prepare", "mq_linear_forward",
            "mq_status_str", "mq_last_error", "mq_version")
 
 
@@ -92,6 +93,8 @@ def lib():
     L.mq_gemm_nvfp4_prefill_grouped.restype = ctypes.c_int32
     L.mq_gemv_bf16_decode.argtypes = [vp, vp, vp, i64, i64, i64, u32, vp]
     L.mq_gemv_bf16_decode.restype = ctypes.c_int32
+    L.mq_gemv_nvfp4_decode.argtypes = [P, P, vp, i64, i64, i64, u32, vp]
+    L.mq_gemv_nvfp4_decode.restype = ctypes.c_int32
     LP = ctypes.POINTER(_LinearC)
     L.mq_linear_path.argtypes = [LP, i64, u32]
     L.mq_linear_path.restype = ctypes.c_int32
@@ -246,6 +249,20 @@ def mq_gemv_bf16_decode(x_bf16, w_bf16, y_bf16, flags: int = 0, stream=None):
         raise ValueError("shape mismatch")
     _check(lib().mq_gemv_bf16_decode(_dev_ptr(x_bf16, "x"), _dev_ptr(w_bf16, "w"), _dev_ptr(y_bf16, "y"),
                                      M, N, K, flags, _stream_ptr(stream)), "mq_gemv_bf16_decode")
+
+
+def mq_gemv_nvfp4_decode(x: NVFP4, w: NVFP4, y_bf16, flags: int = 0, stream=None):
+    """Y = X . W^T with both operands NVFP4, M <= 32 (the uniform-NVFP4 decode)."""
+    import torch
+    M, K = x.shape
+    N, Kw = w.shape
+    if Kw != K:
+        raise ValueError(f"K mismatch: X has {K}, W has {Kw}")
+    if y_bf16.dtype != torch.bfloat16 or tuple(y_bf16.shape) != (M, N):
+        raise ValueError(f"y must be bfloat16 [{M}][{N}]")
+    xc, wc = x._c(), w._c()
+    _check(lib().mq_gemv_nvfp4_decode(ctypes.byref(xc), ctypes.byref(wc), _dev_ptr(y_bf16, "y"), M, N, K, flags,
+                                      _stream_ptr(stream)), "mq_gemv_nvfp4_decode")
 
 
 class Linear:

@@ -183,6 +183,24 @@ mq_status mq_gemv_bf16_decode(const void* x_bf16, const void* w_bf16, void* y_bf
   return launched(mq::launch_gemv(x_bf16, w_bf16, y_bf16, M, N, K, dev, (hipStream_t)hip_stream), "gemv");
 }
 
+mq_status mq_gemv_nvfp4_decode(const mq_nvfp4* x, const mq_nvfp4* w, void* y_bf16, int64_t M, int64_t N,
+                               int64_t K, uint32_t flags, void* hip_stream) {
+  if (flags) return fail(MQ_ERR_INVALID, "unknown flags 0x%x", flags);
+  if (!x || !w || !y_bf16) return fail(MQ_ERR_INVALID, "x, w and y must not be NULL");
+  if (!x->codes || !x->scales || !x->rec || !w->codes || !w->scales || !w->rec)
+    return fail(MQ_ERR_INVALID, "x and w codes, scales and rec must not be NULL");
+  if (M < 1 || M > 32) return fail(MQ_ERR_SHAPE, "M=%lld must be in 1..32", (long long)M);
+  if (mq_status s = check_dims(N, K, "N", "K")) return s;
+  if (K % 16) return fail(MQ_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
+  if (!aligned(x->codes, 16) || !aligned(w->codes, 16) || !aligned(x->scales, 8) || !aligned(w->scales, 8) ||
+      !aligned(x->rec, 16) || !aligned(w->rec, 16) || !aligned(y_bf16, 2))
+    return fail(MQ_ERR_ALIGN, "codes need 16-byte, scales 8-byte, rec 16-byte, y 2-byte alignment");
+  mq::DeviceInfo dev;
+  if (mq_status s = current_device(dev)) return s;
+  const mq::GemvNvfp4Args a{x->codes, x->scales, x->rec, w->codes, w->scales, w->rec, y_bf16, M, N, K};
+  return launched(mq::launch_gemv_nvfp4(a, (hipStream_t)hip_stream), "gemv_nvfp4");
+}
+
 // ------------------------------------------------------- phase-aware linear --
 
 int32_t mq_linear_path(const mq_linear* L, int64_t M, uint32_t flags) {

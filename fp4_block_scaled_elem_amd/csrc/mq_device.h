@@ -208,4 +208,32 @@ __device__ __forceinline__ uint32_t e4m3_to_f16_bits(uint32_t s) {
   return (uint32_t)__builtin_bit_cast(uint16_t, v);
 }
 
+// 8 E2M1 codes (one dword) times the group scale -> 8 exact binary16 values.
+// The hardware conversion yields the E2M1 values themselves (its scale
+// operand only applies a power of two, so it is left at 1); one packed
+// binary16 multiply per pair applies the E4M3 group scale exactly.
+__device__ __forceinline__ half8_t dequant8(uint32_t codes, _Float16 sigma) {
+  const half2_t s = {sigma, sigma};
+  half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s;
+  half2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s;
+  half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s;
+  half2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s;
+  half8_t r;
+  r[0] = h0[0]; r[1] = h0[1]; r[2] = h1[0]; r[3] = h1[1];
+  r[4] = h2[0]; r[5] = h2[1]; r[6] = h3[0]; r[7] = h3[1];
+  return r;
+}
+
+// Two E4M3 scale bytes of a dword (bytes 0,1 or 2,3 by `sel`) as a binary16
+// pair, without branches: the bit pattern s<<7 read as binary16 is
+// value(s) * 2^-8 for every E4M3 byte, normal or subnormal (the formats share
+// their subnormal layout and differ by 8 in exponent bias), and one exact
+// packed multiply by 256 restores the value (binary16 subnormals are kept:
+// the kernels run with denormals enabled).
+__device__ __forceinline__ half2_t sigma_pair(uint32_t scale_dword, uint32_t sel) {
+  const uint32_t b = __builtin_amdgcn_perm(0u, scale_dword, sel);  // (s_lo << 8) | (s_hi << 24)
+  const u16x2_t h = __builtin_bit_cast(u16x2_t, b) >> (uint16_t)1;
+  return __builtin_bit_cast(half2_t, h) * half2_t{(_Float16)256.0f, (_Float16)256.0f};
+}
+
 }  // namespace mq

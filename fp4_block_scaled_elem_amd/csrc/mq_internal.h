@@ -42,4 +42,19 @@ hipError_t launch_gemm(const GemmOperandA& a, const GemmWeight* w, int ngroup, i
 hipError_t launch_gemv(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                        const DeviceInfo& dev, hipStream_t stream);
 
+// NVFP4 x NVFP4 decode GEMV operands: X [M][K] and W [N][K], output bf16
+// Y [M][N].
+struct GemvNvfp4Args {
+  const uint8_t* x_codes;
+  const uint8_t* x_scales;
+  const mq_scale_rec* x_rec;
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  const mq_scale_rec* w_rec;
+  void* y;
+  int64_t M, N, K;
+};
+
+hipError_t launch_gemv_nvfp4(const GemvNvfp4Args& a, hipStream_t stream);
+
 }  // namespace mq

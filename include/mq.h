@@ -17,6 +17,8 @@
  *                          the same for several weights that share A, in one
  *                          launch
  *   mq_gemv_bf16_decode    Y = X . W^T on bf16 X [M][K] and W [N][K]
+ *   mq_gemv_nvfp4_decode   the decode GEMV with X and W in NVFP4 (the
+ *                          uniform-quantization baseline the method avoids)
  *   mq_linear_prepare / mq_linear_forward / mq_linear_path
  *                          one weight kept in both formats (original BF16
  *                          and an NVFP4 copy), each call routed to the
@@ -195,6 +197,27 @@ mq_status mq_gemm_nvfp4_prefill_grouped(const mq_nvfp4* a, const void* a_bf16,
 mq_status mq_gemv_bf16_decode(const void* x_bf16, const void* w_bf16,
                               void* y_bf16, int64_t M, int64_t N, int64_t K,
                               uint32_t flags, void* hip_stream);
+
+/*
+ * mq_gemv_nvfp4_decode - Y[M][N] = X[M][K] . W[N][K]^T with X and W in
+ *   NVFP4: the decode step run the uniform way, in the prefill format, which
+ *   the method avoids because decode errors accumulate (gist.science
+ *   explainer, Technical Summary s.1 Problem Statement; s.4 Experimental
+ *   Results).  Kept to compare the two decode paths on bytes moved: W is
+ *   read at 0.5625 bytes per weight instead of 2.  Same arithmetic as
+ *   mq_gemm_nvfp4_prefill (exact g*sigma operands, binary32 accumulation,
+ *   times s_tX*s_tW, nearest-even bf16), summed in another order.
+ * x        HOST pointer to the quantized rows X [M][K] (e.g. from
+ *          mq_quantize_nvfp4 earlier on the same stream; rec->s_t set).
+ * w        HOST pointer to the quantized weights [N][K] (rec->s_t set).
+ * y_bf16   DEVICE bf16 [M][N].
+ * M        1..32.  N >= 1.  K >= 16, K % 16 == 0 (K % 256 == 0 is fastest).
+ *          codes 16-byte, scales 8-byte, rec 16-byte, y 2-byte aligned.
+ * flags    0.
+ */
+mq_status mq_gemv_nvfp4_decode(const mq_nvfp4* x, const mq_nvfp4* w, void* y_bf16,
+                               int64_t M, int64_t N, int64_t K,
+                               uint32_t flags, void* hip_stream);
 
 /*
  * Phase-aware linear layer.  The method keeps each weight matrix in two

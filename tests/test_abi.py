@@ -36,7 +36,8 @@ def L():
 def test_header_declares_the_entry_points():
     fns = _header_functions()
     for f in ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemm_nvfp4_prefill_grouped",
-              "mq_gemv_bf16_decode", "mq_linear_path", "mq_linear_prepare", "mq_linear_forward"):
+              "mq_gemv_bf16_decode", "mq_gemv_nvfp4_decode", "mq_linear_path", "mq_linear_prepare",
+              "mq_linear_forward"):
         assert f in fns
 
 
@@ -149,6 +150,24 @@ def test_gemv_argument_errors(L):
     assert f(P16, P16, P1, 1, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
 
 
+def test_gemv_nvfp4_argument_errors(L):
+    f = L.mq_gemv_nvfp4_decode
+    q = _q(P16, P16, P16)
+    assert f(None, q, P16, 1, 4, 16, 0, None) == mq.MQ_ERR_INVALID
+    assert f(q, None, P16, 1, 4, 16, 0, None) == mq.MQ_ERR_INVALID
+    assert f(q, q, None, 1, 4, 16, 0, None) == mq.MQ_ERR_INVALID
+    assert f(q, _q(P16, None, P16), P16, 1, 4, 16, 0, None) == mq.MQ_ERR_INVALID
+    assert f(q, q, P16, 1, 4, 16, 1, None) == mq.MQ_ERR_INVALID
+    assert f(q, q, P16, 0, 4, 16, 0, None) == mq.MQ_ERR_SHAPE
+    assert f(q, q, P16, 33, 4, 16, 0, None) == mq.MQ_ERR_SHAPE
+    assert f(q, q, P16, 1, 4, 24, 0, None) == mq.MQ_ERR_SHAPE
+    assert f(q, q, P16, 1, 0, 16, 0, None) == mq.MQ_ERR_SHAPE
+    assert f(_q(P8, P16, P16), q, P16, 1, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
+    assert f(q, _q(P16, P1, P16), P16, 1, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
+    assert f(q, _q(P16, P16, P8), P16, 1, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
+    assert f(q, q, P1, 1, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
+
+
 def _lin(w=P16, codes=P16, scales=P16, rec=P16, N=4, K=16, pmin=33):
     return ctypes.byref(mq._LinearC(w, mq._NVFP4C(codes, scales, rec), N, K, pmin))
 
@@ -222,6 +241,8 @@ def test_valid_arguments_without_a_gpu_report_device_error(L):
     assert L.mq_gemv_bf16_decode(P16, P16, P16, 1, 4, 16, 0, None) == mq.MQ_ERR_DEVICE
     w = (P16, P16, P16)
     assert _grouped(L, _q(P16, P16, P16), None, [w, w, w], [P16, P16, P16], [4, 8, 12]) == mq.MQ_ERR_DEVICE
+    assert L.mq_gemv_nvfp4_decode(_q(P16, P16, P16), _q(P16, P16, P16), P16, 1, 4, 16, 0,
+                                  None) == mq.MQ_ERR_DEVICE
     assert L.mq_linear_prepare(_lin(), None) == mq.MQ_ERR_DEVICE
     assert L.mq_linear_forward(_lin(), P16, 1, None, P1 + 1, 0, None) == mq.MQ_ERR_DEVICE
     assert L.mq_linear_forward(_lin(), P16, 64, _q(P16, P16, P16), P16, 0, None) == mq.MQ_ERR_DEVICE
