@@ -58,3 +58,8 @@ from .linear import (  # noqa: F401
     gemv_bf16_ref,
     round_f64_to_bf16,
 )
+from .producer import (  # noqa: F401
+    rmsnorm_ref,
+    silu_ref,
+    swiglu_ref,
+)
