@@ -280,6 +280,44 @@ def decode_nvfp4_rates(bf16_rates=None, reps=50):
     return res
 
 
+def producer_fused_rates(reps=50):
+    """Activation quantization with the amax pass folded into the op that
+    writes the activation: RMSNorm at the q/k/v and gate/up inputs' shape
+    (4096 x 4096) and the SwiGLU gate at the down input's (4096 x 14336).
+    For each: the producer with its partial maxima (GB/s over its bytes: 2
+    read + 2 written per element for RMSNorm, 4 + 2 for SwiGLU), then the
+    quantization of its output by the two-pass quantizer and by the encode
+    pass alone from the producer's partials (bit-identical results).  Inputs
+    rotate over copies past the Infinity Cache."""
+    import torch
+    import fp4_block_scaled_elem_amd as mq
+    res = {}
+    gen = torch.Generator(device="cuda").manual_seed(3000)
+    for name, rows, cols in (("rmsnorm_4096x4096", 4096, 4096), ("swiglu_4096x14336", 4096, 14336)):
+        swiglu = name.startswith("swiglu")
+        per = (2 if swiglu else 1) * rows * cols * 2
+        ncopy = max(2, -(-600 * 2 ** 20 // per))
+        ins = [torch.randn((rows, cols), generator=gen, device="cuda").to(torch.bfloat16)
+               for _ in range(ncopy * (2 if swiglu else 1))]
+        g = torch.randn((cols,), generator=gen, device="cuda").to(torch.bfloat16)
+        y = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+        q = mq.NVFP4.empty(rows, cols)
+        if swiglu:
+            prod = lambda r: mq.mq_swiglu_amax(ins[2 * (r % ncopy)], ins[2 * (r % ncopy) + 1], y, q)
+        else:
+            prod = lambda r: mq.mq_rmsnorm_amax(ins[r % ncopy], g, y, q)
+        tp, _ = _median_us(prod, reps=reps)
+        t2, _ = _median_us(lambda r: mq.mq_quantize_nvfp4(y, q), reps=reps)
+        prod(0)
+        t1, _ = _median_us(lambda r: mq.mq_quantize_nvfp4(y, q, mq.MQ_SCALE_PARTIALS), reps=reps)
+        nbytes = rows * cols * (6 if swiglu else 4)
+        res[name] = {"producer_us": round(tp, 2), "producer_GBps": round(nbytes / tp / 1e3, 1),
+                     "quant_two_pass_us": round(t2, 2), "quant_from_partials_us": round(t1, 2),
+                     "saved_us": round(t2 - t1, 2)}
+        del ins
+    return res
+
+
 def phase_linear_rates(reps=50):
     """The phase-aware linear (mq_linear_forward) on the 8B q projection's
     weight (4096 x 4096, both formats resident): a decode step at M = 1 and
@@ -443,6 +481,7 @@ def main():
     gemv = None if args.no_extras else decode_gemv_rates()
     gemv_fp4 = None if args.no_extras else decode_nvfp4_rates(gemv)
     phase = None if args.no_extras else phase_linear_rates()
+    producer = None if (args.no_extras or cfg.fused_act_quant) else producer_fused_rates()
     bf16 = None if args.no_bf16 else bf16_reference(cfg, acts, wdev)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.config, acts_host, args.cpu_rows, args.cpu_wrows)
 
@@ -476,6 +515,7 @@ def main():
         "decode_gemv": gemv,
         "decode_nvfp4_gemv": gemv_fp4,
         "phase_linear": phase,
+        "producer_fused_act_quant": producer,
         "bf16_torch_tflops": None if bf16 is None else round(bf16, 2),
         "ratio_vs_bf16_torch": None if bf16 is None else round(value / bf16, 3),
         "cpu_baseline": cpu,

@@ -12,6 +12,8 @@ Entry points (same names as the C ABI in include/mq.h):
     mq_gemm_nvfp4_prefill_grouped(a: NVFP4, a_bf16, ws: [NVFP4], cs: [tensor], flags=0, stream=None)
     mq_gemv_bf16_decode(x_bf16, w_bf16, y_bf16, flags=0, stream=None)
     mq_gemv_nvfp4_decode(x: NVFP4, w: NVFP4, y_bf16, flags=0, stream=None)
+    mq_rmsnorm_amax(x_bf16, gamma_bf16, y_bf16, rec, eps=1e-5, flags=0, stream=None)
+    mq_swiglu_amax(a_bf16, b_bf16, y_bf16, rec, flags=0, stream=None)
     mq_linear_path / mq_linear_prepare / mq_linear_forward (through ``Linear``)
 
 and small conveniences built on them (``quantize``, ``prefill_linear``,
@@ -40,6 +42,7 @@ MQ_OUT_F32 = 2
 MQ_A_FUSED_BF16 = 4
 MQ_PHASE_PREFILL = 8
 MQ_PHASE_DECODE = 16
+MQ_SCALE_PARTIALS = 32
 MQ_PATH_DECODE_BF16 = 1
 MQ_PATH_PREFILL_NVFP4 = 2
 MQ_AMAX_PARTS = 1020
@@ -47,7 +50,7 @@ MQ_MAX_GROUP = 4
 REC_BYTES = 16 + 4 * MQ_AMAX_PARTS  # sizeof(mq_scale_rec) = 4096
 
 EXPORTS = ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemm_nvfp4_prefill_grouped",
-           "mq_gemv_bf16_decode", "mq_gemv_nvfp4_decode", "mq_linear_path", "mq_linear_prepare", "mq_linear_forward",
+           "mq_gemv_bf16_decode", "mq_gemv_nvfp4_decode", "mq_rmsnorm_amax", "mq_swiglu_amax", "mq_linear_path", "mq_linear_prepare", "mq_linear_forward",
            "mq_status_str", "mq_last_error", "mq_version")
 
 
@@ -95,6 +98,10 @@ def lib():
     L.mq_gemv_bf16_decode.restype = ctypes.c_int32
     L.mq_gemv_nvfp4_decode.argtypes = [P, P, vp, i64, i64, i64, u32, vp]
     L.mq_gemv_nvfp4_decode.restype = ctypes.c_int32
+    L.mq_rmsnorm_amax.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_float, u32, vp]
+    L.mq_rmsnorm_amax.restype = ctypes.c_int32
+    L.mq_swiglu_amax.argtypes = [vp, vp, vp, vp, i64, i64, u32, vp]
+    L.mq_swiglu_amax.restype = ctypes.c_int32
     LP = ctypes.POINTER(_LinearC)
     L.mq_linear_path.argtypes = [LP, i64, u32]
     L.mq_linear_path.restype = ctypes.c_int32
@@ -263,6 +270,38 @@ def mq_gemv_nvfp4_decode(x: NVFP4, w: NVFP4, y_bf16, flags: int = 0, stream=None
     xc, wc = x._c(), w._c()
     _check(lib().mq_gemv_nvfp4_decode(ctypes.byref(xc), ctypes.byref(wc), _dev_ptr(y_bf16, "y"), M, N, K, flags,
                                       _stream_ptr(stream)), "mq_gemv_nvfp4_decode")
+
+
+def _rec_ptr(rec):
+    """An NVFP4's rec, or a rec tensor itself (REC_BYTES of device memory)."""
+    t = rec.rec if isinstance(rec, NVFP4) else rec
+    if t.numel() * t.element_size() != REC_BYTES:
+        raise ValueError(f"rec must hold {REC_BYTES} bytes")
+    return _dev_ptr(t, "rec")
+
+
+def mq_rmsnorm_amax(x_bf16, gamma_bf16, y_bf16, rec, eps: float = 1e-5, flags: int = 0, stream=None):
+    """y = RMSNorm(x) * gamma in bf16, and y's partial maxima into rec
+    (quantize y afterwards with MQ_SCALE_PARTIALS)."""
+    import torch
+    if x_bf16.dtype != torch.bfloat16 or x_bf16.dim() != 2 or y_bf16.shape != x_bf16.shape \
+            or y_bf16.dtype != torch.bfloat16 or gamma_bf16.dtype != torch.bfloat16 \
+            or tuple(gamma_bf16.shape) != (x_bf16.shape[1],):
+        raise ValueError("x, y bfloat16 [rows][cols] and gamma bfloat16 [cols]")
+    rows, cols = x_bf16.shape
+    _check(lib().mq_rmsnorm_amax(_dev_ptr(x_bf16, "x"), _dev_ptr(gamma_bf16, "gamma"), _dev_ptr(y_bf16, "y"),
+                                 _rec_ptr(rec), rows, cols, eps, flags, _stream_ptr(stream)), "mq_rmsnorm_amax")
+
+
+def mq_swiglu_amax(a_bf16, b_bf16, y_bf16, rec, flags: int = 0, stream=None):
+    """y = silu(a) * b in bf16, and y's partial maxima into rec."""
+    import torch
+    for t, n in ((a_bf16, "a"), (b_bf16, "b"), (y_bf16, "y")):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or t.shape != a_bf16.shape:
+            raise ValueError(f"{n} must be bfloat16 with a's 2-D shape")
+    rows, cols = a_bf16.shape
+    _check(lib().mq_swiglu_amax(_dev_ptr(a_bf16, "a"), _dev_ptr(b_bf16, "b"), _dev_ptr(y_bf16, "y"),
+                                _rec_ptr(rec), rows, cols, flags, _stream_ptr(stream)), "mq_swiglu_amax")
 
 
 class Linear:

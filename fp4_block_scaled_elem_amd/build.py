@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmq.so")
-SOURCES = ("api.hip", "quant.hip", "gemm.hip", "gemv.hip", "gemv_nvfp4.hip")
+SOURCES = ("api.hip", "quant.hip", "gemm.hip", "gemv.hip", "gemv_nvfp4.hip", "producer.hip")
 ARCH = "gfx950"
 
 FLAGS = [

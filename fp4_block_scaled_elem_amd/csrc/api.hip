@@ -97,7 +97,9 @@ mq_status mq_quantize_nvfp4(const void* x_bf16, int64_t rows, int64_t cols, cons
                             uint32_t flags, void* hip_stream) {
   if (!x_bf16 || !out) return fail(MQ_ERR_INVALID, "x_bf16 and out must not be NULL");
   if (!out->codes || !out->scales || !out->rec) return fail(MQ_ERR_INVALID, "out->codes, scales and rec must not be NULL");
-  if (flags & ~MQ_SCALE_GIVEN) return fail(MQ_ERR_INVALID, "unknown flags 0x%x", flags);
+  if (flags & ~(MQ_SCALE_GIVEN | MQ_SCALE_PARTIALS)) return fail(MQ_ERR_INVALID, "unknown flags 0x%x", flags);
+  if ((flags & MQ_SCALE_GIVEN) && (flags & MQ_SCALE_PARTIALS))
+    return fail(MQ_ERR_INVALID, "MQ_SCALE_GIVEN and MQ_SCALE_PARTIALS are exclusive");
   if (mq_status s = check_dims(rows, cols, "rows", "cols")) return s;
   if (cols % 16) return fail(MQ_ERR_SHAPE, "cols=%lld is not a multiple of 16", (long long)cols);
   if (!aligned(x_bf16, 16) || !aligned(out->codes, 16) || !aligned(out->scales, 8) || !aligned(out->rec, 16))
@@ -106,7 +108,7 @@ mq_status mq_quantize_nvfp4(const void* x_bf16, int64_t rows, int64_t cols, cons
   if (mq_status s = current_device(dev)) return s;
   hipStream_t st = (hipStream_t)hip_stream;
   const bool given = flags & MQ_SCALE_GIVEN;
-  if (!given) {
+  if (!given && !(flags & MQ_SCALE_PARTIALS)) {
     hipError_t e = mq::launch_amax(x_bf16, rows * cols, out->rec, dev, st);
     if (e != hipSuccess) return launched(e, "amax");
   }
@@ -117,10 +119,13 @@ mq_status mq_quantize_nvfp4(const void* x_bf16, int64_t rows, int64_t cols, cons
 mq_status mq_gemm_nvfp4_prefill_grouped(const mq_nvfp4* a, const void* a_bf16, int32_t n_group,
                                         const mq_nvfp4* w, void* const* c, const int64_t* N, int64_t M,
                                         int64_t K, uint32_t flags, void* hip_stream) {
-  const uint32_t known = MQ_OUT_F32 | MQ_A_FUSED_BF16 | MQ_SCALE_GIVEN;
+  const uint32_t known = MQ_OUT_F32 | MQ_A_FUSED_BF16 | MQ_SCALE_GIVEN | MQ_SCALE_PARTIALS;
   if (flags & ~known) return fail(MQ_ERR_INVALID, "unknown flags 0x%x", flags);
   const bool fused = flags & MQ_A_FUSED_BF16;
-  if ((flags & MQ_SCALE_GIVEN) && !fused) return fail(MQ_ERR_INVALID, "MQ_SCALE_GIVEN needs MQ_A_FUSED_BF16");
+  if ((flags & (MQ_SCALE_GIVEN | MQ_SCALE_PARTIALS)) && !fused)
+    return fail(MQ_ERR_INVALID, "MQ_SCALE_GIVEN and MQ_SCALE_PARTIALS need MQ_A_FUSED_BF16");
+  if ((flags & MQ_SCALE_GIVEN) && (flags & MQ_SCALE_PARTIALS))
+    return fail(MQ_ERR_INVALID, "MQ_SCALE_GIVEN and MQ_SCALE_PARTIALS are exclusive");
   if (n_group < 1 || n_group > MQ_MAX_GROUP)
     return fail(MQ_ERR_INVALID, "n_group=%d must be in 1..%d", (int)n_group, MQ_MAX_GROUP);
   if (!a || !w || !c || !N) return fail(MQ_ERR_INVALID, "a, w, c and N must not be NULL");
@@ -154,7 +159,7 @@ mq_status mq_gemm_nvfp4_prefill_grouped(const mq_nvfp4* a, const void* a_bf16, i
   if (mq_status s = current_device(dev)) return s;
   hipStream_t st = (hipStream_t)hip_stream;
   const bool given = flags & MQ_SCALE_GIVEN;
-  if (fused && !given) {
+  if (fused && !given && !(flags & MQ_SCALE_PARTIALS)) {
     hipError_t e = mq::launch_amax(a_bf16, M * K, a->rec, dev, st);
     if (e != hipSuccess) return launched(e, "amax");
   }
@@ -201,6 +206,38 @@ mq_status mq_gemv_nvfp4_decode(const mq_nvfp4* x, const mq_nvfp4* w, void* y_bf1
   return launched(mq::launch_gemv_nvfp4(a, (hipStream_t)hip_stream), "gemv_nvfp4");
 }
 
+mq_status mq_rmsnorm_amax(const void* x_bf16, const void* gamma_bf16, void* y_bf16, mq_scale_rec* rec,
+                          int64_t rows, int64_t cols, float eps, uint32_t flags, void* hip_stream) {
+  if (flags) return fail(MQ_ERR_INVALID, "unknown flags 0x%x", flags);
+  if (!x_bf16 || !gamma_bf16 || !y_bf16 || !rec) return fail(MQ_ERR_INVALID, "x, gamma, y and rec must not be NULL");
+  if (mq_status s = check_dims(rows, cols, "rows", "cols")) return s;
+  if (cols % 16) return fail(MQ_ERR_SHAPE, "cols=%lld is not a multiple of 16", (long long)cols);
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(MQ_ERR_INVALID, "eps must be finite and >= 0");
+  if (!aligned(x_bf16, 16) || !aligned(gamma_bf16, 16) || !aligned(y_bf16, 16) || !aligned(rec, 16))
+    return fail(MQ_ERR_ALIGN, "x, gamma, y and rec need 16-byte alignment");
+  if (x_bf16 == y_bf16) return fail(MQ_ERR_INVALID, "y must not alias x");
+  mq::DeviceInfo dev;
+  if (mq_status s = current_device(dev)) return s;
+  return launched(mq::launch_rmsnorm_amax(x_bf16, gamma_bf16, y_bf16, rows, cols, eps, rec, dev,
+                                          (hipStream_t)hip_stream),
+                  "rmsnorm_amax");
+}
+
+mq_status mq_swiglu_amax(const void* a_bf16, const void* b_bf16, void* y_bf16, mq_scale_rec* rec, int64_t rows,
+                         int64_t cols, uint32_t flags, void* hip_stream) {
+  if (flags) return fail(MQ_ERR_INVALID, "unknown flags 0x%x", flags);
+  if (!a_bf16 || !b_bf16 || !y_bf16 || !rec) return fail(MQ_ERR_INVALID, "a, b, y and rec must not be NULL");
+  if (mq_status s = check_dims(rows, cols, "rows", "cols")) return s;
+  if (cols % 16) return fail(MQ_ERR_SHAPE, "cols=%lld is not a multiple of 16", (long long)cols);
+  if (!aligned(a_bf16, 16) || !aligned(b_bf16, 16) || !aligned(y_bf16, 16) || !aligned(rec, 16))
+    return fail(MQ_ERR_ALIGN, "a, b, y and rec need 16-byte alignment");
+  if (y_bf16 == a_bf16 || y_bf16 == b_bf16) return fail(MQ_ERR_INVALID, "y must not alias a or b");
+  mq::DeviceInfo dev;
+  if (mq_status s = current_device(dev)) return s;
+  return launched(mq::launch_swiglu_amax(a_bf16, b_bf16, y_bf16, rows * cols, rec, dev, (hipStream_t)hip_stream),
+                  "swiglu_amax");
+}
+
 // ------------------------------------------------------- phase-aware linear --
 
 int32_t mq_linear_path(const mq_linear* L, int64_t M, uint32_t flags) {
@@ -241,7 +278,7 @@ mq_status mq_linear_prepare(const mq_linear* L, void* hip_stream) {
 
 mq_status mq_linear_forward(const mq_linear* L, const void* x_bf16, int64_t M, const mq_nvfp4* a_work,
                             void* y_bf16, uint32_t flags, void* hip_stream) {
-  const uint32_t known = MQ_PHASE_PREFILL | MQ_PHASE_DECODE | MQ_A_FUSED_BF16;
+  const uint32_t known = MQ_PHASE_PREFILL | MQ_PHASE_DECODE | MQ_A_FUSED_BF16 | MQ_SCALE_PARTIALS;
   if (flags & ~known) return fail(MQ_ERR_INVALID, "unknown flags 0x%x", flags);
   if ((flags & MQ_PHASE_PREFILL) && (flags & MQ_PHASE_DECODE))
     return fail(MQ_ERR_INVALID, "MQ_PHASE_PREFILL and MQ_PHASE_DECODE are exclusive");
@@ -267,9 +304,11 @@ mq_status mq_linear_forward(const mq_linear* L, const void* x_bf16, int64_t M, c
   if (!aligned(y_bf16, 16)) return fail(MQ_ERR_ALIGN, "y needs 16-byte alignment on the prefill path");
   if (M * L->K > ((int64_t)1 << 40) || M * L->N > ((int64_t)1 << 40))
     return fail(MQ_ERR_SHAPE, "M=%lld exceeds the supported size", (long long)M);
+  const uint32_t scale = flags & MQ_SCALE_PARTIALS;
   if (fused)
-    return mq_gemm_nvfp4_prefill(a_work, x_bf16, &L->w_nvfp4, y_bf16, M, L->N, L->K, MQ_A_FUSED_BF16, hip_stream);
-  if (mq_status s = mq_quantize_nvfp4(x_bf16, M, L->K, a_work, MQ_SCALE_DYNAMIC, hip_stream)) return s;
+    return mq_gemm_nvfp4_prefill(a_work, x_bf16, &L->w_nvfp4, y_bf16, M, L->N, L->K, MQ_A_FUSED_BF16 | scale,
+                                 hip_stream);
+  if (mq_status s = mq_quantize_nvfp4(x_bf16, M, L->K, a_work, scale, hip_stream)) return s;
   return mq_gemm_nvfp4_prefill(a_work, nullptr, &L->w_nvfp4, y_bf16, M, L->N, L->K, 0, hip_stream);
 }
 

@@ -57,4 +57,9 @@ struct GemvNvfp4Args {
 
 hipError_t launch_gemv_nvfp4(const GemvNvfp4Args& a, hipStream_t stream);
 
+hipError_t launch_rmsnorm_amax(const void* x, const void* g, void* y, int64_t rows, int64_t cols, float eps,
+                               mq_scale_rec* rec, const DeviceInfo& dev, hipStream_t stream);
+hipError_t launch_swiglu_amax(const void* a, const void* b, void* y, int64_t n, mq_scale_rec* rec,
+                              const DeviceInfo& dev, hipStream_t stream);
+
 }  // namespace mq

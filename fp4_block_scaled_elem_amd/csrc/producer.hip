@@ -1,0 +1,194 @@
+// producer.hip - the ops that write the prefill linears' activations, with
+// the activation quantizer's amax pass folded into them (gfx950).
+//
+// NVFP4's tensor-level scale of an activation comes from the absolute
+// maximum of the whole tensor, taken at run time (gist.science English
+// explainer of "Mix-Quant: Quantized Prefilling, Precise Decoding for
+// Agentic LLMs", Technical Summary s.2 Hybrid Precision Strategy), which
+// costs the quantizer one full read of the activation before it can encode.
+// The op that writes the activation can take that maximum on the way out:
+// each workgroup stores one partial maximum of the bf16 values it wrote,
+// in the layout of the amax pass's record (binary32 bits of a bf16
+// magnitude per workgroup, their count in nparts), and the encode pass then
+// runs alone (MQ_SCALE_PARTIALS).  The two ops of an 8B-shaped layer that
+// produce the linears' inputs:
+//   rmsnorm_amax_kernel  y = bf16((x * rstd) * g), rstd = 1 / sqrt(mean(x^2)
+//                        + eps) per row, a wave per row (grid-stride);
+//   swiglu_amax_kernel   y = bf16(silu(a) * b), silu(a) = a / (1 + exp(-a)),
+//                        elementwise, 16-byte loads.
+// Both are HBM-bound: 2 bytes read and 2 written per element (RMSNorm),
+// 4 read and 2 written (SwiGLU).  Their outputs are rounded binary32 results, not bit-identical
+// to any other order of evaluation; the maxima they emit are those of the
+// exact bf16 values they store.
+#include "mq_device.h"
+#include "mq_internal.h"
+
+namespace mq {
+
+constexpr int kPThreads = 256;
+
+template <int NT>
+__device__ __forceinline__ uint32_t block_max_bits(uint32_t v, uint32_t* sh) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t o = __shfl_xor(v, off, 64);
+    v = v > o ? v : o;
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) r = r > sh[i] ? r : sh[i];
+  return r;
+}
+
+// nearest-even bf16 bits of a finite binary32
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// One wave per row (a workgroup's eight waves take eight rows at a time,
+// grid-stride over rows; eight so that 4096 rows fit in one round of the
+// workgroups the record has partial slots for), no block barriers in the
+// loop.  A row of up to
+// 64 * 8 * kRowPieces elements stays in registers between the sum of squares
+// and the output; longer rows are read twice (the second time from L2).
+// 8 elements per 16-byte piece, cols % 16 == 0.
+constexpr int kRowPieces = 8;  // pieces per lane held in registers: rows up to 4096 elements
+constexpr int kRThreads = 512;  // eight waves per workgroup
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint4 rms_piece(uint4 v, uint4 gv, float rstd, uint32_t& am) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = bf16_bits_rne((bf16_lo(w[j]) * rstd) * bf16_lo(gw[j]));
+    const uint32_t hi = bf16_bits_rne((bf16_hi(w[j]) * rstd) * bf16_hi(gw[j]));
+    o[j] = lo | (hi << 16);
+    const uint32_t m = bf16x2_absmax_bits(o[j]);
+    am = am > m ? am : m;
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ float sumsq_piece(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+    ss += lo * lo;
+    ss += hi * hi;
+  }
+  return ss;
+}
+
+__global__ __launch_bounds__(kRThreads) void rmsnorm_amax_kernel(const uint4* __restrict__ x,
+                                                                 const uint4* __restrict__ g,
+                                                                 uint4* __restrict__ y, int64_t rows, int cols,
+                                                                 float eps, mq_scale_rec* __restrict__ rec) {
+  __shared__ uint32_t shm[kRThreads / 64];
+  constexpr int kWaves = kRThreads / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int pieces = cols / 8;
+  const float inv_cols = 1.0f / (float)cols;
+  uint32_t am = 0;  // max bf16 magnitude bits written by this lane
+  for (int64_t r = (int64_t)blockIdx.x * kWaves + wave; r < rows; r += (int64_t)gridDim.x * kWaves) {
+    const uint4* xr = x + r * pieces;
+    uint4* yr = y + r * pieces;
+    if (pieces <= 64 * kRowPieces) {
+      uint4 v[kRowPieces];
+      float ss = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kRowPieces; ++k) {
+        const int p = lane + 64 * k;
+        v[k] = p < pieces ? ld_stream(&xr[p]) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < kRowPieces; ++k) ss += sumsq_piece(v[k]);
+      const float rstd = 1.0f / sqrtf(wave_sum_f32(ss) * inv_cols + eps);
+#pragma unroll
+      for (int k = 0; k < kRowPieces; ++k) {
+        const int p = lane + 64 * k;
+        if (p < pieces) yr[p] = rms_piece(v[k], g[p], rstd, am);
+      }
+    } else {
+      float ss = 0.0f;
+      for (int p = lane; p < pieces; p += 64) ss += sumsq_piece(xr[p]);
+      const float rstd = 1.0f / sqrtf(wave_sum_f32(ss) * inv_cols + eps);
+      for (int p = lane; p < pieces; p += 64) yr[p] = rms_piece(xr[p], g[p], rstd, am);
+    }
+  }
+  const uint32_t m = block_max_bits<kRThreads>(am, shm);
+  if (threadIdx.x == 0) {
+    rec->part[blockIdx.x] = m << 16;
+    if (blockIdx.x == 0) rec->nparts = gridDim.x;
+  }
+}
+
+// Elementwise over n8 pieces of 8 elements, grid-stride.
+__global__ __launch_bounds__(kPThreads) void swiglu_amax_kernel(const uint4* __restrict__ a,
+                                                                const uint4* __restrict__ b,
+                                                                uint4* __restrict__ y, int64_t n8,
+                                                                mq_scale_rec* __restrict__ rec) {
+  __shared__ uint32_t shm[kPThreads / 64];
+  uint32_t am = 0;
+  const int64_t stride = (int64_t)gridDim.x * kPThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kPThreads + threadIdx.x; i < n8; i += stride) {
+    const uint4 va = ld_stream(&a[i]), vb = ld_stream(&b[i]);
+    const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a0 = bf16_lo(wa[j]), a1 = bf16_hi(wa[j]);
+      // silu(a) = a * (1 / (1 + exp(-a))); exp(-a) = inf for very negative a
+      // gives a * 0 = -0
+      const float s0 = a0 * __builtin_amdgcn_rcpf(1.0f + __expf(-a0));
+      const float s1 = a1 * __builtin_amdgcn_rcpf(1.0f + __expf(-a1));
+      const uint32_t lo = bf16_bits_rne(s0 * bf16_lo(wb[j]));
+      const uint32_t hi = bf16_bits_rne(s1 * bf16_hi(wb[j]));
+      o[j] = lo | (hi << 16);
+      const uint32_t m = bf16x2_absmax_bits(o[j]);
+      am = am > m ? am : m;
+    }
+    y[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  const uint32_t m = block_max_bits<kPThreads>(am, shm);
+  if (threadIdx.x == 0) {
+    rec->part[blockIdx.x] = m << 16;
+    if (blockIdx.x == 0) rec->nparts = gridDim.x;
+  }
+}
+
+hipError_t launch_rmsnorm_amax(const void* x, const void* g, void* y, int64_t rows, int64_t cols, float eps,
+                               mq_scale_rec* rec, const DeviceInfo& dev, hipStream_t stream) {
+  const int64_t row_groups = (rows + kRThreads / 64 - 1) / (kRThreads / 64);  // eight rows per workgroup
+  int64_t blocks = row_groups < 2 * (int64_t)dev.num_cu ? row_groups : 2 * (int64_t)dev.num_cu;
+  if (blocks > MQ_AMAX_PARTS) blocks = MQ_AMAX_PARTS;
+  hipLaunchKernelGGL(rmsnorm_amax_kernel, dim3((unsigned)blocks), dim3(kRThreads), 0, stream, (const uint4*)x,
+                     (const uint4*)g, (uint4*)y, rows, (int)cols, eps, rec);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_amax(const void* a, const void* b, void* y, int64_t n, mq_scale_rec* rec,
+                              const DeviceInfo& dev, hipStream_t stream) {
+  const int64_t n8 = n / 8;
+  int64_t blocks = (n8 + 4 * kPThreads - 1) / (4 * kPThreads);
+  if (blocks > 2 * (int64_t)dev.num_cu) blocks = 2 * (int64_t)dev.num_cu;
+  if (blocks > MQ_AMAX_PARTS) blocks = MQ_AMAX_PARTS;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(swiglu_amax_kernel, dim3((unsigned)blocks), dim3(kPThreads), 0, stream, (const uint4*)a,
+                     (const uint4*)b, (uint4*)y, n8, rec);
+  return hipGetLastError();
+}
+
+}  // namespace mq

@@ -17,6 +17,9 @@
  *                          the same for several weights that share A, in one
  *                          launch
  *   mq_gemv_bf16_decode    Y = X . W^T on bf16 X [M][K] and W [N][K]
+ *   mq_rmsnorm_amax / mq_swiglu_amax
+ *                          the ops that write the linears' activations,
+ *                          emitting the amax pass's partial maxima
  *   mq_gemv_nvfp4_decode   the decode GEMV with X and W in NVFP4 (the
  *                          uniform-quantization baseline the method avoids)
  *   mq_linear_prepare / mq_linear_forward / mq_linear_path
@@ -112,6 +115,9 @@ typedef struct mq_nvfp4 {
 #define MQ_A_FUSED_BF16  4u  /* GEMM: A given as bf16, quantized in-kernel      */
 #define MQ_PHASE_PREFILL 8u  /* linear: this call is a prefill (NVFP4 path)     */
 #define MQ_PHASE_DECODE 16u  /* linear: this call is a decode step (BF16 path)  */
+#define MQ_SCALE_PARTIALS 32u /* rec already holds the input's partial maxima,
+                                 written by mq_rmsnorm_amax / mq_swiglu_amax
+                                 earlier on the same stream: no amax pass    */
 
 /*
  * mq_quantize_nvfp4 - quantize a bf16 matrix to NVFP4.
@@ -124,7 +130,9 @@ typedef struct mq_nvfp4 {
  * out      HOST pointer to an mq_nvfp4 whose codes/scales/rec are written.
  *          out->rec->s_t, amax_bits, nparts and part[] are overwritten
  *          (with MQ_SCALE_GIVEN only out->rec->s_t is read).
- * flags    MQ_SCALE_DYNAMIC or MQ_SCALE_GIVEN.
+ * flags    MQ_SCALE_DYNAMIC, MQ_SCALE_GIVEN or MQ_SCALE_PARTIALS (out->rec's
+ *          nparts and part[] already hold x's partial maxima from a producer
+ *          op: s_t is derived from them, bit-identical to the dynamic case).
  * Launches: an amax pass (dynamic only), then the quantizer.
  */
 mq_status mq_quantize_nvfp4(const void* x_bf16, int64_t rows, int64_t cols,
@@ -151,7 +159,8 @@ mq_status mq_quantize_nvfp4(const void* x_bf16, int64_t rows, int64_t cols,
  * c        DEVICE output [M][N], bf16 (16-byte aligned) or binary32.
  * M, N     >= 1.  K >= 16, K % 16 == 0.
  * flags    MQ_OUT_BF16 | MQ_OUT_F32, optionally | MQ_A_FUSED_BF16, and with
- *          it optionally | MQ_SCALE_GIVEN.
+ *          it optionally | MQ_SCALE_GIVEN or | MQ_SCALE_PARTIALS (a->rec
+ *          holds a_bf16's partial maxima: no amax pass).
  */
 mq_status mq_gemm_nvfp4_prefill(const mq_nvfp4* a, const void* a_bf16,
                                 const mq_nvfp4* w, void* c,
@@ -197,6 +206,43 @@ mq_status mq_gemm_nvfp4_prefill_grouped(const mq_nvfp4* a, const void* a_bf16,
 mq_status mq_gemv_bf16_decode(const void* x_bf16, const void* w_bf16,
                               void* y_bf16, int64_t M, int64_t N, int64_t K,
                               uint32_t flags, void* hip_stream);
+
+/*
+ * Producer ops with the amax pass folded in.  NVFP4's tensor scale of an
+ * activation is taken from the absolute maximum of the whole tensor at run
+ * time (gist.science explainer, Technical Summary s.2 Hybrid Precision
+ * Strategy), which costs the quantizer a full read of the activation before
+ * it can encode.  These two ops write the activations of an 8B-shaped
+ * layer's prefill linears and, on the way out, one partial maximum of the
+ * bf16 values stored per workgroup into rec (the layout the amax pass
+ * writes: nparts, part[]); quantizing their output with MQ_SCALE_PARTIALS
+ * then skips the amax pass and gives exactly the codes, scales and s_t of
+ * the dynamic quantization of that output.  Outputs are bf16, rounded to
+ * nearest-even from binary32 arithmetic.
+ *
+ * mq_rmsnorm_amax - y[r][c] = bf16(x[r][c] * rstd_r * g[c]),
+ *   rstd_r = 1/sqrt(mean_c x[r][c]^2 + eps).
+ * x_bf16, y_bf16  DEVICE bf16 [rows][cols], 16-byte aligned (y may not alias x).
+ * gamma_bf16      DEVICE bf16 [cols], 16-byte aligned.
+ * rec             DEVICE mq_scale_rec, 16-byte aligned; nparts and part[]
+ *                 are overwritten (s_t and amax_bits are not touched).
+ * rows >= 1; cols >= 16, cols % 16 == 0; eps finite, >= 0.  flags 0.
+ */
+mq_status mq_rmsnorm_amax(const void* x_bf16, const void* gamma_bf16, void* y_bf16,
+                          mq_scale_rec* rec, int64_t rows, int64_t cols, float eps,
+                          uint32_t flags, void* hip_stream);
+
+/*
+ * mq_swiglu_amax - y = bf16(silu(a) * b) elementwise, silu(a) = a/(1+exp(-a))
+ *   (exp and the reciprocal from the hardware's approximate instructions).
+ * a_bf16, b_bf16, y_bf16  DEVICE bf16 [rows][cols], 16-byte aligned (y may
+ *                 not alias a or b).
+ * rec, flags      as for mq_rmsnorm_amax.
+ * rows >= 1; cols >= 16, cols % 16 == 0.
+ */
+mq_status mq_swiglu_amax(const void* a_bf16, const void* b_bf16, void* y_bf16,
+                         mq_scale_rec* rec, int64_t rows, int64_t cols,
+                         uint32_t flags, void* hip_stream);
 
 /*
  * mq_gemv_nvfp4_decode - Y[M][N] = X[M][K] . W[N][K]^T with X and W in
@@ -280,7 +326,8 @@ mq_status mq_linear_prepare(const mq_linear* L, void* hip_stream);
  *          16-byte, scales 8-byte, rec 16-byte aligned); prefill only.
  * y_bf16   DEVICE bf16 [M][N]; 16-byte aligned for prefill, 2 for decode.
  * flags    0, MQ_PHASE_PREFILL or MQ_PHASE_DECODE, optionally
- *          | MQ_A_FUSED_BF16.
+ *          | MQ_A_FUSED_BF16, optionally | MQ_SCALE_PARTIALS (a_work->rec
+ *          holds x's partial maxima; prefill path).
  * All arguments of the chosen path are checked before anything is queued.
  */
 mq_status mq_linear_forward(const mq_linear* L, const void* x_bf16, int64_t M,

@@ -36,8 +36,8 @@ def L():
 def test_header_declares_the_entry_points():
     fns = _header_functions()
     for f in ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemm_nvfp4_prefill_grouped",
-              "mq_gemv_bf16_decode", "mq_gemv_nvfp4_decode", "mq_linear_path", "mq_linear_prepare",
-              "mq_linear_forward"):
+              "mq_gemv_bf16_decode", "mq_gemv_nvfp4_decode", "mq_rmsnorm_amax", "mq_swiglu_amax",
+              "mq_linear_path", "mq_linear_prepare", "mq_linear_forward"):
         assert f in fns
 
 
@@ -168,6 +168,32 @@ def test_gemv_nvfp4_argument_errors(L):
     assert f(q, q, P1, 1, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
 
 
+def test_producer_argument_errors(L):
+    r = L.mq_rmsnorm_amax
+    assert r(None, P16, P16 + 16, P16, 4, 16, 1e-5, 0, None) == mq.MQ_ERR_INVALID
+    assert r(P16, P16, P16 + 16, None, 4, 16, 1e-5, 0, None) == mq.MQ_ERR_INVALID
+    assert r(P16, P16, P16 + 16, P16, 4, 16, 1e-5, 1, None) == mq.MQ_ERR_INVALID
+    assert r(P16, P16, P16 + 16, P16, 4, 16, -1.0, 0, None) == mq.MQ_ERR_INVALID
+    assert r(P16, P16, P16 + 16, P16, 4, 16, float("nan"), 0, None) == mq.MQ_ERR_INVALID
+    assert r(P16, P16, P16, P16, 4, 16, 1e-5, 0, None) == mq.MQ_ERR_INVALID              # y aliases x
+    assert r(P16, P16, P16 + 16, P16, 0, 16, 1e-5, 0, None) == mq.MQ_ERR_SHAPE
+    assert r(P16, P16, P16 + 16, P16, 4, 24, 1e-5, 0, None) == mq.MQ_ERR_SHAPE
+    assert r(P8, P16, P16 + 16, P16, 4, 16, 1e-5, 0, None) == mq.MQ_ERR_ALIGN
+    assert r(P16, P16, P16 + 16, P8, 4, 16, 1e-5, 0, None) == mq.MQ_ERR_ALIGN
+    s = L.mq_swiglu_amax
+    assert s(P16, None, P16 + 16, P16, 4, 16, 0, None) == mq.MQ_ERR_INVALID
+    assert s(P16, P16, P16 + 16, P16, 4, 16, 2, None) == mq.MQ_ERR_INVALID
+    assert s(P16, P16 + 16, P16 + 16, P16, 4, 16, 0, None) == mq.MQ_ERR_INVALID          # y aliases b
+    assert s(P16, P16, P16 + 16, P16, 4, 0, 0, None) == mq.MQ_ERR_SHAPE
+    assert s(P16, P16, P8, P16, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
+    # the partial-maxima flag: exclusive with a given scale, GEMM only with the fused prologue
+    q = L.mq_quantize_nvfp4
+    assert q(P16, 4, 16, _q(P16, P16, P16), mq.MQ_SCALE_GIVEN | mq.MQ_SCALE_PARTIALS, None) == mq.MQ_ERR_INVALID
+    g = L.mq_gemm_nvfp4_prefill
+    assert g(_q(P16, P16, P16), None, _q(P16, P16, P16), P16, 4, 4, 16, mq.MQ_SCALE_PARTIALS,
+             None) == mq.MQ_ERR_INVALID
+
+
 def _lin(w=P16, codes=P16, scales=P16, rec=P16, N=4, K=16, pmin=33):
     return ctypes.byref(mq._LinearC(w, mq._NVFP4C(codes, scales, rec), N, K, pmin))
 
@@ -243,6 +269,9 @@ def test_valid_arguments_without_a_gpu_report_device_error(L):
     assert _grouped(L, _q(P16, P16, P16), None, [w, w, w], [P16, P16, P16], [4, 8, 12]) == mq.MQ_ERR_DEVICE
     assert L.mq_gemv_nvfp4_decode(_q(P16, P16, P16), _q(P16, P16, P16), P16, 1, 4, 16, 0,
                                   None) == mq.MQ_ERR_DEVICE
+    assert L.mq_rmsnorm_amax(P16, P16, P16 + 16, P16, 4, 16, 1e-5, 0, None) == mq.MQ_ERR_DEVICE
+    assert L.mq_swiglu_amax(P16, P16 + 16, P16 + 32, P16, 4, 16, 0, None) == mq.MQ_ERR_DEVICE
+    assert L.mq_quantize_nvfp4(P16, 4, 16, _q(P16, P16, P16), mq.MQ_SCALE_PARTIALS, None) == mq.MQ_ERR_DEVICE
     assert L.mq_linear_prepare(_lin(), None) == mq.MQ_ERR_DEVICE
     assert L.mq_linear_forward(_lin(), P16, 1, None, P1 + 1, 0, None) == mq.MQ_ERR_DEVICE
     assert L.mq_linear_forward(_lin(), P16, 64, _q(P16, P16, P16), P16, 0, None) == mq.MQ_ERR_DEVICE
