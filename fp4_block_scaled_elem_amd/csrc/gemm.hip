@@ -198,12 +198,12 @@ struct ScaleLoader {
 // elements per stage = BM*8 groups, each thread owning whole groups.  The
 // arithmetic is quantize_group16, bit-identical to the standalone quantizer.
 // Tiles of more than 128 rows take a stage in kParts parts (loaded and
-// quantized at different pipeline steps) so that at most four groups of raw
-// bf16 data are held in registers.
+// quantized at different pipeline steps) so that at most two groups of raw
+// bf16 data per thread are held in registers.
 template <int BM, bool FAST>
 struct FusedALoader {
   static constexpr int kGroupsAll = BM * 8 / kThreads;
-  static constexpr int kParts = kGroupsAll > 4 ? kGroupsAll / 4 : 1;
+  static constexpr int kParts = kGroupsAll > 4 ? kGroupsAll / 2 : 1;
   static constexpr int kGroupsPer = kGroupsAll / kParts;
   u32x4_t raw[kGroupsPer][2];
 
@@ -634,8 +634,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
     // loaders' bounds checks zero a stage past the end instead, which lets an
     // odd stage count finish on a zero half.
     // The A operand of a stage goes through registers in kParts parts (the
-    // fused prologue of a 256-row tile: two), part p loaded at pipeline step
-    // 2p and stored at step 2p + 2.
+    // fused prologue of a 256-row tile: four), part p loaded at pipeline step
+    // 2p and stored at step min(2p + 2, 7), a store before a load in one step.
     constexpr int kParts = FUSED ? FusedALoader<BM, FAST>::kParts : 1;
     auto reg_load = [&](int k, int part) __attribute__((always_inline)) {
       const int kc = FAST ? min(k, nk - 1) : k;
@@ -646,13 +646,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
       if constexpr (FUSED) fa.template quantize_store<BN, OVF>(slot, k & 1, gtab, part);
       else if constexpr (!FAST) la.store(slot + SM::kA, k & 1);
     };
-    // pipeline step of one A part's register traffic: store of part step/2 - 1,
-    // then load of part step/2
+    // the A parts' register traffic at pipeline step `step` (0..7)
     auto reg_step = [&](uint8_t* slot, int k, int step) __attribute__((always_inline)) {
-      if (step % 2 == 0 && step / 2 <= kParts) {
-        if (step > 0) reg_store(slot, k, step / 2 - 1);
-        if (step / 2 < kParts) reg_load(k, step / 2);
-      }
+#pragma unroll
+      for (int part = 0; part < kParts; ++part)
+        if (step == min(2 * part + 2, 7)) reg_store(slot, k, part);
+#pragma unroll
+      for (int part = 0; part < kParts; ++part)
+        if (step == 2 * part) reg_load(k, part);
     };
     auto load_stage_reg = [&](uint8_t* slot, int k) __attribute__((always_inline)) {
   #pragma unroll
@@ -856,9 +857,16 @@ hipError_t launch_gemm(const GemmOperandA& A, const GemmWeight* w, int ngroup, i
   }
   a.ngroup = ngroup;
   a.M = (int)M; a.K = (int)K;
-  // fused: a tall A tile is re-quantized once per column tile, so BM stays
-  // small and BN wide to keep the quantize work per MFMA low
-  if (A.bf16) return dispatch_flags<128, 256, true>(a, out_f32, dev.device, stream);
+  // fused: an A tile is re-quantized once per column tile, so wide tiles
+  // keep the quantize work per MFMA low
+  if (A.bf16) {
+    bool fast = fast_shape(K);  // 256x256 where the direct W copies apply
+    for (int g = 0; g < ngroup; ++g) fast = fast && ((uintptr_t)a.w_scales[g] & 15) == 0;
+    if (fast)
+      return out_f32 ? launch_cfg<256, 256, true, true, true>(a, dev.device, stream)
+                     : launch_cfg<256, 256, true, false, true>(a, dev.device, stream);
+    return dispatch_flags<128, 256, true>(a, out_f32, dev.device, stream);
+  }
   switch (pick_tile(M, n, ngroup, K, dev.num_cu)) {
     case 0: return dispatch_flags<256, 256, false>(a, out_f32, dev.device, stream);
     case 1: return dispatch_flags<256, 128, false>(a, out_f32, dev.device, stream);
