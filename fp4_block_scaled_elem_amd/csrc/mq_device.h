@@ -58,21 +58,18 @@ __device__ __forceinline__ uint32_t bf16_absmax_bits(const uint32_t* w) {
 }
 
 // Nearest E4M3 byte to rho >= 0, ties to even, saturating at 448 (0x7E),
-// subnormals (multiples of 2^-9) kept; NaN -> 0x7E.  Below 2^-5 the E4M3
-// values are the multiples of 2^-9 and the code of k * 2^-9 is k, so one
-// binary32 addition of 2^14 (whose ulp is 2^-9) rounds rho to that grid with
-// ties to even and leaves k in the low bits.  From 2^-6 up, rounding the
-// binary32 pattern to 3 fraction bits with ties to even is an integer add of
-// 0x7FFFF plus the kept LSB (a carry moves into the exponent), and the
-// rounded pattern's top bits minus 120 << 3 (binary32 vs E4M3 exponent bias)
-// are the code.  Both forms were checked against the plain case analysis on
-// every binary32 value in [0, 448).
+// subnormals (multiples of 2^-9) kept; NaN -> 0x7E.  This is the hardware
+// fp32 -> fp8 conversion (OCP E4M3 on gfx950) of min(rho, 448) (minNum: a
+// NaN rho gives 448).  It was checked on
+// every binary32 in [0, 448) on gfx950 against the integer form: below 2^-5
+// one binary32 addition of 2^14 (ulp 2^-9) rounds rho to the multiples of
+// 2^-9 with ties to even and leaves the code in the low bits; from 2^-6 up
+// an integer round-to-nearest-even of the pattern to 3 fraction bits gives
+// exponent and mantissa together (minus 120 << 3 for the exponent bias) --
+// which in turn was checked against the plain case analysis on the same
+// range.
 __device__ __forceinline__ uint32_t e4m3_from_f32(float rho) {
-  const uint32_t fine = __float_as_uint(rho + 16384.0f) - 0x46800000u;
-  const uint32_t b = __float_as_uint(rho);
-  const uint32_t coarse = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - 960u;
-  const uint32_t S = rho < 0.03125f ? fine : coarse;
-  return rho < 448.0f ? S : 0x7Eu;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(rho, 448.0f), 0.0f, 0, false) & 0xFFu;
 }
 
 // Exact binary32 value of an E4M3 byte (0x00..0x7E).
@@ -110,7 +107,7 @@ __device__ __forceinline__ float tensor_scale_from_amax(uint32_t amax_bits) {
 // reciprocal to overflow (GroupScaleTab::ovf).
 template <bool OVF>
 __device__ __forceinline__ uint32_t encode8(const uint32_t w[4], float e) {
-  uint32_t c = 0;
+  uint32_t c = w[0];  // any value: the four conversions overwrite all four bytes
   c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, bf16_lo(w[0]) * e, bf16_hi(w[0]) * e, 1.0f, 0);
   c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, bf16_lo(w[1]) * e, bf16_hi(w[1]) * e, 1.0f, 1);
   c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, bf16_lo(w[2]) * e, bf16_hi(w[2]) * e, 1.0f, 2);
