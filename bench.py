@@ -58,6 +58,8 @@ def parse():
                    help="skip the per-kernel rates measured after the timed region (quantizer and decode GEMV)")
     p.add_argument("--cpu-rows", type=int, default=4096, help="activation rows in the CPU sample (at most M)")
     p.add_argument("--cpu-wrows", type=int, default=4096, help="weight rows per projection in the CPU sample")
+    p.add_argument("--layer", action="store_true",
+                   help="only the decoder-layer prefill context measurement (NVFP4 vs BF16 linears)")
     p.add_argument("--decode-only", action="store_true",
                    help="only measure the BF16 decode GEMV at the decode shapes (one JSON line, not the step metric)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -358,6 +360,97 @@ def phase_linear_rates(reps=50):
     return res
 
 
+def layer_prefill(M=4096, reps=20, warm=5):
+    """Context: one 8B-shaped decoder layer's prefill over M tokens (one
+    causal sequence; 32 query heads and 8 key/value heads of 128, no rotary
+    embedding), run twice -- with the method's prefill linears (producer-fused
+    quantization, NVFP4 GEMMs) and with torch's BF16 linears (hipBLASLt),
+    everything else the same torch BF16 ops (attention: torch's
+    scaled_dot_product_attention restricted to its flash / memory-efficient
+    kernels).  Median layer time of each over `reps` event-timed runs, their
+    ratio, the attention's share, and the relative Frobenius difference of
+    the two layers' outputs.  Weights random (N(0, 0.02)), input N(0, 1)."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import fp4_block_scaled_elem_amd as mq
+    import workloads
+    lay = workloads.LLAMA8B
+    D, DKV, FF, H, HKV, HD = lay.d_model, lay.d_kv, lay.d_ffn, 32, 8, 128
+    gen = torch.Generator(device="cuda").manual_seed(4000)
+    rnd = lambda *s, sc=0.02: (torch.randn(s, generator=gen, device="cuda") * sc).to(torch.bfloat16)
+    w = {"q": rnd(D, D), "k": rnd(DKV, D), "v": rnd(DKV, D), "o": rnd(D, D), "gate": rnd(FF, D),
+         "up": rnd(FF, D), "down": rnd(D, FF)}
+    w4 = {p: mq.quantize(t) for p, t in w.items()}
+    g1, g2 = rnd(D, sc=1.0), rnd(D, sc=1.0)
+    h = rnd(M, D, sc=1.0)
+    eps = 1e-5
+    buf = {n: torch.empty((M, c), dtype=torch.bfloat16, device="cuda")
+           for n, c in (("x1", D), ("q", D), ("k", DKV), ("v", DKV), ("o", D), ("x2", D), ("gate", FF),
+                        ("up", FF), ("x3", FF), ("d", D))}
+    qa = {n: mq.NVFP4.empty(M, c) for n, c in (("qkv", D), ("o", D), ("gu", D), ("down", FF))}
+
+    def attention(q, k, v):
+        qh = q.view(1, M, H, HD).transpose(1, 2).contiguous()
+        kh = k.view(1, M, HKV, HD).transpose(1, 2).repeat_interleave(H // HKV, dim=1).contiguous()
+        vh = v.view(1, M, HKV, HD).transpose(1, 2).repeat_interleave(H // HKV, dim=1).contiguous()
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            a = F.scaled_dot_product_attention(qh, kh, vh, is_causal=True)
+        return a.transpose(1, 2).reshape(M, D).contiguous()
+
+    def nvfp4_layer():
+        b = buf
+        mq.mq_rmsnorm_amax(h, g1, b["x1"], qa["qkv"], eps)
+        mq.mq_quantize_nvfp4(b["x1"], qa["qkv"], mq.MQ_SCALE_PARTIALS)
+        mq.mq_gemm_nvfp4_prefill(qa["qkv"], None, w4["q"], b["q"])
+        mq.mq_gemm_nvfp4_prefill_grouped(qa["qkv"], None, [w4["k"], w4["v"]], [b["k"], b["v"]])
+        xo = attention(b["q"], b["k"], b["v"])
+        mq.mq_quantize_nvfp4(xo, qa["o"])
+        mq.mq_gemm_nvfp4_prefill(qa["o"], None, w4["o"], b["o"])
+        h2 = h + b["o"]
+        mq.mq_rmsnorm_amax(h2, g2, b["x2"], qa["gu"], eps)
+        mq.mq_quantize_nvfp4(b["x2"], qa["gu"], mq.MQ_SCALE_PARTIALS)
+        mq.mq_gemm_nvfp4_prefill_grouped(qa["gu"], None, [w4["gate"], w4["up"]], [b["gate"], b["up"]])
+        mq.mq_swiglu_amax(b["gate"], b["up"], b["x3"], qa["down"])
+        mq.mq_quantize_nvfp4(b["x3"], qa["down"], mq.MQ_SCALE_PARTIALS)
+        mq.mq_gemm_nvfp4_prefill(qa["down"], None, w4["down"], b["d"])
+        return h2 + b["d"]
+
+    def bf16_layer():
+        x1 = F.rms_norm(h, (D,), g1, eps)
+        xo = attention(F.linear(x1, w["q"]), F.linear(x1, w["k"]), F.linear(x1, w["v"]))
+        h2 = h + F.linear(xo, w["o"])
+        x2 = F.rms_norm(h2, (D,), g2, eps)
+        x3 = F.silu(F.linear(x2, w["gate"])) * F.linear(x2, w["up"])
+        return h2 + F.linear(x3, w["down"])
+
+    def attn_only():
+        return attention(buf["q"], buf["k"], buf["v"])
+
+    def timed(fn):
+        import statistics
+        for _ in range(warm):
+            fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)
+
+    t4, t16, ta = timed(nvfp4_layer), timed(bf16_layer), timed(attn_only)
+    y4, y16 = nvfp4_layer().float(), bf16_layer().float()
+    torch.cuda.synchronize()
+    lin_flops = 2 * M * sum(a * b for a, b in (lay.proj_nk(p) for p in ("q", "k", "v", "o", "gate", "up", "down")))
+    return {"M": M, "nvfp4_layer_ms": round(t4, 4), "bf16_layer_ms": round(t16, 4),
+            "speedup_vs_bf16": round(t16 / t4, 3), "attention_ms": round(ta, 4),
+            "linear_tflop": round(lin_flops / 1e12, 3),
+            "rel_fro_nvfp4_vs_bf16": round(float(torch.linalg.norm(y4 - y16) / torch.linalg.norm(y16)), 5)}
+
+
 def bf16_reference(cfg, acts, wdev, iters=10):
     """torch's BF16 GEMM (hipBLASLt) at the same shapes, TFLOP/s."""
     import torch
@@ -439,6 +532,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.layer:
+        print(json.dumps({"layer_prefill": layer_prefill()}), flush=True)
         return
     if args.decode_only:
         gemv = decode_gemv_rates()
