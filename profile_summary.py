@@ -16,6 +16,13 @@ Writes profiles/<kernel>_<workload>.txt (per-kernel durations, HBM bytes
 per launch after scaling by the copy calibration) and
 profiles/gemm_traffic_<workload>.json, which bench.py reads for the
 roofline's `traffic` field when the GEMM source is unchanged since.
+
+    python profile_summary.py --counters <run_dir> <workload-name>
+
+<run_dir> holds p1/ and p2/, two `rocprofv3 --kernel-trace --pmc ...` runs
+of the same bench.py command with the counter sets COUNTERS_P1 and
+COUNTERS_P2, and commands.txt; writes profiles/counters_<workload>.txt
+(MFMA, VALU and LDS counters per kind of launch).
 """
 
 from __future__ import annotations
@@ -117,5 +124,96 @@ def main():
     print(path)
 
 
+COUNTERS_P1 = ("GRBM_GUI_ACTIVE SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES "
+               "SQ_INSTS_VALU SQ_ACTIVE_INST_VALU")
+COUNTERS_P2 = ("GRBM_GUI_ACTIVE SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS SQ_INSTS_LDS SQ_VALU_MFMA_COEXEC_CYCLES "
+               "SQ_WAIT_INST_ANY SQ_INSTS_SALU SQ_ACTIVE_INST_ANY")
+N_SIMD = 1024     # 256 CUs x 4 SIMDs
+N_XCD = 8
+MFMA_MACS = 32 * 32 * 16  # v_mfma_f32_32x32x16_f16
+
+
+def dispatches(db_dir: str):
+    """[(kernel, grid, duration_ns, {counter: value})] in dispatch order."""
+    db = glob.glob(os.path.join(db_dir, "**", "*.db"), recursive=True)[0]
+    con = sqlite3.connect(db)
+    meta = {d: (n, g, t) for d, n, g, t in con.execute("select dispatch_id, name, grid_x, duration from kernels")}
+    ev = collections.defaultdict(dict)
+    for d, cn, v in con.execute("select dispatch_id, counter_name, counter_value from pmc_events"):
+        ev[d][cn] = ev[d].get(cn, 0.0) + v
+    return [(short(meta[d][0]), meta[d][1], meta[d][2], ev[d]) for d in sorted(ev)]
+
+
+def counters_main(run: str, workload: str):
+    p1, p2 = dispatches(os.path.join(run, "p1")), dispatches(os.path.join(run, "p2"))
+    if [(a[0], a[1]) for a in p1] != [(b[0], b[1]) for b in p2]:
+        raise SystemExit("the two passes dispatched different kernels")
+    gemm = lambda n: n.startswith("gemm_nvfp4_kernel")
+    tflop = lambda c: 2.0 * MFMA_MACS * c["SQ_INSTS_MFMA"] / 1e12
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for i, ((n, g, t1, c1), (_, _, t2, c2)) in enumerate(zip(p1, p2)):
+        if gemm(n):
+            label = f"{n} : {tflop(c1):.3f} TFLOP"
+        else:
+            # an activation's amax and quantize launches precede its GEMM;
+            # the set-up quantization of a weight is followed by the next one
+            j = i + (1 if n.startswith("quantize") else 2)
+            nxt = p1[j] if j < len(p1) and gemm(p1[j][0]) else None
+            label = f"{n} : input of the {tflop(nxt[3]):.3f} TFLOP GEMM" if nxt else f"{n} : weights (set-up)"
+        r = agg[label]
+        r["us"].append((t1 + t2) / 2e3)
+        for k, v in c1.items():
+            r[k].append(v)
+        for k, v in c2.items():
+            r[k + "/2"].append(v)
+    mean = lambda r, k: sum(r[k]) / len(r[k])
+    hdr = ["kernel : launch", "calls", "avg us", "clock GHz", "MFMA instr", "cycles/MFMA", "MFMA busy %",
+           "co-exec %", "VALU/MFMA", "LDS conflict/instr", "wait %"]
+    rows = []
+    for label in sorted(agg):
+        r = agg[label]
+        us = mean(r, "us")
+        cyc = (mean(r, "GRBM_GUI_ACTIVE") + mean(r, "GRBM_GUI_ACTIVE/2")) / 2 / N_XCD
+        mf, busy = mean(r, "SQ_INSTS_MFMA"), mean(r, "SQ_VALU_MFMA_BUSY_CYCLES")
+        valu, lds = mean(r, "SQ_INSTS_VALU"), mean(r, "SQ_INSTS_LDS/2")
+        conf, coex = mean(r, "SQ_LDS_BANK_CONFLICT/2"), mean(r, "SQ_VALU_MFMA_COEXEC_CYCLES/2")
+        wait, wc = mean(r, "SQ_WAIT_INST_ANY/2"), mean(r, "SQ_WAVE_CYCLES")
+        rows.append([label, str(len(r["us"])), f"{us:.1f}", f"{cyc / (us * 1e3):.2f}", f"{mf:.0f}",
+                     f"{busy / mf:.1f}" if mf else "-", f"{100 * busy / (N_SIMD * cyc):.1f}" if mf else "-",
+                     f"{100 * coex / busy:.1f}" if busy else "-",
+                     f"{valu / mf:.2f}" if mf else f"{valu:.0f} VALU", f"{conf / lds:.2f}" if lds else "-",
+                     f"{100 * wait / wc:.1f}" if wc else "-"])
+    w = [max(len(hdr[i]), *(len(x[i]) for x in rows)) for i in range(len(hdr))]
+    commands = open(os.path.join(run, "commands.txt")).read().strip()
+    lines = [f"# rocprofv3 counters: {workload} (MFMA, VALU and LDS per kind of launch)", "",
+             "Commands (run from the repository root on one MI355X; two passes with their own counter sets):", "",
+             commands, f"python3 profile_summary.py --counters <out> {workload}", "",
+             f"gemm.hip sha256[:16] = {source_hash()}", "",
+             "Averages over the profiled run's dispatches.  GEMM launches are named by their work",
+             "(2 x 32 x 32 x 16 flop per MFMA instruction); quantizer launches by the GEMM they feed.",
+             "Reading of the counters:",
+             f"- SQ_VALU_MFMA_BUSY_CYCLES is summed over the {N_SIMD} SIMDs; per SQ_INSTS_MFMA it is the pipe time",
+             "  of one v_mfma_f32_32x32x16_f16 in cycles (cycles/MFMA).",
+             f"- GRBM_GUI_ACTIVE is summed over the {N_XCD} XCDs: GRBM/{N_XCD} over the duration is the clock.  For",
+             "  launches of a few microseconds it also counts the profiler's per-dispatch overhead, so their",
+             "  clock column is not a clock.",
+             f"- MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / ({N_SIMD} x GRBM/{N_XCD}), the share of SIMD-cycles with the",
+             "  MFMA pipe busy; it equals the achieved flops over the peak at the clock the launch ran at.",
+             "- co-exec % = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES (VALU issued while the pipe ran).",
+             "- VALU/MFMA = SQ_INSTS_VALU / SQ_INSTS_MFMA in wave instructions (kernels without MFMA: the count).",
+             "- LDS conflict/instr = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS (cycles).",
+             "- wait % = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (waves waiting on memory, LDS or MFMA results).", "",
+             " | ".join(h.ljust(w[i]) for i, h in enumerate(hdr)),
+             "-|-".join("-" * x for x in w)]
+    lines += [" | ".join(c.ljust(w[i]) for i, c in enumerate(x)).rstrip() for x in rows]
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.txt")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    open(path, "w").write("\n".join(lines) + "\n")
+    print(path)
+
+
 if __name__ == "__main__":
-    main()
+    if len(sys.argv) > 1 and sys.argv[1] == "--counters":
+        counters_main(sys.argv[2], sys.argv[3])
+    else:
+        main()
