@@ -183,6 +183,43 @@ def _median_us(fn, reps=50, warm=20, batch=10):
     return statistics.median(ts), min(ts)
 
 
+def _graph_us(fn, out, calls=20, reps=20):
+    """Median per-call microseconds of `calls` calls (fn(i)) captured in one
+    HIP graph and replayed `reps` times: the kernels' own back-to-back time,
+    without the host's per-call launch cost that bounds small calls made one
+    by one.  Every replay's output must equal the eager result of the last
+    call (the captured calls record no memsets; the check makes sure)."""
+    import statistics
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            fn(i)
+    fn(calls - 1)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    ts = []
+    for _ in range(reps):
+        out.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / calls)
+        if not torch.equal(out.view(torch.int16), ref.view(torch.int16)):
+            raise RuntimeError("graph replay differs from the eager call")
+    del g
+    return statistics.median(ts)
+
+
 def per_launch(cfg, plan, acts, qw, qa, fa, out, events, steps):
     """TFLOP/s of each launch of the step, from the events of the kernel-timing pass."""
     import workloads
@@ -237,10 +274,12 @@ def decode_gemv_rates(reps=50):
             x = torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16)
             y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
             med, mn = _median_us(lambda r: mq.mq_gemv_bf16_decode(x, ws[r % ncopy], y), reps=reps)
+            gus = _graph_us(lambda r: mq.mq_gemv_bf16_decode(x, ws[r % ncopy], y), y)
             tmed, _ = _median_us(lambda r: F.linear(x, ws[r % ncopy]), reps=reps)
             b = 2 * N * K + 2 * M * K + 2 * M * N
             res[f"{p}_M{M}"] = {"N": N, "K": K, "M": M, "us_median": round(med, 2), "us_min": round(mn, 2),
                                 "GBps": round(b / med / 1e3, 1), "pct_hbm": round(100 * b / med / 1e3 / PEAK_HBM_GBS, 1),
+                                "us_graph": round(gus, 2), "GBps_graph": round(b / gus / 1e3, 1),
                                 "torch_us": round(tmed, 2)}
         del ws
     return res
@@ -270,13 +309,16 @@ def decode_nvfp4_rates(bf16_rates=None, reps=50):
             xq = mq.quantize(torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16))
             y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
             med, mn = _median_us(lambda r: mq.mq_gemv_nvfp4_decode(xq, ws[r % ncopy], y), reps=reps)
+            gus = _graph_us(lambda r: mq.mq_gemv_nvfp4_decode(xq, ws[r % ncopy], y), y)
             b = (N * K + M * K) * 9 // 16 + 2 * M * N
             e = {"N": N, "K": K, "M": M, "us_median": round(med, 2), "us_min": round(mn, 2),
-                 "GBps": round(b / med / 1e3, 1), "pct_hbm": round(100 * b / med / 1e3 / PEAK_HBM_GBS, 1)}
+                 "GBps": round(b / med / 1e3, 1), "pct_hbm": round(100 * b / med / 1e3 / PEAK_HBM_GBS, 1),
+                 "us_graph": round(gus, 2), "GBps_graph": round(b / gus / 1e3, 1)}
             ref = (bf16_rates or {}).get(f"{p}_M{M}")
             if ref:
                 e["bf16_gemv_us"] = ref["us_median"]
                 e["speedup_vs_bf16"] = round(ref["us_median"] / med, 2)
+                e["speedup_vs_bf16_graph"] = round(ref["us_graph"] / gus, 2)
             res[f"{p}_M{M}"] = e
         del ws
     return res
