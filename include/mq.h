@@ -51,6 +51,10 @@
  *     hipStream_t; NULL = the default stream) and MQ_OK is returned without
  *     synchronising.  Launch failures seen by hipGetLastError() right after
  *     the launch give MQ_ERR_LAUNCH.
+ *   - The queued work is kernel launches only (no memset, copy or host
+ *     synchronisation), so calls may be captured into a HIP graph and
+ *     replayed; the first call of each kernel on a device sets its
+ *     dynamic-LDS attribute, so make one eager call before capturing.
  *   - Matrices are contiguous and row-major (leading dimension = columns).
  *   - Outputs are bit-deterministic: no atomics touch output values.
  *   - Calls are thread-safe.  Two calls in flight at once must not share an
