@@ -12,8 +12,11 @@ the GPU better (k with v, gate with up: mq_gemm_nvfp4_prefill_grouped);
 ``--launches separate`` runs one launch per projection instead.
 Weights are quantized once before timing (offline, as the method keeps them
 in the low-precision format).  With --config 3 (M=32768) every GEMM instead
-quantizes its bf16 input in its own prologue.  Inputs are seeded synthetic
-bf16 tensors, resident in HBM before the timed region.
+quantizes its bf16 input in its own prologue: by default each workgroup
+quantizes the 256-row panel of A its tiles read, once, into A's NVFP4
+buffers and multiplies from them (``--fused-form tile``: every A tile is
+re-quantized inside the GEMM's pipeline for each column tile).  Inputs are
+seeded synthetic bf16 tensors, resident in HBM before the timed region.
 
 Prints one JSON line with the whole-step TFLOP/s, the roofline of the
 dominant kernel (the GEMM), torch's BF16 GEMM at the same shapes for
@@ -52,6 +55,10 @@ def parse():
     p.add_argument("--config", type=int, default=2, choices=(2, 3, 5))
     p.add_argument("--launches", choices=("grouped", "separate"), default="grouped",
                    help="grouped: k+v and gate+up as one launch each; separate: one launch per projection")
+    p.add_argument("--fused-form", choices=("panel", "tile"), default="panel",
+                   help="config 3's fused quantization: panel = each workgroup quantizes its 256-row A panel "
+                        "once into A's NVFP4 buffers, then multiplies from them; tile = every A tile is "
+                        "re-quantized in the GEMM's pipeline for each column tile")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16", action="store_true")
     p.add_argument("--no-extras", action="store_true",
@@ -583,6 +590,10 @@ def main():
         print(json.dumps({"decode_gemv": gemv, "decode_nvfp4_gemv": decode_nvfp4_rates(gemv)}), flush=True)
         return
     cfg, acts_host, acts, wdev, qw, qa, fa, out = setup(args.config)
+    fused_form = args.fused_form if cfg.fused_act_quant else None
+    if fused_form == "panel":
+        # the fused launches get A's NVFP4 buffers: the quantize-once form
+        fa = {p: qa[workloads.PROJ_INPUT[p]] for p in cfg.projs}
     flops = cfg.flops()
     plan = launch_plan(cfg, args.launches)
 
@@ -638,11 +649,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "desc": cfg.desc, "M": cfg.M[0],
                    "layer": {"d_model": cfg.layer.d_model, "d_kv": cfg.layer.d_kv, "d_ffn": cfg.layer.d_ffn},
-                   "projections": list(cfg.projs), "act_quant": "fused" if cfg.fused_act_quant else "separate",
+                   "projections": list(cfg.projs), "act_quant": f"fused-{fused_form}" if fused_form else "separate",
                    "launches": ["+".join(g) for _, g in plan],
                    "flop_per_step": flops},
         "pct_mfma_peak": round(100.0 * value / PEAK_F16_MFMA_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "kernel": "gemm_nvfp4_kernel", "achieved": round(gemm_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "gemm_panel_kernel" if fused_form == "panel" else "gemm_nvfp4_kernel",
+                     "achieved": round(gemm_tflops, 2),
                      "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_F16_MFMA_TFLOPS, 4), "traffic": gemm_traffic(cfg.name),
                      "launches_per_step": n_gemm, "avg_launch_ms": round(gemm_ms / n_gemm, 4)},

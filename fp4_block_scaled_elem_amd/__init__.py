@@ -363,15 +363,19 @@ def quantize(x_bf16, stream=None) -> NVFP4:
     return q
 
 
-def prefill_linear(x_bf16, w: NVFP4, out=None, fused: bool = False, rec=None, stream=None):
-    """y = NVFP4(x) . NVFP4(W)^T in bf16, quantizing x on the fly."""
+def prefill_linear(x_bf16, w: NVFP4, out=None, fused: bool = False, rec=None, keep_a: NVFP4 | None = None,
+                   stream=None):
+    """y = NVFP4(x) . NVFP4(W)^T in bf16, quantizing x on the fly.  fused:
+    inside the GEMM launch; with keep_a (an NVFP4 of x's shape) in its
+    quantize-once form, which also leaves x's NVFP4 in keep_a."""
     import torch
     M = x_bf16.shape[0]
     N = w.shape[0]
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x_bf16.device)
     if fused:
-        a = NVFP4(None, None, rec if rec is not None else
-                  torch.zeros(REC_BYTES // 4, dtype=torch.int32, device=x_bf16.device))
+        a = keep_a if keep_a is not None else NVFP4(None, None, rec if rec is not None else
+                                                    torch.zeros(REC_BYTES // 4, dtype=torch.int32,
+                                                                device=x_bf16.device))
         mq_gemm_nvfp4_prefill(a, x_bf16, w, y, MQ_A_FUSED_BF16, stream)
     else:
         a = quantize(x_bf16, stream)

@@ -132,6 +132,8 @@ mq_status mq_gemm_nvfp4_prefill_grouped(const mq_nvfp4* a, const void* a_bf16, i
   if (!a->rec) return fail(MQ_ERR_INVALID, "a->rec must not be NULL");
   if (fused) {
     if (!a_bf16) return fail(MQ_ERR_INVALID, "MQ_A_FUSED_BF16 needs a_bf16");
+    if (!a->codes != !a->scales)
+      return fail(MQ_ERR_INVALID, "with MQ_A_FUSED_BF16 give both a->codes and a->scales, or neither");
   } else {
     if (a_bf16) return fail(MQ_ERR_INVALID, "a_bf16 must be NULL without MQ_A_FUSED_BF16");
     if (!a->codes || !a->scales) return fail(MQ_ERR_INVALID, "a->codes and a->scales must not be NULL");
@@ -139,8 +141,9 @@ mq_status mq_gemm_nvfp4_prefill_grouped(const mq_nvfp4* a, const void* a_bf16, i
   if (mq_status s = check_dims(M, K, "M", "K")) return s;
   if (K % 16) return fail(MQ_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
   if (!aligned(a->rec, 16)) return fail(MQ_ERR_ALIGN, "a->rec needs 16-byte alignment");
-  if (fused ? !aligned(a_bf16, 16) : (!aligned(a->codes, 16) || !aligned(a->scales, 8)))
-    return fail(MQ_ERR_ALIGN, "A operand misaligned");
+  if (fused && !aligned(a_bf16, 16)) return fail(MQ_ERR_ALIGN, "a_bf16 needs 16-byte alignment");
+  if ((!fused || a->codes) && (!aligned(a->codes, 16) || !aligned(a->scales, 8)))
+    return fail(MQ_ERR_ALIGN, "a->codes need 16-byte, a->scales 8-byte alignment");
   mq::GemmWeight gw[MQ_MAX_GROUP];
   int64_t ncols = 0;
   for (int g = 0; g < n_group; ++g) {
@@ -164,7 +167,7 @@ mq_status mq_gemm_nvfp4_prefill_grouped(const mq_nvfp4* a, const void* a_bf16, i
     if (e != hipSuccess) return launched(e, "amax");
   }
   const mq::GemmOperandA A{fused ? nullptr : a->codes, fused ? nullptr : a->scales, fused ? a_bf16 : nullptr,
-                           a->rec, given};
+                           a->rec, given, fused ? a->codes : nullptr, fused ? a->scales : nullptr};
   return launched(mq::launch_gemm(A, gw, n_group, M, K, flags & MQ_OUT_F32, dev, st), fused ? "gemm_fused" : "gemm");
 }
 

@@ -226,9 +226,12 @@ struct FusedALoader {
     }
   }
   // Quantize the loaded groups into stage half p of a slot's A codes and
-  // scale bytes.
-  template <int BN, bool OVF>
-  __device__ __forceinline__ void quantize_store(uint8_t* stage, int p, const GroupScaleTab& tab, int part) const {
+  // scale bytes.  STORE_G: also into A's NVFP4 in global memory (standard
+  // layout) when the stage kt exists (kt < nk) and the row is inside A.
+  template <int BN, bool OVF, bool STORE_G = false>
+  __device__ __forceinline__ void quantize_store(uint8_t* stage, int p, const GroupScaleTab& tab, int part,
+                                                 uint8_t* gcodes = nullptr, uint8_t* gscales = nullptr, int m0 = 0,
+                                                 int M = 0, int K = 0, int kt = 0, int nk = 0) const {
 #pragma unroll
     for (int j = 0; j < kGroupsPer; ++j) {
       const int gi = threadIdx.x + kThreads * (part * kGroupsPer + j);
@@ -240,6 +243,18 @@ struct FusedALoader {
       const int chunk = (4 * p + (grp >> 1)) ^ swz(row);
       *(u32x2_t*)(stage + Smem<BM, BN>::kA + row * kRowStride + chunk * 16 + (grp & 1) * 8) = u32x2_t{lo, hi};
       stage[Smem<BM, BN>::kAs + row * kScaleStride + 8 * p + grp] = (uint8_t)S;
+      if constexpr (STORE_G) {
+        // buffer stores through resources covering the tile's rows inside A
+        // (none past the last stage): the rest are dropped, with no branch
+        const bool live = kt < nk;
+        const int rows = min(BM, M - m0);
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+            gcodes + (int64_t)m0 * (K / 2), 0, live ? rows * (K / 2) : 0, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            gscales + (int64_t)m0 * (K / kGroup), 0, live ? rows * (K / kGroup) : 0, 0x00020000);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo, hi}, rc, row * (K / 2) + grp * 8, kt * kRowBytes, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)S, rs, row * (K / kGroup) + grp, kt * 8, 0);
+      }
     }
   }
 };
@@ -279,9 +294,9 @@ struct DmaLoader {
 
   // Requires BM * K / 2 < 2^31 (checked by the host).
   __device__ __forceinline__ void init(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
-                                       const uint8_t* w_scales, int M, int N, int K, int m0, int n0) {
-    const int lane = threadIdx.x & 63;
-    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+                                       const uint8_t* w_scales, int M, int N, int K, int m0, int n0, int tid) {
+    const int lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int ldc = K / 2, ng = K / kGroup;
     const int ma = min(BM, M - m0), nw = min(BN, N - n0);  // valid rows of the tiles
     if (WITH_A) {
@@ -556,47 +571,53 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
   tn = in / gm;
 }
 
-template <int BM, int BN, bool FAST, bool OUT_F32, bool FUSED>
-__global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int TM = BM / 64, TN = BN / 64;
+// A's tensor scale: from the record, or (REDUCE: the fused prologue without
+// a given scale) reduced from the amax pass's partial maxima by the
+// quantizer's rule, workgroup 0 storing it in the record.
+template <bool REDUCE>
+__device__ __forceinline__ float a_tensor_scale(const GemmArgs& args) {
+  if (!REDUCE || args.a_given) return args.a_rec->s_t;
+  __shared__ uint32_t red[kThreads / 64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint32_t np = args.a_rec->nparts;
+  uint32_t m = 0;
+  for (uint32_t j = tid; j < np; j += kThreads) {
+    uint32_t v = args.a_rec->part[j];
+    m = m > v ? m : v;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = __shfl_xor(m, off, 64);
+    m = m > o ? m : o;
+  }
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = red[0];
+  for (int i = 1; i < kThreads / 64; ++i) m = m > red[i] ? m : red[i];
+  const float s_ta = tensor_scale_from_amax(m);
+  if (blockIdx.x == 0 && tid == 0) {
+    args.a_rec->s_t = s_ta;
+    args.a_rec->amax_bits = m;
+  }
+  return s_ta;
+}
+
+// One output tile (tm, tn): the LDS ring, the main loop and the epilogue.
+// s_ta is A's tensor scale; tid is threadIdx.x (a caller that loops over
+// tiles passes it through an opaque copy, so that the tile's lane-dependent
+// addressing is not hoisted out of its loop and kept live across it).  The
+// LDS is free again when it returns.
+template <int BM, int BN, bool FAST, bool OUT_F32, bool FUSED, bool WRITE_A = false>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& args, int tm, int tn, float s_ta, uint8_t* smem,
+                                          int tid) {
+  constexpr int TM = BM / 64, TN = BN / 64;
+  const int wave = tid >> 6, lane = tid & 63;
   const int li = lane & 31, lh = lane >> 5;
   const int wave_m = (wave >> 1) * (BM / 2), wave_n = (wave & 1) * (BN / 2);
-  int tm, tn;
-  tile_of(blockIdx.x, args.tiles_m, args.tiles_n, tm, tn);
   const GroupView grp = group_of(args, tn);
   const int m0 = tm * BM, n0 = (tn - grp.tn0) * BN;
   const int M = args.M, N = grp.N, K = args.K;
   const int nk = (K + kBK - 1) / kBK;
-
-  float s_ta;
-  if (FUSED && !args.a_given) {
-    // reduce the amax pass's partial maxima (same rule as the quantizer)
-    __shared__ uint32_t red[kThreads / 64];
-    const uint32_t np = args.a_rec->nparts;
-    uint32_t m = 0;
-    for (uint32_t j = tid; j < np; j += kThreads) {
-      uint32_t v = args.a_rec->part[j];
-      m = m > v ? m : v;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      uint32_t o = __shfl_xor(m, off, 64);
-      m = m > o ? m : o;
-    }
-    if (lane == 0) red[wave] = m;
-    __syncthreads();
-    m = red[0];
-    for (int i = 1; i < kThreads / 64; ++i) m = m > red[i] ? m : red[i];
-    s_ta = tensor_scale_from_amax(m);
-    if (blockIdx.x == 0 && tid == 0) {
-      args.a_rec->s_t = s_ta;
-      args.a_rec->amax_bits = m;
-    }
-  } else {
-    s_ta = args.a_rec->s_t;
-  }
   const float scale = s_ta * grp.w_rec->s_t;
   // fused prologue: the group-scale constants of A's tensor scale
   GroupScaleTab gtab{};
@@ -627,7 +648,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
     FusedALoader<BM, FAST> fa;
     PackedLoader<BN, FAST> lw;
     ScaleLoader<BM, BN, FAST, !FUSED> ls;
-    if constexpr (FAST) dma.init(args.a_codes, args.a_scales, grp.w_codes, grp.w_scales, M, N, K, m0, n0);
+    if constexpr (FAST) dma.init(args.a_codes, args.a_scales, grp.w_codes, grp.w_scales, M, N, K, m0, n0, tid);
 
     // Register-path fill of stage k into half (k & 1) of a slot.  FAST (only
     // the fused A tile goes this way) clamps k to the last stage; the ragged
@@ -643,7 +664,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
       else if constexpr (!FAST) la.load(args.a_codes, m0, M, K, kc);
     };
     auto reg_store = [&](uint8_t* slot, int k, int part) __attribute__((always_inline)) {
-      if constexpr (FUSED) fa.template quantize_store<BN, OVF>(slot, k & 1, gtab, part);
+      if constexpr (FUSED && WRITE_A)
+        fa.template quantize_store<BN, OVF, true>(slot, k & 1, gtab, part, (uint8_t*)args.a_codes,
+                                                  (uint8_t*)args.a_scales, m0, M, K, k, nk);
+      else if constexpr (FUSED)
+        fa.template quantize_store<BN, OVF>(slot, k & 1, gtab, part);
       else if constexpr (!FAST) la.store(slot + SM::kA, k & 1);
     };
     // the A parts' register traffic at pipeline step `step` (0..7)
@@ -783,6 +808,49 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
   }
 }
 
+template <int BM, int BN, bool FAST, bool OUT_F32, bool FUSED>
+__global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int tm, tn;
+  tile_of(blockIdx.x, args.tiles_m, args.tiles_n, tm, tn);
+  const float s_ta = a_tensor_scale<FUSED>(args);
+  gemm_tile<BM, BN, FAST, OUT_F32, FUSED>(args, tm, tn, s_ta, smem, threadIdx.x);
+}
+
+// Fused prologue, quantize-once form.  A workgroup takes the column tiles
+// tn = share, share + per_panel, ... of one 256-row panel tm of A.  Its
+// first tile runs the fused pipeline (A's stages quantized in registers
+// while the MFMAs run) and also stores the quantized stages into the
+// caller's NVFP4 buffers for A (standard layout: the bytes mq_quantize_nvfp4
+// writes); its other tiles copy A from there with the direct-to-LDS path.
+// So an A element is quantized once per workgroup of its panel instead of
+// once per column tile.  The per_panel workgroups of a panel each quantize
+// all of it (identical bytes; no synchronisation between workgroups).  A
+// workgroup's own stores have reached L2 (all waves waited for them, then a
+// barrier) before its next tile copies them, and no line of the panel was in
+// its L1 before: only this workgroup reads the panel, and only afterwards.
+template <bool OUT_F32>
+__global__ __launch_bounds__(kThreads, 1) void gemm_panel_kernel(GemmArgs args, int per_panel) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  // sharers of a panel are consecutive in the XCD-major order (one L2)
+  const int nwg = gridDim.x;
+  int logical = blockIdx.x;
+  if ((nwg & 7) == 0) logical = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+  const int tm = logical / per_panel, share = logical - tm * per_panel;
+  const float s_ta = a_tensor_scale<true>(args);
+  gemm_tile<256, 256, true, OUT_F32, true, true>(args, tm, share, s_ta, smem, threadIdx.x);
+  // every wave's stores of A acknowledged (in L2), then the barrier; a
+  // device-scope fence here would write back and invalidate the whole L2
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  __syncthreads();
+  for (int tn = share + per_panel; tn < args.tiles_n; tn += per_panel) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    gemm_tile<256, 256, true, OUT_F32, false>(args, tm, tn, s_ta, smem, tid);
+    __syncthreads();  // the epilogue's LDS staging is done before the next fill
+  }
+}
+
 // ------------------------------------------------------------------ host --
 
 constexpr int kMaxDevices = 64;
@@ -812,6 +880,35 @@ static hipError_t launch_cfg(const GemmArgs& a0, int dev, hipStream_t stream) {
 // The fast variant needs whole double stages (K % 256 == 0) and buffer
 // offsets of a 256-row tile below 2^31 (256 * K/2 < 2^31).
 static bool fast_shape(int64_t K) { return K % (2 * kBK) == 0 && K < (int64_t(1) << 24); }
+
+// Quantize-once fused launch: one workgroup per (panel, share), with as many
+// sharers per panel as fill the CUs (at most one per column tile).
+template <bool OUT_F32>
+static hipError_t launch_panel(const GemmArgs& a0, uint8_t* codes, uint8_t* scales, const DeviceInfo& dev,
+                               hipStream_t stream) {
+  GemmArgs a = a0;
+  a.a_codes = codes;
+  a.a_scales = scales;
+  a.tiles_m = (a.M + 255) / 256;
+  int tn = 0;
+  for (int g = 0; g < a.ngroup; ++g) {
+    tn += (a.n[g] + 255) / 256;
+    a.tn_end[g] = tn;
+  }
+  a.tiles_n = tn;
+  int per = dev.num_cu / a.tiles_m;
+  per = per < 1 ? 1 : (per > tn ? tn : per);
+  auto kern = gemm_panel_kernel<OUT_F32>;
+  constexpr int lds = Smem<256, 256>::kTotal;
+  static bool attr_done[kMaxDevices] = {};  // benign race: the call is idempotent
+  if (dev.device < 0 || dev.device >= kMaxDevices || !attr_done[dev.device]) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    if (dev.device >= 0 && dev.device < kMaxDevices) attr_done[dev.device] = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(a.tiles_m * per), dim3(kThreads), lds, stream, a, per);
+  return hipGetLastError();
+}
 
 template <int BM, int BN, bool FUSED>
 static hipError_t dispatch_flags(const GemmArgs& a, bool out_f32, int d, hipStream_t s) {
@@ -857,9 +954,22 @@ hipError_t launch_gemm(const GemmOperandA& A, const GemmWeight* w, int ngroup, i
   }
   a.ngroup = ngroup;
   a.M = (int)M; a.K = (int)K;
-  // fused: an A tile is re-quantized once per column tile, so wide tiles
-  // keep the quantize work per MFMA low
-  if (A.bf16) {
+  if (A.bf16 && A.out_codes) {
+    // fused, A's NVFP4 kept: quantize once per panel, or (other shapes) the
+    // standalone encode pass into the same buffers and the plain GEMM
+    bool fast = fast_shape(K) && ((uintptr_t)A.out_codes & 15) == 0 && ((uintptr_t)A.out_scales & 15) == 0;
+    for (int g = 0; g < ngroup; ++g) fast = fast && ((uintptr_t)a.w_scales[g] & 15) == 0;
+    if (fast)
+      return out_f32 ? launch_panel<true>(a, A.out_codes, A.out_scales, dev, stream)
+                     : launch_panel<false>(a, A.out_codes, A.out_scales, dev, stream);
+    hipError_t e = launch_quantize(A.bf16, M * K, A.out_codes, A.out_scales, A.rec, A.given, dev, stream);
+    if (e != hipSuccess) return e;
+    a.a_codes = A.out_codes;
+    a.a_scales = A.out_scales;
+    a.a_bf16 = nullptr;
+  } else if (A.bf16) {
+    // fused: an A tile is re-quantized once per column tile, so wide tiles
+    // keep the quantize work per MFMA low
     bool fast = fast_shape(K);  // 256x256 where the direct W copies apply
     for (int g = 0; g < ngroup; ++g) fast = fast && ((uintptr_t)a.w_scales[g] & 15) == 0;
     if (fast)

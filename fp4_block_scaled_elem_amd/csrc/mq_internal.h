@@ -26,6 +26,10 @@ struct GemmOperandA {
   const void* bf16;
   mq_scale_rec* rec;
   bool given;
+  // fused (bf16 given): buffers that receive A's NVFP4, which switches the
+  // launch to the quantize-once form; NULL: re-quantize per tile
+  uint8_t* out_codes;
+  uint8_t* out_scales;
 };
 
 // One weight of a (grouped) GEMM launch and its output C [M][n].

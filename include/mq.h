@@ -153,9 +153,17 @@ mq_status mq_quantize_nvfp4(const void* x_bf16, int64_t rows, int64_t cols,
  * a        HOST pointer to the quantized activations (codes, scales, rec;
  *          rec->s_t must already hold A's scale, e.g. from
  *          mq_quantize_nvfp4 earlier on the same stream).  With
- *          MQ_A_FUSED_BF16, a->codes and a->scales are ignored (may be NULL)
- *          and a->rec receives the amax pass of a_bf16 (or supplies s_t
- *          under MQ_SCALE_GIVEN).
+ *          MQ_A_FUSED_BF16, a->rec receives the amax pass of a_bf16 (or
+ *          supplies s_t under MQ_SCALE_GIVEN) and a->codes / a->scales are
+ *          either both NULL (every A tile is re-quantized inside the GEMM's
+ *          pipeline for each column tile) or both given, [M][K/2] and
+ *          [M][K/16] bytes, 16- and 8-byte aligned: then A's NVFP4 is
+ *          written there (the bytes mq_quantize_nvfp4 writes) and each
+ *          workgroup quantizes the 256-row panel of A it reads once, in its
+ *          first tile, and copies it from there for its other tiles (the
+ *          faster form for long activations; shapes outside the direct-copy
+ *          path run the encode pass into the buffers, then the plain GEMM).
+ *          Nothing else may read or write those buffers during the call.
  * a_bf16   DEVICE bf16 [M][K], 16-byte aligned; only with MQ_A_FUSED_BF16,
  *          else must be NULL.  The fused path computes exactly the codes
  *          mq_quantize_nvfp4 would, inside the GEMM.

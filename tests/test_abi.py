@@ -107,6 +107,12 @@ def test_gemm_argument_errors(L):
     assert f(_q(P8, P16, P16), None, w, P16, 4, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
     assert f(a, None, _q(P16, P1, P16), P16, 4, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
     assert f(_q(None, None, P16), P8, w, P16, 4, 4, 16, mq.MQ_A_FUSED_BF16, None) == mq.MQ_ERR_ALIGN
+    # fused with A's buffers (the quantize-once form): both or neither, aligned
+    fz = mq.MQ_A_FUSED_BF16
+    assert f(_q(P16, None, P16), P16, w, P16, 4, 4, 16, fz, None) == mq.MQ_ERR_INVALID
+    assert f(_q(None, P16, P16), P16, w, P16, 4, 4, 16, fz, None) == mq.MQ_ERR_INVALID
+    assert f(_q(P8, P16, P16), P16, w, P16, 4, 4, 16, fz, None) == mq.MQ_ERR_ALIGN
+    assert f(_q(P16, P1, P16), P16, w, P16, 4, 4, 16, fz, None) == mq.MQ_ERR_ALIGN
 
 
 def _grouped(L, a, a_bf16, ws, cs, ns, M=4, K=16, flags=0, n_group=None):
