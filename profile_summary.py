@@ -40,6 +40,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 GEMM_SRC = os.path.join(ROOT, "fp4_block_scaled_elem_amd", "csrc", "gemm.hip")
 
 
+# the prefill GEMM's kernels: one tile per workgroup, and the fused
+# prologue's quantize-once form
+GEMM_KERNELS = ("gemm_nvfp4_kernel", "gemm_panel_kernel")
+
+
 def source_hash(path=GEMM_SRC) -> str:
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -95,11 +100,11 @@ def main():
     for r in stats:
         lines.append(f"{short(r['Name'])[:72]:72s} {int(r['Calls']):5d} {float(r['AverageNs'])/1e3:9.1f} "
                      f"{float(r['MinNs'])/1e3:9.1f} {float(r['MaxNs'])/1e3:9.1f} {float(r['Percentage']):7.2f}")
-    g_all = [r for r in stats if short(r["Name"]).startswith("gemm_nvfp4_kernel")]
+    g_all = [r for r in stats if short(r["Name"]).startswith(GEMM_KERNELS)]
     if g_all:
         calls = sum(int(r["Calls"]) for r in g_all)
         tot_ns = sum(float(r["TotalDurationNs"]) for r in g_all)
-        lines += ["", f"all gemm_nvfp4_kernel launches: {calls} calls, average {tot_ns / calls / 1e3:.1f} us"]
+        lines += ["", f"all GEMM launches: {calls} calls, average {tot_ns / calls / 1e3:.1f} us"]
     lines += ["", "## HBM bytes per launch (scaled counters), by kernel and grid size", "",
               f"{'kernel':60s} {'grid':>9s} {'read_MiB':>10s} {'write_MiB':>10s}"]
     for k in sorted(set(fb) | set(wb)):
@@ -109,7 +114,7 @@ def main():
     # traffic for the GEMM launches of one step, per launch (mean over launches)
     launches = collections.Counter()
     for (n, g, c), v in fetch.items():
-        if n.startswith("gemm_nvfp4_kernel") and c == "FETCH_SIZE":
+        if n.startswith(GEMM_KERNELS) and c == "FETCH_SIZE":
             launches[(n, g)] += len(v)
     tot = sum(launches.values())
     if not tot:
@@ -148,7 +153,7 @@ def counters_main(run: str, workload: str):
     p1, p2 = dispatches(os.path.join(run, "p1")), dispatches(os.path.join(run, "p2"))
     if [(a[0], a[1]) for a in p1] != [(b[0], b[1]) for b in p2]:
         raise SystemExit("the two passes dispatched different kernels")
-    gemm = lambda n: n.startswith("gemm_nvfp4_kernel")
+    gemm = lambda n: n.startswith(GEMM_KERNELS)
     tflop = lambda c: 2.0 * MFMA_MACS * c["SQ_INSTS_MFMA"] / 1e12
     agg = collections.defaultdict(lambda: collections.defaultdict(list))
     for i, ((n, g, t1, c1), (_, _, t2, c2)) in enumerate(zip(p1, p2)):
