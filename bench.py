@@ -554,18 +554,31 @@ def cpu_baseline(cfg_id, acts_host, rows, wrows):
                        f"elementwise steps single-threaded, float64 matmul on {blas} BLAS threads)")}
 
 
+GEMM_SRC = os.path.join(ROOT, "fp4_block_scaled_elem_amd", "csrc", "gemm.hip")
+
+
+def code_digest(path=GEMM_SRC) -> str:
+    """sha256[:16] of a source file's code with comments and whitespace
+    removed: a comment edit keeps it, any change to the code does not."""
+    import hashlib
+    import re
+    src = open(path).read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = re.sub(r"\s+", " ", src).strip()
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
+
+
 def gemm_traffic(workload):
     """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
-    or None when the GEMM source has changed since the counters were taken."""
-    import hashlib
+    or None when the GEMM's code has changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"gemm_traffic_{workload}.json")
-    src = os.path.join(ROOT, "fp4_block_scaled_elem_amd", "csrc", "gemm.hip")
     try:
         rec = json.load(open(path))
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        h = code_digest()
     except (OSError, ValueError):
         return None
-    if rec.get("gemm_source_sha256_16") != h:
+    if rec.get("gemm_code_digest_16") != h:
         return None
     return int(rec["bytes_per_launch"])
 

@@ -832,7 +832,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nvfp4_kernel(GemmArgs args) 
 template <bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 1) void gemm_panel_kernel(GemmArgs args, int per_panel) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  // sharers of a panel are consecutive in the XCD-major order (one L2)
+  // workgroups go round-robin to the 8 XCDs; in the XCD-major order a
+  // panel's sharers are consecutive, so they share an L2 whenever per_panel
+  // divides the grid's share of one XCD (as for M = 16384 or 32768 on 256 CUs)
   const int nwg = gridDim.x;
   int logical = blockIdx.x;
   if ((nwg & 7) == 0) logical = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);

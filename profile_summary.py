@@ -46,8 +46,10 @@ GEMM_KERNELS = ("gemm_nvfp4_kernel", "gemm_panel_kernel")
 
 
 def source_hash(path=GEMM_SRC) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of gemm.hip's code (comments and whitespace ignored), the one
+    bench.py compares before it reports the traffic figure."""
+    from bench import code_digest
+    return code_digest(path)
 
 
 def short(name: str) -> str:
@@ -94,7 +96,7 @@ def main():
              "Commands (run from the repository root on one MI355X):", "", commands, "",
              f"HBM byte counters scaled by the copy calibration: FETCH_SIZE x {f_fetch:.3f}, "
              f"WRITE_SIZE x {f_write:.3f} (a plain 1 GiB read + 1 GiB write elementwise kernel).",
-             f"gemm.hip sha256[:16] = {source_hash()}", "",
+             f"gemm.hip code digest (sha256[:16], comments and whitespace ignored) = {source_hash()}", "",
              "## Kernel trace (--kernel-trace --stats)", "",
              f"{'kernel':72s} {'calls':>5s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'share%':>7s}"]
     for r in stats:
@@ -122,7 +124,7 @@ def main():
         return
     mean_read = sum(fb[k] * launches[k] for k in launches) / tot
     mean_write = sum(wb.get(k, 0) * launches[k] for k in launches) / tot
-    json.dump({"workload": workload, "gemm_source_sha256_16": source_hash(),
+    json.dump({"workload": workload, "gemm_code_digest_16": source_hash(),
                "bytes_per_launch": mean_read + mean_write, "read_bytes_per_launch": mean_read,
                "write_bytes_per_launch": mean_write, "fetch_scale": f_fetch, "write_scale": f_write},
               open(os.path.join(ROOT, "profiles", f"gemm_traffic_{workload}.json"), "w"), indent=1)
@@ -193,7 +195,7 @@ def counters_main(run: str, workload: str):
     lines = [f"# rocprofv3 counters: {workload} (MFMA, VALU and LDS per kind of launch)", "",
              "Commands (run from the repository root on one MI355X; two passes with their own counter sets):", "",
              commands, f"python3 profile_summary.py --counters <out> {workload}", "",
-             f"gemm.hip sha256[:16] = {source_hash()}", "",
+             f"gemm.hip code digest (sha256[:16], comments and whitespace ignored) = {source_hash()}", "",
              "Averages over the profiled run's dispatches.  GEMM launches are named by their work",
              "(2 x 32 x 32 x 16 flop per MFMA instruction); quantizer launches by the GEMM they feed.",
              "Reading of the counters:",
