@@ -174,3 +174,22 @@ def test_panel_from_producer_partials():
     qa = mq.quantize(y)
     (c2,) = _run_plain(qa, [qw], M)
     assert _same(c, c2) and _same_quantization(a, qa)
+
+
+def test_linear_fused_with_work_buffers_takes_the_panel_form():
+    # the phase-aware linear's fused prefill with a full NVFP4 work buffer
+    # routes to the quantize-once form: same output as the plain path, and
+    # the work buffer ends up holding x's NVFP4
+    announce("linear fused with work buffers")
+    import torch
+    mq = _mq()
+    M, K, N = 300, 1024, 512
+    lin = mq.Linear(to_dev_bf16(workloads.random_bf16((N, K), 41, 0.02))).prepare()
+    x = to_dev_bf16(workloads.random_bf16((M, K), 42, 1.0, "lognormal_mixed"))
+    aw = mq.NVFP4.empty(M, K)
+    y = lin.forward(x, flags=mq.MQ_A_FUSED_BF16, a_work=aw)
+    y2 = lin.forward(x)
+    qa = mq.quantize(x)
+    torch.cuda.synchronize()
+    assert _same(y, y2)
+    assert _same_quantization(aw, qa)

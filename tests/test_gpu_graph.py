@@ -77,8 +77,11 @@ def test_prefill_quantize_and_gemm_replay():
         assert _same(c, ce), f"replay {r}: gemm output"
 
 
-def test_fused_prologue_gemm_replay():
-    announce("graph: fused-prologue gemm")
+@pytest.mark.parametrize("form", ["tile", "panel"])
+def test_fused_prologue_gemm_replay(form):
+    # tile: A re-quantized per column tile; panel: quantized once per
+    # workgroup into A's NVFP4 buffers (the quantize-once kernel)
+    announce("graph: fused-prologue gemm", form)
     import torch
     mq = _mq()
     M, K, N = 256, 512, 512
@@ -87,7 +90,8 @@ def test_fused_prologue_gemm_replay():
     x.copy_(to_dev_bf16(workloads.random_bf16((M, K), 4, 1.0)))
     c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     rec = torch.zeros(mq.REC_BYTES // 4, dtype=torch.int32, device="cuda")
-    g = _capture(lambda: mq.prefill_linear(x, w, out=c, fused=True, rec=rec))
+    keep = mq.NVFP4.empty(M, K) if form == "panel" else None
+    g = _capture(lambda: mq.prefill_linear(x, w, out=c, fused=True, rec=rec, keep_a=keep))
     for r in range(REPLAYS):
         xr = to_dev_bf16(workloads.random_bf16((M, K), 20 + r, 0.5 + r, "lognormal_mixed"))
         x.copy_(xr)
