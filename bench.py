@@ -292,6 +292,49 @@ def decode_gemv_rates(reps=50):
     return res
 
 
+def decode_layer_rates():
+    """One 8B-shaped decoder layer's decode linears on BF16 weights (q, k, v,
+    o, gate, up, down: 432 MB, more than the 256 MB Infinity Cache, so every
+    step streams them from HBM), M in {1, 4, 16, 32}: seven launches of
+    mq_gemv_bf16_decode vs four (q+k+v and gate+up through
+    mq_gemv_bf16_decode_grouped: they read the same input).  Both timed as
+    graph replays (the kernels' own time); GB/s over the weights' bytes."""
+    import torch
+    import fp4_block_scaled_elem_amd as mq
+    import workloads
+    lay = workloads.LLAMA8B
+    gen = torch.Generator(device="cuda").manual_seed(3000)
+    projs = ("q", "k", "v", "o", "gate", "up", "down")
+    w = {p: (torch.randn(lay.proj_nk(p), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+         for p in projs}
+    wbytes = sum(2 * t.numel() for t in w.values())
+    res = {}
+    for M in (1, 4, 16, 32):
+        x = {a: torch.randn((M, lay.act_k(a)), generator=gen, device="cuda").to(torch.bfloat16)
+             for a in ("x_qkv", "x_o", "x_gu", "x_down")}
+        inp = {"q": "x_qkv", "k": "x_qkv", "v": "x_qkv", "o": "x_o", "gate": "x_gu", "up": "x_gu",
+               "down": "x_down"}
+        y = {p: torch.empty((M, lay.proj_nk(p)[0]), dtype=torch.bfloat16, device="cuda") for p in projs}
+
+        def singles(_):
+            for p in projs:
+                mq.mq_gemv_bf16_decode(x[inp[p]], w[p], y[p])
+
+        def grouped(_):
+            mq.mq_gemv_bf16_decode_grouped(x["x_qkv"], [w["q"], w["k"], w["v"]], [y["q"], y["k"], y["v"]])
+            mq.mq_gemv_bf16_decode(x["x_o"], w["o"], y["o"])
+            mq.mq_gemv_bf16_decode_grouped(x["x_gu"], [w["gate"], w["up"]], [y["gate"], y["up"]])
+            mq.mq_gemv_bf16_decode(x["x_down"], w["down"], y["down"])
+
+        t7 = _graph_us(singles, y["v"], calls=5)
+        t4 = _graph_us(grouped, y["v"], calls=5)
+        res[f"M{M}"] = {"us_7_launches": round(t7, 2), "us_4_launches": round(t4, 2),
+                        "GBps_4_launches": round(wbytes / t4 / 1e3, 1), "speedup": round(t7 / t4, 3)}
+        del x, y
+    del w
+    return res
+
+
 def decode_nvfp4_rates(bf16_rates=None, reps=50):
     """The uniform-NVFP4 decode GEMV (X and W both NVFP4) at the decode
     configuration's shapes, M in {1, 16, 32}; weights rotated over copies
@@ -600,7 +643,8 @@ def main():
         return
     if args.decode_only:
         gemv = decode_gemv_rates()
-        print(json.dumps({"decode_gemv": gemv, "decode_nvfp4_gemv": decode_nvfp4_rates(gemv)}), flush=True)
+        print(json.dumps({"decode_gemv": gemv, "decode_nvfp4_gemv": decode_nvfp4_rates(gemv),
+                          "decode_layer": decode_layer_rates()}), flush=True)
         return
     cfg, acts_host, acts, wdev, qw, qa, fa, out = setup(args.config)
     fused_form = args.fused_form if cfg.fused_act_quant else None
@@ -642,6 +686,7 @@ def main():
     quant = None if (args.no_extras or cfg.fused_act_quant) else act_quant_rates(acts)
     gemv = None if args.no_extras else decode_gemv_rates()
     gemv_fp4 = None if args.no_extras else decode_nvfp4_rates(gemv)
+    dec_layer = None if args.no_extras else decode_layer_rates()
     phase = None if args.no_extras else phase_linear_rates()
     producer = None if (args.no_extras or cfg.fused_act_quant) else producer_fused_rates()
     bf16 = None if args.no_bf16 else bf16_reference(cfg, acts, wdev)
@@ -677,6 +722,7 @@ def main():
         "act_quant": quant,
         "decode_gemv": gemv,
         "decode_nvfp4_gemv": gemv_fp4,
+        "decode_layer": dec_layer,
         "phase_linear": phase,
         "producer_fused_act_quant": producer,
         "bf16_torch_tflops": None if bf16 is None else round(bf16, 2),

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI in include/mq.h):
     mq_gemm_nvfp4_prefill(a: NVFP4, a_bf16, w: NVFP4, c, flags=0, stream=None)
     mq_gemm_nvfp4_prefill_grouped(a: NVFP4, a_bf16, ws: [NVFP4], cs: [tensor], flags=0, stream=None)
     mq_gemv_bf16_decode(x_bf16, w_bf16, y_bf16, flags=0, stream=None)
+    mq_gemv_bf16_decode_grouped(x_bf16, ws_bf16: [tensor], ys_bf16: [tensor], flags=0, stream=None)
     mq_gemv_nvfp4_decode(x: NVFP4, w: NVFP4, y_bf16, flags=0, stream=None)
     mq_rmsnorm_amax(x_bf16, gamma_bf16, y_bf16, rec, eps=1e-5, flags=0, stream=None)
     mq_swiglu_amax(a_bf16, b_bf16, y_bf16, rec, flags=0, stream=None)
@@ -50,7 +51,7 @@ MQ_MAX_GROUP = 4
 REC_BYTES = 16 + 4 * MQ_AMAX_PARTS  # sizeof(mq_scale_rec) = 4096
 
 EXPORTS = ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemm_nvfp4_prefill_grouped",
-           "mq_gemv_bf16_decode", "mq_gemv_nvfp4_decode", "mq_rmsnorm_amax", "mq_swiglu_amax", "mq_linear_path", "mq_linear_prepare", "mq_linear_forward",
+           "mq_gemv_bf16_decode", "mq_gemv_bf16_decode_grouped", "mq_gemv_nvfp4_decode", "mq_rmsnorm_amax", "mq_swiglu_amax", "mq_linear_path", "mq_linear_prepare", "mq_linear_forward",
            "mq_status_str", "mq_last_error", "mq_version")
 
 
@@ -96,6 +97,9 @@ def lib():
     L.mq_gemm_nvfp4_prefill_grouped.restype = ctypes.c_int32
     L.mq_gemv_bf16_decode.argtypes = [vp, vp, vp, i64, i64, i64, u32, vp]
     L.mq_gemv_bf16_decode.restype = ctypes.c_int32
+    L.mq_gemv_bf16_decode_grouped.argtypes = [vp, ctypes.c_int32, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                              ctypes.POINTER(i64), i64, i64, u32, vp]
+    L.mq_gemv_bf16_decode_grouped.restype = ctypes.c_int32
     L.mq_gemv_nvfp4_decode.argtypes = [P, P, vp, i64, i64, i64, u32, vp]
     L.mq_gemv_nvfp4_decode.restype = ctypes.c_int32
     L.mq_rmsnorm_amax.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_float, u32, vp]
@@ -256,6 +260,27 @@ def mq_gemv_bf16_decode(x_bf16, w_bf16, y_bf16, flags: int = 0, stream=None):
         raise ValueError("shape mismatch")
     _check(lib().mq_gemv_bf16_decode(_dev_ptr(x_bf16, "x"), _dev_ptr(w_bf16, "w"), _dev_ptr(y_bf16, "y"),
                                      M, N, K, flags, _stream_ptr(stream)), "mq_gemv_bf16_decode")
+
+
+def mq_gemv_bf16_decode_grouped(x_bf16, ws_bf16, ys_bf16, flags: int = 0, stream=None):
+    """ys[g] = X . ws[g]^T for every g, one launch (ws share K; len 1..MQ_MAX_GROUP)."""
+    import torch
+    if len(ws_bf16) != len(ys_bf16) or not ws_bf16:
+        raise ValueError("ws and ys must be non-empty lists of the same length")
+    if x_bf16.dtype != torch.bfloat16 or x_bf16.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    M, K = x_bf16.shape
+    for w, y in zip(ws_bf16, ys_bf16):
+        if w.dtype != torch.bfloat16 or w.dim() != 2 or w.shape[1] != K:
+            raise ValueError(f"each w must be bfloat16 [N_g][{K}]")
+        if y.dtype != torch.bfloat16 or tuple(y.shape) != (M, w.shape[0]):
+            raise ValueError(f"each y must be bfloat16 [{M}][N_g]")
+    n = len(ws_bf16)
+    wp = (ctypes.c_void_p * n)(*[_dev_ptr(w, "w").value for w in ws_bf16])
+    yp = (ctypes.c_void_p * n)(*[_dev_ptr(y, "y").value for y in ys_bf16])
+    nn = (ctypes.c_int64 * n)(*[w.shape[0] for w in ws_bf16])
+    _check(lib().mq_gemv_bf16_decode_grouped(_dev_ptr(x_bf16, "x"), n, wp, yp, nn, M, K, flags,
+                                             _stream_ptr(stream)), "mq_gemv_bf16_decode_grouped")
 
 
 def mq_gemv_nvfp4_decode(x: NVFP4, w: NVFP4, y_bf16, flags: int = 0, stream=None):

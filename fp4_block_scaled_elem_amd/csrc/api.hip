@@ -177,18 +177,37 @@ mq_status mq_gemm_nvfp4_prefill(const mq_nvfp4* a, const void* a_bf16, const mq_
   return mq_gemm_nvfp4_prefill_grouped(a, a_bf16, 1, w, &c, &N, M, K, flags, hip_stream);
 }
 
-mq_status mq_gemv_bf16_decode(const void* x_bf16, const void* w_bf16, void* y_bf16, int64_t M, int64_t N,
-                              int64_t K, uint32_t flags, void* hip_stream) {
+mq_status mq_gemv_bf16_decode_grouped(const void* x_bf16, int32_t n_group, const void* const* w_bf16,
+                                      void* const* y_bf16, const int64_t* N, int64_t M, int64_t K, uint32_t flags,
+                                      void* hip_stream) {
   if (flags) return fail(MQ_ERR_INVALID, "unknown flags 0x%x", flags);
-  if (!x_bf16 || !w_bf16 || !y_bf16) return fail(MQ_ERR_INVALID, "x, w and y must not be NULL");
+  if (n_group < 1 || n_group > MQ_MAX_GROUP)
+    return fail(MQ_ERR_INVALID, "n_group=%d must be in 1..%d", (int)n_group, MQ_MAX_GROUP);
+  if (!x_bf16 || !w_bf16 || !y_bf16 || !N) return fail(MQ_ERR_INVALID, "x, w, y and N must not be NULL");
   if (M < 1 || M > 32) return fail(MQ_ERR_SHAPE, "M=%lld must be in 1..32", (long long)M);
-  if (mq_status s = check_dims(N, K, "N", "K")) return s;
+  if (K < 1 || K > kMaxDim) return fail(MQ_ERR_SHAPE, "K=%lld out of range", (long long)K);
   if (K % 16) return fail(MQ_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
-  if (!aligned(x_bf16, 16) || !aligned(w_bf16, 16) || !aligned(y_bf16, 2))
-    return fail(MQ_ERR_ALIGN, "x and w need 16-byte alignment, y 2-byte");
+  if (!aligned(x_bf16, 16)) return fail(MQ_ERR_ALIGN, "x needs 16-byte alignment");
+  mq::GemvWeight gw[MQ_MAX_GROUP];
+  int64_t nrows = 0;
+  for (int g = 0; g < n_group; ++g) {
+    if (!w_bf16[g] || !y_bf16[g]) return fail(MQ_ERR_INVALID, "group %d: w and y must not be NULL", g);
+    if (mq_status s = check_dims(N[g], K, "N", "K")) return s;
+    if (!aligned(w_bf16[g], 16) || !aligned(y_bf16[g], 2))
+      return fail(MQ_ERR_ALIGN, "group %d: w needs 16-byte alignment, y 2-byte", g);
+    nrows += N[g];
+    gw[g] = mq::GemvWeight{w_bf16[g], y_bf16[g], N[g]};
+  }
+  if (nrows > kMaxDim) return fail(MQ_ERR_SHAPE, "the groups' N add up to more than %lld", (long long)kMaxDim);
   mq::DeviceInfo dev;
   if (mq_status s = current_device(dev)) return s;
-  return launched(mq::launch_gemv(x_bf16, w_bf16, y_bf16, M, N, K, dev, (hipStream_t)hip_stream), "gemv");
+  return launched(mq::launch_gemv_grouped(x_bf16, gw, n_group, M, K, dev, (hipStream_t)hip_stream), "gemv");
+}
+
+mq_status mq_gemv_bf16_decode(const void* x_bf16, const void* w_bf16, void* y_bf16, int64_t M, int64_t N,
+                              int64_t K, uint32_t flags, void* hip_stream) {
+  if (!w_bf16 || !y_bf16) return fail(MQ_ERR_INVALID, "x, w and y must not be NULL");
+  return mq_gemv_bf16_decode_grouped(x_bf16, 1, &w_bf16, &y_bf16, &N, M, K, flags, hip_stream);
 }
 
 mq_status mq_gemv_nvfp4_decode(const mq_nvfp4* x, const mq_nvfp4* w, void* y_bf16, int64_t M, int64_t N,

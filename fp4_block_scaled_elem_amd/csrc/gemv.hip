@@ -89,17 +89,53 @@ __device__ __forceinline__ void lds_read_chunk(const uint32_t (&a)[4], uint4 (&w
 template <int MT>
 constexpr int gv_lds_bytes() { return kGvWaves * 2 * (1 + MT) * kGvTile; }
 
+// Up to MQ_MAX_GROUP weights that read the same X, in one launch: weight g
+// owns the row tiles [tile_end[g-1], tile_end[g]) of the grid.
+struct GvGroups {
+  const uint16_t* w[MQ_MAX_GROUP];
+  uint16_t* y[MQ_MAX_GROUP];
+  int n[MQ_MAX_GROUP];
+  int tile_end[MQ_MAX_GROUP];
+  int ngroup;
+};
+
+// The weight of row tile `tile`, its output, row count and first tile,
+// selected with constant indices (the arrays stay in the argument segment).
+struct GvView {
+  const uint16_t* w;
+  uint16_t* y;
+  int N, t0;
+};
+__device__ __forceinline__ GvView gv_group_of(const GvGroups& g, int tile) {
+  GvView v{g.w[0], g.y[0], g.n[0], 0};
+#pragma unroll
+  for (int k = 1; k < MQ_MAX_GROUP; ++k)
+    if (k < g.ngroup && tile >= g.tile_end[k - 1]) v = GvView{g.w[k], g.y[k], g.n[k], g.tile_end[k - 1]};
+  return v;
+}
+
+// The row tile's weight: looked up (GROUPED), or the only one (a single
+// call, which then reads no other group's fields).
+template <bool GROUPED>
+__device__ __forceinline__ GvView gv_view(const GvGroups& g, int tile) {
+  if constexpr (GROUPED) return gv_group_of(g, tile);
+  return GvView{g.w[0], g.y[0], g.n[0], 0};
+}
+
 // MT column tiles of X (16 rows each) against 16 rows of W per workgroup.
-template <int MT>
-__global__ __launch_bounds__(kGvWaves * 64) void gemv_bf16_kernel(const uint16_t* __restrict__ x,
-                                                                const uint16_t* __restrict__ w,
-                                                                uint16_t* __restrict__ y, int M, int N, int K) {
+template <int MT, bool GROUPED>
+__global__ __launch_bounds__(kGvWaves * 64) void gemv_bf16_kernel(const uint16_t* __restrict__ x, GvGroups grp,
+                                                                int M, int K) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const GvView gv = gv_view<GROUPED>(grp, blockIdx.x);
+  const uint16_t* __restrict__ w = gv.w;
+  uint16_t* __restrict__ y = gv.y;
+  const int N = gv.N;
   constexpr int kBufBytes = (1 + MT) * kGvTile;  // W tile, then MT X tiles
   constexpr int kCopies = 4 * (1 + MT);          // copy instructions per chunk
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int i = lane & 15, h = lane >> 4;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = (blockIdx.x - gv.t0) * 16;
   // the host guarantees 32 * K * 2 < 2^31
   const uint16_t* wtile = w + (int64_t)n0 * K;
   const int wbytes = min(16, N - n0) * K * 2, xbytes = M * K * 2;
@@ -195,16 +231,18 @@ __global__ __launch_bounds__(kGvWaves * 64) void gemv_bf16_kernel(const uint16_t
 // contiguous bytes per instruction), every piece bounds-checked.
 constexpr int kGvMaxWaves = 16;
 
-template <int MT>
+template <int MT, bool GROUPED>
 __global__ __launch_bounds__(kGvMaxWaves * 64) void gemv_bf16_ragged_kernel(const uint16_t* __restrict__ x,
-                                                                   const uint16_t* __restrict__ w,
-                                                                   uint16_t* __restrict__ y, int M, int N,
-                                                                   int K) {
+                                                                   GvGroups grp, int M, int K) {
   __shared__ f32x4_t red[kGvMaxWaves][MT][64];
+  const GvView gv = gv_view<GROUPED>(grp, blockIdx.x);
+  const uint16_t* __restrict__ w = gv.w;
+  uint16_t* __restrict__ y = gv.y;
+  const int N = gv.N;
   const int nw = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = lane & 15, h = lane >> 4;
-  const int n0 = blockIdx.x * 16;
+  const int n0 = (blockIdx.x - gv.t0) * 16;
   int nrow = n0 + i;
   nrow = nrow < N ? nrow : N - 1;
   const uint16_t* wrow = w + (int64_t)nrow * K + 8 * h;
@@ -283,10 +321,10 @@ __global__ __launch_bounds__(kGvMaxWaves * 64) void gemv_bf16_ragged_kernel(cons
   }
 }
 
-template <int MT>
-static hipError_t launch_ring(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K, int dev,
+template <int MT, bool GROUPED>
+static hipError_t launch_ring(const void* x, const GvGroups& g, int tiles, int64_t M, int64_t K, int dev,
                               hipStream_t stream) {
-  auto kern = gemv_bf16_kernel<MT>;
+  auto kern = gemv_bf16_kernel<MT, GROUPED>;
   constexpr int lds = gv_lds_bytes<MT>();
   static bool attr_done[64] = {};  // benign race: the call is idempotent
   if (dev < 0 || dev >= 64 || !attr_done[dev]) {
@@ -294,36 +332,58 @@ static hipError_t launch_ring(const void* x, const void* w, void* y, int64_t M, 
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < 64) attr_done[dev] = true;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)((N + 15) / 16)), dim3(kGvWaves * 64), lds, stream,
-                     (const uint16_t*)x, (const uint16_t*)w, (uint16_t*)y, (int)M, (int)N, (int)K);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kGvWaves * 64), lds, stream, (const uint16_t*)x, g, (int)M,
+                     (int)K);
   return hipGetLastError();
 }
 
-static hipError_t launch_ragged(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
+template <bool GROUPED>
+static hipError_t launch_ragged(const void* x, const GvGroups& g, int tiles, int64_t M, int64_t K,
                                 const DeviceInfo& dev, hipStream_t stream) {
-  const int nwg = (int)((N + 15) / 16);
   const int nchunks = (int)((K + kGvChunk - 1) / kGvChunk);
   // aim for about eight waves per CU over the whole grid
-  int nw = (8 * dev.num_cu + nwg - 1) / nwg;
+  int nw = (8 * dev.num_cu + tiles - 1) / tiles;
   nw = nw < 4 ? 4 : nw;
   nw = nw > kGvMaxWaves ? kGvMaxWaves : nw;
   nw = nw > nchunks ? (nchunks < 1 ? 1 : nchunks) : nw;
   if (M <= 16) {
-    hipLaunchKernelGGL(gemv_bf16_ragged_kernel<1>, dim3(nwg), dim3(nw * 64), 0, stream, (const uint16_t*)x,
-                       (const uint16_t*)w, (uint16_t*)y, (int)M, (int)N, (int)K);
+    hipLaunchKernelGGL((gemv_bf16_ragged_kernel<1, GROUPED>), dim3(tiles), dim3(nw * 64), 0, stream, (const uint16_t*)x, g,
+                       (int)M, (int)K);
   } else {
-    hipLaunchKernelGGL(gemv_bf16_ragged_kernel<2>, dim3(nwg), dim3(nw * 64), 0, stream, (const uint16_t*)x,
-                       (const uint16_t*)w, (uint16_t*)y, (int)M, (int)N, (int)K);
+    hipLaunchKernelGGL((gemv_bf16_ragged_kernel<2, GROUPED>), dim3(tiles), dim3(nw * 64), 0, stream, (const uint16_t*)x, g,
+                       (int)M, (int)K);
   }
   return hipGetLastError();
 }
 
+hipError_t launch_gemv_grouped(const void* x, const GemvWeight* w, int ngroup, int64_t M, int64_t K,
+                               const DeviceInfo& dev, hipStream_t stream) {
+  GvGroups g{};
+  int tiles = 0;
+  for (int k = 0; k < ngroup; ++k) {
+    g.w[k] = (const uint16_t*)w[k].w;
+    g.y[k] = (uint16_t*)w[k].y;
+    g.n[k] = (int)w[k].n;
+    tiles += (int)((w[k].n + 15) / 16);
+    g.tile_end[k] = tiles;
+  }
+  g.ngroup = ngroup;
+  // the ring kernel needs whole chunks and buffer offsets of 32 rows below 2^31
+  const bool ring = K % kGvChunk == 0 && K < (int64_t(1) << 25);
+  if (ngroup == 1) {
+    if (!ring) return launch_ragged<false>(x, g, tiles, M, K, dev, stream);
+    return M <= 16 ? launch_ring<1, false>(x, g, tiles, M, K, dev.device, stream)
+                   : launch_ring<2, false>(x, g, tiles, M, K, dev.device, stream);
+  }
+  if (!ring) return launch_ragged<true>(x, g, tiles, M, K, dev, stream);
+  return M <= 16 ? launch_ring<1, true>(x, g, tiles, M, K, dev.device, stream)
+                 : launch_ring<2, true>(x, g, tiles, M, K, dev.device, stream);
+}
+
 hipError_t launch_gemv(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                        const DeviceInfo& dev, hipStream_t stream) {
-  // the ring kernel needs whole chunks and buffer offsets of 32 rows below 2^31
-  if (K % kGvChunk != 0 || K >= (int64_t(1) << 25)) return launch_ragged(x, w, y, M, N, K, dev, stream);
-  if (M <= 16) return launch_ring<1>(x, w, y, M, N, K, dev.device, stream);
-  return launch_ring<2>(x, w, y, M, N, K, dev.device, stream);
+  const GemvWeight one{w, y, N};
+  return launch_gemv_grouped(x, &one, 1, M, K, dev, stream);
 }
 
 }  // namespace mq

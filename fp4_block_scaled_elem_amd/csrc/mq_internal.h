@@ -45,6 +45,14 @@ hipError_t launch_gemm(const GemmOperandA& a, const GemmWeight* w, int ngroup, i
                        const DeviceInfo& dev, hipStream_t stream);
 hipError_t launch_gemv(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,
                        const DeviceInfo& dev, hipStream_t stream);
+// One weight of a grouped decode GEMV: W [n][K] bf16 and its output Y [M][n].
+struct GemvWeight {
+  const void* w;
+  void* y;
+  int64_t n;
+};
+hipError_t launch_gemv_grouped(const void* x, const GemvWeight* w, int ngroup, int64_t M, int64_t K,
+                               const DeviceInfo& dev, hipStream_t stream);
 
 // NVFP4 x NVFP4 decode GEMV operands: X [M][K] and W [N][K], output bf16
 // Y [M][N].

@@ -17,6 +17,9 @@
  *                          the same for several weights that share A, in one
  *                          launch
  *   mq_gemv_bf16_decode    Y = X . W^T on bf16 X [M][K] and W [N][K]
+ *   mq_gemv_bf16_decode_grouped
+ *                          the same for several weights that share X, in one
+ *                          launch
  *   mq_rmsnorm_amax / mq_swiglu_amax
  *                          the ops that write the linears' activations,
  *                          emitting the amax pass's partial maxima
@@ -218,6 +221,30 @@ mq_status mq_gemm_nvfp4_prefill_grouped(const mq_nvfp4* a, const void* a_bf16,
 mq_status mq_gemv_bf16_decode(const void* x_bf16, const void* w_bf16,
                               void* y_bf16, int64_t M, int64_t N, int64_t K,
                               uint32_t flags, void* hip_stream);
+
+/*
+ * mq_gemv_bf16_decode_grouped - Y_g[M][N_g] = X[M][K] . W_g[N_g][K]^T for
+ *   g = 0 .. n_group-1: the decode linears that read one input (q, k and v
+ *   of attention; gate and up of an MLP) as a single launch, whose
+ *   workgroups cover all the weights' row tiles.  Same arithmetic as
+ *   mq_gemv_bf16_decode (gist.science explainer, s.2 Hybrid Precision
+ *   Strategy, Decoding); each Y_g is bit-identical to what
+ *   mq_gemv_bf16_decode(x, W_g, Y_g) writes.  A decode step is short, so
+ *   fewer launches matter.
+ * x_bf16   DEVICE bf16 [M][K], 16-byte aligned.
+ * n_group  1 .. MQ_MAX_GROUP.
+ * w_bf16   HOST array of n_group DEVICE pointers, W_g bf16 [N_g][K], 16-byte
+ *          aligned.
+ * y_bf16   HOST array of n_group DEVICE pointers, Y_g bf16 [M][N_g].
+ * N        HOST array of n_group row counts, each >= 1, at most 2^30 in all.
+ * M        1..32.  K >= 16, K % 16 == 0.
+ * flags    0.
+ */
+mq_status mq_gemv_bf16_decode_grouped(const void* x_bf16, int32_t n_group,
+                                      const void* const* w_bf16,
+                                      void* const* y_bf16, const int64_t* N,
+                                      int64_t M, int64_t K, uint32_t flags,
+                                      void* hip_stream);
 
 /*
  * Producer ops with the amax pass folded in.  NVFP4's tensor scale of an

@@ -156,6 +156,33 @@ def test_gemv_argument_errors(L):
     assert f(P16, P16, P1, 1, 4, 16, 0, None) == mq.MQ_ERR_ALIGN
 
 
+def test_grouped_gemv_argument_errors(L):
+    f = L.mq_gemv_bf16_decode_grouped
+
+    def call(x, ws, ys, ns, M=1, K=16, flags=0, n_group=None):
+        n = len(ws) if n_group is None else n_group
+        m = max(len(ws), 1)
+        wa = (ctypes.c_void_p * m)(*(ws or [None]))
+        ya = (ctypes.c_void_p * m)(*(ys or [None]))
+        na = (ctypes.c_int64 * m)(*(ns or [1]))
+        return f(x, n, wa, ya, na, M, K, flags, None)
+
+    assert call(P16, [P16], [P16], [4], flags=1) == mq.MQ_ERR_INVALID
+    assert call(P16, [P16], [P16], [4], n_group=0) == mq.MQ_ERR_INVALID
+    assert call(P16, [P16] * 5, [P16] * 5, [4] * 5) == mq.MQ_ERR_INVALID    # more than MQ_MAX_GROUP
+    assert call(None, [P16], [P16], [4]) == mq.MQ_ERR_INVALID
+    assert call(P16, [P16, None], [P16, P16], [4, 4]) == mq.MQ_ERR_INVALID
+    assert call(P16, [P16, P16], [P16, None], [4, 4]) == mq.MQ_ERR_INVALID
+    assert f(P16, 1, None, None, None, 1, 16, 0, None) == mq.MQ_ERR_INVALID
+    assert call(P16, [P16], [P16], [4], M=0) == mq.MQ_ERR_SHAPE
+    assert call(P16, [P16], [P16], [4], M=33) == mq.MQ_ERR_SHAPE
+    assert call(P16, [P16], [P16], [4], K=24) == mq.MQ_ERR_SHAPE
+    assert call(P16, [P16, P16], [P16, P16], [4, 0]) == mq.MQ_ERR_SHAPE
+    assert call(P8, [P16], [P16], [4]) == mq.MQ_ERR_ALIGN
+    assert call(P16, [P16, P8], [P16, P16], [4, 4]) == mq.MQ_ERR_ALIGN
+    assert call(P16, [P16], [P1], [4]) == mq.MQ_ERR_ALIGN
+
+
 def test_gemv_nvfp4_argument_errors(L):
     f = L.mq_gemv_nvfp4_decode
     q = _q(P16, P16, P16)
@@ -271,6 +298,10 @@ def test_valid_arguments_without_a_gpu_report_device_error(L):
     assert L.mq_gemm_nvfp4_prefill(_q(P16, P16, P16), None, _q(P16, P16, P16), P16, 4, 4, 16, 0,
                                    None) == mq.MQ_ERR_DEVICE
     assert L.mq_gemv_bf16_decode(P16, P16, P16, 1, 4, 16, 0, None) == mq.MQ_ERR_DEVICE
+    wa, ya, na = (ctypes.c_void_p * 2)(P16, P16), (ctypes.c_void_p * 2)(P16, P16), (ctypes.c_int64 * 2)(4, 8)
+    assert L.mq_gemv_bf16_decode_grouped(P16, 2, wa, ya, na, 1, 16, 0, None) == mq.MQ_ERR_DEVICE
+    assert L.mq_gemm_nvfp4_prefill(_q(P16, P16, P16), P16, _q(P16, P16, P16), P16, 4, 4, 16,
+                                   mq.MQ_A_FUSED_BF16, None) == mq.MQ_ERR_DEVICE
     w = (P16, P16, P16)
     assert _grouped(L, _q(P16, P16, P16), None, [w, w, w], [P16, P16, P16], [4, 8, 12]) == mq.MQ_ERR_DEVICE
     assert L.mq_gemv_nvfp4_decode(_q(P16, P16, P16), _q(P16, P16, P16), P16, 1, 4, 16, 0,

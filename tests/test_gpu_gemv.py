@@ -77,3 +77,31 @@ def test_deterministic():
     announce("gemv determinism")
     xb, wb = workloads.random_bf16((32, 4096), 1), workloads.random_bf16((1024, 4096), 2, 0.02)
     assert np.array_equal(_gemv(xb, wb), _gemv(xb, wb))
+
+
+@pytest.mark.parametrize("M,Ns,K", [
+    (1, (4096, 1024, 1024), 4096),         # a decode step's q, k and v as one launch
+    (32, (14336, 14336), 4096),           # gate and up
+    (5, (17, 300, 1, 48), 512),           # ragged row counts, four groups
+    (17, (1000, 33), 4112),               # K % 128 != 0: the register-path kernel
+])
+def test_grouped_bit_identical_to_single_calls(M, Ns, K):
+    # one launch over several weights that read the same X: every output is
+    # the single call's, bit for bit (and the single calls are held to the
+    # oracle above); the first group is also checked against the oracle
+    announce("gemv grouped", M, Ns, K)
+    import torch
+    import fp4_block_scaled_elem_amd as mq
+    xb = workloads.random_bf16((M, K), 300 + M, 1.0)
+    wbs = [workloads.random_bf16((n, K), 400 + i, 0.02) for i, n in enumerate(Ns)]
+    x = to_dev_bf16(xb)
+    ws = [to_dev_bf16(wb) for wb in wbs]
+    ys = [torch.empty((M, n), dtype=torch.bfloat16, device="cuda") for n in Ns]
+    mq.mq_gemv_bf16_decode_grouped(x, ws, ys)
+    singles = [mq.decode_linear(x, w) for w in ws]
+    torch.cuda.synchronize()
+    for g, (y, y1) in enumerate(zip(ys, singles)):
+        assert torch.equal(y.view(torch.int16), y1.view(torch.int16)), f"group {g}"
+    ref = oracle.gemv_bf16_ref(workloads.bf16_bits_to_f32(xb), workloads.bf16_bits_to_f32(wbs[0]))
+    r = rule_t(bf16_dev_to_f64(ys[0]), ref, bf16_out=True)
+    assert r.ok, str(r)
