@@ -7,10 +7,29 @@
 // memory or synchronises.
 #include <mutex>
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
 #include "mq_internal.h"
+
+namespace mq {
+
+void log_launch(const char* kernel, unsigned grid, unsigned block, size_t lds, const char* fmt, ...) {
+  static const bool on = [] {
+    const char* v = getenv("MQ_LOG");
+    return v && v[0] && strcmp(v, "0") != 0;
+  }();
+  if (!on) return;
+  char shape[192];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(shape, sizeof shape, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "mq: %s grid=%u block=%u lds=%zu %s\n", kernel, grid, block, lds, shape);
+}
+
+}  // namespace mq
 
 namespace {
 

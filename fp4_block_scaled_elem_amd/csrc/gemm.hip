@@ -875,6 +875,9 @@ static hipError_t launch_cfg(const GemmArgs& a0, int dev, hipStream_t stream) {
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < kMaxDevices) attr_done[dev] = true;
   }
+  log_launch("gemm_nvfp4_kernel", a.tiles_m * a.tiles_n, kThreads, lds,
+             "tile=%dx%d fast=%d out_f32=%d fused=%d M=%d K=%d tiles=%dx%d groups=%d", BM, BN, (int)FAST,
+             (int)OUT_F32, (int)FUSED, a.M, a.K, a.tiles_m, a.tiles_n, a.ngroup);
   hipLaunchKernelGGL(kern, dim3(a.tiles_m * a.tiles_n), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
@@ -908,6 +911,9 @@ static hipError_t launch_panel(const GemmArgs& a0, uint8_t* codes, uint8_t* scal
     if (e != hipSuccess) return e;
     if (dev.device >= 0 && dev.device < kMaxDevices) attr_done[dev.device] = true;
   }
+  log_launch("gemm_panel_kernel", a.tiles_m * per, kThreads, lds,
+             "out_f32=%d M=%d K=%d panels=%d per_panel=%d column_tiles=%d groups=%d", (int)OUT_F32, a.M, a.K,
+             a.tiles_m, per, tn, a.ngroup);
   hipLaunchKernelGGL(kern, dim3(a.tiles_m * per), dim3(kThreads), lds, stream, a, per);
   return hipGetLastError();
 }

@@ -332,6 +332,8 @@ static hipError_t launch_ring(const void* x, const GvGroups& g, int tiles, int64
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < 64) attr_done[dev] = true;
   }
+  log_launch("gemv_bf16_kernel", tiles, kGvWaves * 64, lds, "column_tiles=%d grouped=%d M=%lld K=%lld groups=%d",
+             MT, (int)GROUPED, (long long)M, (long long)K, g.ngroup);
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kGvWaves * 64), lds, stream, (const uint16_t*)x, g, (int)M,
                      (int)K);
   return hipGetLastError();
@@ -346,6 +348,8 @@ static hipError_t launch_ragged(const void* x, const GvGroups& g, int tiles, int
   nw = nw < 4 ? 4 : nw;
   nw = nw > kGvMaxWaves ? kGvMaxWaves : nw;
   nw = nw > nchunks ? (nchunks < 1 ? 1 : nchunks) : nw;
+  log_launch("gemv_bf16_ragged_kernel", tiles, nw * 64, 0, "grouped=%d M=%lld K=%lld groups=%d", (int)GROUPED,
+             (long long)M, (long long)K, g.ngroup);
   if (M <= 16) {
     hipLaunchKernelGGL((gemv_bf16_ragged_kernel<1, GROUPED>), dim3(tiles), dim3(nw * 64), 0, stream, (const uint16_t*)x, g,
                        (int)M, (int)K);

@@ -168,6 +168,9 @@ __global__ __launch_bounds__(kGnWaves * 64) void gemv_nvfp4_kernel(
 
 template <int MT, bool FAST>
 static hipError_t launch_gn(const GemvNvfp4Args& a, hipStream_t stream) {
+  log_launch("gemv_nvfp4_kernel", (unsigned)((a.N + 15) / 16), kGnWaves * 64, 0,
+             "column_tiles=%d fast=%d M=%lld N=%lld K=%lld", MT, (int)FAST, (long long)a.M, (long long)a.N,
+             (long long)a.K);
   hipLaunchKernelGGL((gemv_nvfp4_kernel<MT, FAST>), dim3((unsigned)((a.N + 15) / 16)), dim3(kGnWaves * 64), 0,
                      stream, a.x_codes, a.x_scales, a.x_rec, a.w_codes, a.w_scales, a.w_rec, (uint16_t*)a.y,
                      (int)a.M, (int)a.N, (int)a.K);

@@ -14,6 +14,12 @@ struct DeviceInfo {
   int ok = 0;  // gfx950
 };
 
+// With MQ_LOG=1 in the environment (read once per process) every launch
+// prints its kernel, grid, block, dynamic LDS and shape to stderr; otherwise
+// the call returns at once.
+void log_launch(const char* kernel, unsigned grid, unsigned block, size_t lds, const char* fmt, ...)
+    __attribute__((format(printf, 5, 6)));
+
 hipError_t launch_amax(const void* x_bf16, int64_t nelem, mq_scale_rec* rec, const DeviceInfo& dev,
                        hipStream_t stream);
 hipError_t launch_quantize(const void* x_bf16, int64_t nelem, uint8_t* codes, uint8_t* scales,

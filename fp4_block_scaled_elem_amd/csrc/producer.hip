@@ -174,6 +174,7 @@ hipError_t launch_rmsnorm_amax(const void* x, const void* g, void* y, int64_t ro
   const int64_t row_groups = (rows + kRThreads / 64 - 1) / (kRThreads / 64);  // eight rows per workgroup
   int64_t blocks = row_groups < 2 * (int64_t)dev.num_cu ? row_groups : 2 * (int64_t)dev.num_cu;
   if (blocks > MQ_AMAX_PARTS) blocks = MQ_AMAX_PARTS;
+  log_launch("rmsnorm_amax_kernel", blocks, kRThreads, 0, "rows=%lld cols=%lld", (long long)rows, (long long)cols);
   hipLaunchKernelGGL(rmsnorm_amax_kernel, dim3((unsigned)blocks), dim3(kRThreads), 0, stream, (const uint4*)x,
                      (const uint4*)g, (uint4*)y, rows, (int)cols, eps, rec);
   return hipGetLastError();
@@ -186,6 +187,7 @@ hipError_t launch_swiglu_amax(const void* a, const void* b, void* y, int64_t n, 
   if (blocks > 2 * (int64_t)dev.num_cu) blocks = 2 * (int64_t)dev.num_cu;
   if (blocks > MQ_AMAX_PARTS) blocks = MQ_AMAX_PARTS;
   if (blocks < 1) blocks = 1;
+  log_launch("swiglu_amax_kernel", blocks, kPThreads, 0, "elements=%lld", (long long)n);
   hipLaunchKernelGGL(swiglu_amax_kernel, dim3((unsigned)blocks), dim3(kPThreads), 0, stream, (const uint4*)a,
                      (const uint4*)b, (uint4*)y, n8, rec);
   return hipGetLastError();

@@ -221,6 +221,7 @@ hipError_t launch_amax(const void* x_bf16, int64_t nelem, mq_scale_rec* rec, con
   // maxima for every quantize workgroup to reduce (measured faster than four)
   int blocks = grid_for((n16 + 3) / 4, kQThreads, dev.num_cu * 2);
   if (blocks > MQ_AMAX_PARTS) blocks = MQ_AMAX_PARTS;
+  log_launch("amax_kernel", blocks, kQThreads, 0, "elements=%lld", (long long)nelem);
   hipLaunchKernelGGL(amax_kernel, dim3(blocks), dim3(kQThreads), 0, stream,
                      (const uint4*)x_bf16, n16, rec);
   return hipGetLastError();
@@ -230,6 +231,7 @@ hipError_t launch_quantize(const void* x_bf16, int64_t nelem, uint8_t* codes, ui
                            mq_scale_rec* rec, bool given, const DeviceInfo& dev, hipStream_t stream) {
   const int64_t nhalf = nelem / 8;  // 8 elements per lane, two lanes per group
   int blocks = grid_for((nhalf + 3) / 4, kQThreads, dev.num_cu * 8);
+  log_launch("quantize_kernel", blocks, kQThreads, 0, "elements=%lld given=%d", (long long)nelem, (int)given);
   hipLaunchKernelGGL(quantize_kernel, dim3(blocks), dim3(kQThreads), 0, stream,
                      (const uint4*)x_bf16, nhalf, (uint32_t*)codes, scales, rec, given ? 1 : 0);
   return hipGetLastError();

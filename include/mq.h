@@ -62,6 +62,8 @@
  *   - Outputs are bit-deterministic: no atomics touch output values.
  *   - Calls are thread-safe.  Two calls in flight at once must not share an
  *     output buffer or an mq_scale_rec.
+ *   - With MQ_LOG=1 in the environment (read once per process), every launch
+ *     prints its kernel, grid, block, dynamic LDS and shape to stderr.
  */
 #ifndef MQ_H_
 #define MQ_H_
