@@ -358,7 +358,8 @@ mq_status mq_linear_prepare(const mq_linear* L, void* hip_stream);
  *   (mq_quantize_nvfp4, dynamic scale), then mq_gemm_nvfp4_prefill with
  *   L->w_nvfp4, bf16 output; with MQ_A_FUSED_BF16 the quantization runs in
  *   the GEMM's prologue instead (a_work->rec is still used; codes and scales
- *   may be NULL).
+ *   may both be NULL, or both given: then the GEMM takes its quantize-once
+ *   form and leaves X's NVFP4 in them, as mq_gemm_nvfp4_prefill describes).
  *   Each path's output is bit-identical to the direct calls it names.
  * L        HOST pointer; L->w_nvfp4 must hold mq_linear_prepare's result
  *          before a prefill call runs.
