@@ -57,10 +57,13 @@ __global__ __launch_bounds__(kQThreads) void amax_kernel(const uint4* __restrict
   int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
   uint32_t m0 = 0, m1 = 0;
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    uint4 a = ld_stream(&x[i]);
-    uint4 b = ld_stream(&x[i + stride]);
-    uint4 c = ld_stream(&x[i + 2 * stride]);
-    uint4 d = ld_stream(&x[i + 3 * stride]);
+    // ordinary (cached) loads: the encode pass reads the same bytes next,
+    // and finds part of them in the caches (3% faster for both passes than
+    // streaming loads here, measured)
+    uint4 a = x[i];
+    uint4 b = x[i + stride];
+    uint4 c = x[i + 2 * stride];
+    uint4 d = x[i + 3 * stride];
     uint32_t ma = uint4_absmax(a), mb = uint4_absmax(b), mc = uint4_absmax(c), md = uint4_absmax(d);
     ma = ma > mb ? ma : mb;
     mc = mc > md ? mc : md;
