@@ -6,8 +6,9 @@
 // workers) runs on the original BF16 weights.  With M <= 32 rows of X the
 // work is bound by streaming W from HBM (2 bytes per weight, M flops/byte),
 // so the kernel is organised around W's bytes:
-//   - a workgroup owns 16 rows of W and all of K; its four waves take the
-//     K chunks (128 elements = 256 bytes per row) in turn;
+//   - a workgroup owns 16 rows of W (32 at M > 16 when the grid still has
+//     a workgroup per CU) and all of K; its four waves take the K chunks
+//     (128 elements = 256 bytes per row) in turn;
 //   - each wave has two LDS buffers, one chunk each: the chunk's 16 W rows
 //     and the matching X pieces (16 rows per column tile) arrive by
 //     buffer_load ... lds, every instruction copying four rows of 256 bytes
@@ -87,8 +88,45 @@ __device__ __forceinline__ void lds_read_chunk(const uint32_t (&a)[4], uint4 (&w
   wv[3] = __builtin_bit_cast(uint4, w3);
 }
 
-template <int MT>
-constexpr int gv_lds_bytes() { return kGvWaves * 2 * (1 + MT) * kGvTile; }
+// Two W tiles and two X tiles (32 W rows against 32 X rows): the pieces of
+// W tile t at a[q] + 4096 t, of X tile u at a[q] + 4096 (2 + u).  One asm
+// block with its wait, as above.
+__device__ __forceinline__ void lds_read_chunk_w2(const uint32_t (&a)[4], uint4 (&wv)[2][4], uint4 (&xv)[4][2]) {
+  u32x4_t w0, w1, w2, w3, v0, v1, v2, v3, x0, x1, x2, x3, y0, y1, y2, y3;
+  asm volatile(
+      "ds_read_b128 %0, %16\n\tds_read_b128 %4, %16 offset:4096\n\t"
+      "ds_read_b128 %8, %16 offset:8192\n\tds_read_b128 %12, %16 offset:12288\n\t"
+      "ds_read_b128 %1, %17\n\tds_read_b128 %5, %17 offset:4096\n\t"
+      "ds_read_b128 %9, %17 offset:8192\n\tds_read_b128 %13, %17 offset:12288\n\t"
+      "ds_read_b128 %2, %18\n\tds_read_b128 %6, %18 offset:4096\n\t"
+      "ds_read_b128 %10, %18 offset:8192\n\tds_read_b128 %14, %18 offset:12288\n\t"
+      "ds_read_b128 %3, %19\n\tds_read_b128 %7, %19 offset:4096\n\t"
+      "ds_read_b128 %11, %19 offset:8192\n\tds_read_b128 %15, %19 offset:12288\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3), "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3), "=&v"(x0),
+        "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(y0), "=&v"(y1), "=&v"(y2), "=&v"(y3)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+  wv[0][0] = __builtin_bit_cast(uint4, w0);
+  wv[0][1] = __builtin_bit_cast(uint4, w1);
+  wv[0][2] = __builtin_bit_cast(uint4, w2);
+  wv[0][3] = __builtin_bit_cast(uint4, w3);
+  wv[1][0] = __builtin_bit_cast(uint4, v0);
+  wv[1][1] = __builtin_bit_cast(uint4, v1);
+  wv[1][2] = __builtin_bit_cast(uint4, v2);
+  wv[1][3] = __builtin_bit_cast(uint4, v3);
+  xv[0][0] = __builtin_bit_cast(uint4, x0);
+  xv[1][0] = __builtin_bit_cast(uint4, x1);
+  xv[2][0] = __builtin_bit_cast(uint4, x2);
+  xv[3][0] = __builtin_bit_cast(uint4, x3);
+  xv[0][1] = __builtin_bit_cast(uint4, y0);
+  xv[1][1] = __builtin_bit_cast(uint4, y1);
+  xv[2][1] = __builtin_bit_cast(uint4, y2);
+  xv[3][1] = __builtin_bit_cast(uint4, y3);
+}
+
+template <int MT, int WT>
+constexpr int gv_lds_bytes() { return kGvWaves * 2 * (WT + MT) * kGvTile; }
 
 // Up to MQ_MAX_GROUP weights that read the same X, in one launch: weight g
 // owns the row tiles [tile_end[g-1], tile_end[g]) of the grid.
@@ -123,9 +161,11 @@ __device__ __forceinline__ GvView gv_view(const GvGroups& g, int tile) {
   return GvView{g.w[0], g.y[0], g.n[0], 0};
 }
 
-// MT column tiles of X (16 rows each) against 16 rows of W per workgroup.
+// MT column tiles of X (16 rows each) against WT row tiles of W (16 rows
+// each) per workgroup (WT = 2 only with MT = 2: at M > 16 two X tiles would
+// otherwise take two thirds of the ring, and with it of the bytes in flight).
 // NT: W's copies are non-temporal (W is read once; X stays in L2).
-template <int MT, bool GROUPED, bool NT>
+template <int MT, bool GROUPED, bool NT, int WT>
 __global__ __launch_bounds__(kGvWaves * 64) void gemv_bf16_kernel(const uint16_t* __restrict__ x, GvGroups grp,
                                                                 int M, int K) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -133,14 +173,15 @@ __global__ __launch_bounds__(kGvWaves * 64) void gemv_bf16_kernel(const uint16_t
   const uint16_t* __restrict__ w = gv.w;
   uint16_t* __restrict__ y = gv.y;
   const int N = gv.N;
-  constexpr int kBufBytes = (1 + MT) * kGvTile;  // W tile, then MT X tiles
-  constexpr int kCopies = 4 * (1 + MT);          // copy instructions per chunk
+  static_assert(WT == 1 || (WT == 2 && MT == 2), "tile combination");
+  constexpr int kBufBytes = (WT + MT) * kGvTile;  // WT W tiles, then MT X tiles
+  constexpr int kCopies = 4 * (WT + MT);          // copy instructions per chunk
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int i = lane & 15, h = lane >> 4;
-  const int n0 = (blockIdx.x - gv.t0) * 16;
+  const int n0 = (blockIdx.x - gv.t0) * 16 * WT;
   // the host guarantees 32 * K * 2 < 2^31
   const uint16_t* wtile = w + (int64_t)n0 * K;
-  const int wbytes = min(16, N - n0) * K * 2, xbytes = M * K * 2;
+  const int wbytes = min(16 * WT, N - n0) * K * 2, xbytes = M * K * 2;
   // copy j of a chunk covers rows 4(j%4) .. +3 of tile j/4 (W, then the X
   // column tiles); lane l: row
   // r = 4(j%4) + l/16, LDS piece l%16 holds logical piece (l%16) ^ r, i.e.
@@ -150,7 +191,7 @@ __global__ __launch_bounds__(kGvWaves * 64) void gemv_bf16_kernel(const uint16_t
 #pragma unroll
   for (int j = 0; j < kCopies; ++j) {
     const int r = 4 * (j % 4) + (lane >> 4), tile = j / 4;
-    const int row = tile == 0 ? r : 16 * (tile - 1) + r;  // row of W or of X
+    const int row = tile < WT ? 16 * tile + r : 16 * (tile - WT) + r;  // row of W or of X
     off[j] = (uint32_t)(row * K + 8 * ((lane & 15) ^ r)) * 2u;
   }
   uint8_t* ring = lds + wave * 2 * kBufBytes;
@@ -167,18 +208,20 @@ __global__ __launch_bounds__(kGvWaves * 64) void gemv_bf16_kernel(const uint16_t
         __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, live ? xbytes : 0, kGvBufferWord3);
     constexpr int kAuxW = NT ? 2 : 0;  // cache policy of W's copies: nt
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4 * WT; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (gv_lds_t*)(dst + 1024 * j), 16, (int)off[j],
                                                live ? k0 * 2 : 0, 0, kAuxW);
 #pragma unroll
-    for (int j = 4; j < kCopies; ++j)
+    for (int j = 4 * WT; j < kCopies; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (gv_lds_t*)(dst + 1024 * j), 16, (int)off[j],
                                                live ? k0 * 2 : 0, 0, 0);
   };
 
-  f32x4_t acc[MT];
+  f32x4_t acc[WT][MT];
 #pragma unroll
-  for (int u = 0; u < MT; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < WT; ++t)
+#pragma unroll
+    for (int u = 0; u < MT; ++u) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Copies run one chunk ahead through two buffers that alternate; before
   // chunk t is read, every copy but the next chunk's must have landed (vmcnt
@@ -196,34 +239,43 @@ __global__ __launch_bounds__(kGvWaves * 64) void gemv_bf16_kernel(const uint16_t
     uint32_t ad[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) ad[q] = (uint32_t)(uintptr_t)(cur + i * kGvRowBytes + (((4 * q + h) ^ i) << 4));
-    uint4 wv[4], xv[4][MT];
-    lds_read_chunk<MT>(ad, wv, xv);
+    uint4 wv[WT][4], xv[4][MT];
+    if constexpr (WT == 1)
+      lds_read_chunk<MT>(ad, wv[0], xv);
+    else
+      lds_read_chunk_w2(ad, wv, xv);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int u = 0; u < MT; ++u)
-        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv[q]),
-                                                        __builtin_bit_cast(bf16x8_t, xv[q][u]), acc[u], 0, 0, 0);
+      for (int t = 0; t < WT; ++t)
+#pragma unroll
+        for (int u = 0; u < MT; ++u)
+          acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv[t][q]),
+                                                             __builtin_bit_cast(bf16x8_t, xv[q][u]), acc[t][u], 0,
+                                                             0, 0);
     uint8_t* done = cur;
     cur = nxt;
     nxt = done;
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): no copy still writes the ring
   __syncthreads();
-  f32x4_t* red = (f32x4_t*)lds;  // [wave][MT][64]
+  constexpr int kPairs = WT * MT;
+  f32x4_t* red = (f32x4_t*)lds;  // [wave][WT * MT][64]
 #pragma unroll
-  for (int u = 0; u < MT; ++u) red[(wave * MT + u) * 64 + lane] = acc[u];
+  for (int t = 0; t < WT; ++t)
+#pragma unroll
+    for (int u = 0; u < MT; ++u) red[(wave * kPairs + t * MT + u) * 64 + lane] = acc[t][u];
   __syncthreads();
-  // wave u finishes column tile u
-  if (wave < MT) {
-    const int u = wave;
-    f32x4_t s = red[u * 64 + lane];
-    for (int v = 1; v < kGvWaves; ++v) s += red[(v * MT + u) * 64 + lane];
+  // wave p finishes W tile p / MT against X tile p % MT
+  if (wave < kPairs) {
+    const int t = wave / MT, u = wave % MT;
+    f32x4_t s = red[wave * 64 + lane];
+    for (int v = 1; v < kGvWaves; ++v) s += red[(v * kPairs + wave) * 64 + lane];
     const int m = (lane & 15) + 16 * u;
     if (m < M) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int n = n0 + 4 * (lane >> 4) + r;
+        const int n = n0 + 16 * t + 4 * (lane >> 4) + r;
         if (n < N) {
           uint32_t b = __float_as_uint(s[r]);
           y[(int64_t)m * N + n] = (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
@@ -328,11 +380,11 @@ __global__ __launch_bounds__(kGvMaxWaves * 64) void gemv_bf16_ragged_kernel(cons
   }
 }
 
-template <int MT, bool GROUPED, bool NT>
+template <int MT, bool GROUPED, bool NT, int WT>
 static hipError_t launch_ring(const void* x, const GvGroups& g, int tiles, int64_t M, int64_t K, int dev,
                               hipStream_t stream) {
-  auto kern = gemv_bf16_kernel<MT, GROUPED, NT>;
-  constexpr int lds = gv_lds_bytes<MT>();
+  auto kern = gemv_bf16_kernel<MT, GROUPED, NT, WT>;
+  constexpr int lds = gv_lds_bytes<MT, WT>();
   static bool attr_done[64] = {};  // benign race: the call is idempotent
   if (dev < 0 || dev >= 64 || !attr_done[dev]) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -340,8 +392,8 @@ static hipError_t launch_ring(const void* x, const GvGroups& g, int tiles, int64
     if (dev >= 0 && dev < 64) attr_done[dev] = true;
   }
   log_launch("gemv_bf16_kernel", tiles, kGvWaves * 64, lds,
-             "column_tiles=%d grouped=%d nt=%d M=%lld K=%lld groups=%d", MT, (int)GROUPED, (int)NT, (long long)M,
-             (long long)K, g.ngroup);
+             "column_tiles=%d row_tiles=%d grouped=%d nt=%d M=%lld K=%lld groups=%d", MT, WT, (int)GROUPED, (int)NT,
+             (long long)M, (long long)K, g.ngroup);
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kGvWaves * 64), lds, stream, (const uint16_t*)x, g, (int)M,
                      (int)K);
   return hipGetLastError();
@@ -350,11 +402,11 @@ static hipError_t launch_ring(const void* x, const GvGroups& g, int tiles, int64
 // W's copies are non-temporal when the grid fills the CUs: measured 4-11%
 // faster on such bandwidth-bound grids (e.g. 4096 x 14336 at M=1: 23.2 ->
 // 20.9 us), but 15-30% slower on the 64-workgroup 1024 x 4096 one.
-template <int MT, bool GROUPED>
+template <int MT, bool GROUPED, int WT = 1>
 static hipError_t launch_ring_nt(const void* x, const GvGroups& g, int tiles, int64_t M, int64_t K,
                                  const DeviceInfo& dev, hipStream_t stream) {
-  return tiles >= dev.num_cu ? launch_ring<MT, GROUPED, true>(x, g, tiles, M, K, dev.device, stream)
-                             : launch_ring<MT, GROUPED, false>(x, g, tiles, M, K, dev.device, stream);
+  return tiles >= dev.num_cu ? launch_ring<MT, GROUPED, true, WT>(x, g, tiles, M, K, dev.device, stream)
+                             : launch_ring<MT, GROUPED, false, WT>(x, g, tiles, M, K, dev.device, stream);
 }
 
 template <bool GROUPED>
@@ -380,25 +432,33 @@ static hipError_t launch_ragged(const void* x, const GvGroups& g, int tiles, int
 
 hipError_t launch_gemv_grouped(const void* x, const GemvWeight* w, int ngroup, int64_t M, int64_t K,
                                const DeviceInfo& dev, hipStream_t stream) {
+  // the ring kernel needs whole chunks and buffer offsets of 32 rows below 2^31
+  const bool ring = K % kGvChunk == 0 && K < (int64_t(1) << 25);
+  // At M > 16 a workgroup takes 32 W rows when that still leaves a workgroup
+  // for every CU: twice the W bytes in flight per CU, half the X bytes per W
+  // byte.  Smaller grids keep 16 rows (more workgroups).
+  int64_t rows = 0;
+  for (int k = 0; k < ngroup; ++k) rows += (w[k].n + 31) / 32;
+  const int wt = ring && M > 16 && rows >= dev.num_cu ? 2 : 1;
   GvGroups g{};
   int tiles = 0;
   for (int k = 0; k < ngroup; ++k) {
     g.w[k] = (const uint16_t*)w[k].w;
     g.y[k] = (uint16_t*)w[k].y;
     g.n[k] = (int)w[k].n;
-    tiles += (int)((w[k].n + 15) / 16);
+    tiles += (int)((w[k].n + 16 * wt - 1) / (16 * wt));
     g.tile_end[k] = tiles;
   }
   g.ngroup = ngroup;
-  // the ring kernel needs whole chunks and buffer offsets of 32 rows below 2^31
-  const bool ring = K % kGvChunk == 0 && K < (int64_t(1) << 25);
   if (ngroup == 1) {
     if (!ring) return launch_ragged<false>(x, g, tiles, M, K, dev, stream);
-    return M <= 16 ? launch_ring_nt<1, false>(x, g, tiles, M, K, dev, stream)
+    if (M <= 16) return launch_ring_nt<1, false>(x, g, tiles, M, K, dev, stream);
+    return wt == 2 ? launch_ring_nt<2, false, 2>(x, g, tiles, M, K, dev, stream)
                    : launch_ring_nt<2, false>(x, g, tiles, M, K, dev, stream);
   }
   if (!ring) return launch_ragged<true>(x, g, tiles, M, K, dev, stream);
-  return M <= 16 ? launch_ring_nt<1, true>(x, g, tiles, M, K, dev, stream)
+  if (M <= 16) return launch_ring_nt<1, true>(x, g, tiles, M, K, dev, stream);
+  return wt == 2 ? launch_ring_nt<2, true, 2>(x, g, tiles, M, K, dev, stream)
                  : launch_ring_nt<2, true>(x, g, tiles, M, K, dev, stream);
 }
 

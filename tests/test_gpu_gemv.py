@@ -42,6 +42,9 @@ def test_cfg4_decode(M, proj):
     # K % 128 == 0: the LDS-ring kernel, with ragged N and M, one chunk (three
     # waves without work), and chunk counts that do not divide by four
     (31, 64, 8192), (1, 1, 128), (17, 1000, 1024), (32, 4100, 256), (2, 33, 384), (16, 17, 640),
+    # M > 16 with at least 256 workgroups of 32 W rows: the two-row-tile
+    # workgroups, the last one's second tile partly or wholly past N
+    (32, 8200, 256), (20, 8197, 384), (17, 8208, 128),
 ])
 def test_ragged(M, N, K):
     announce("gemv ragged", M, N, K)
@@ -84,6 +87,8 @@ def test_deterministic():
     (32, (14336, 14336), 4096),           # gate and up
     (5, (17, 300, 1, 48), 512),           # ragged row counts, four groups
     (17, (1000, 33), 4112),               # K % 128 != 0: the register-path kernel
+    # 32 W rows per workgroup in the grouped launch, 16 in the single calls
+    (32, (5000, 3300), 4096), (17, (8200, 48), 1024),
 ])
 def test_grouped_bit_identical_to_single_calls(M, Ns, K):
     # one launch over several weights that read the same X: every output is

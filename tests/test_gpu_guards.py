@@ -100,7 +100,7 @@ def test_prefill_paths_stay_inside_their_buffers(M, N, K):
     assert torch.equal(kp.codes, qa.codes) and torch.equal(kp.scales, qa.scales)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 17, 128), (17, 1000, 4112), (32, 33, 640), (5, 4100, 256)])
+@pytest.mark.parametrize("M,N,K", [(1, 17, 128), (17, 1000, 4112), (32, 33, 640), (5, 4100, 256), (24, 8200, 256)])
 def test_decode_paths_stay_inside_their_buffers(M, N, K):
     announce("guards decode", M, N, K)
     import torch
