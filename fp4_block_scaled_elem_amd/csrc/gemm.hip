@@ -712,8 +712,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, int tm, int tn, 
       load_stage_reg(smem, 1);
       load_stage_reg(smem + SM::kSlot, 2);
     }
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): direct-to-LDS copies included
-    __syncthreads();
+    if constexpr (FAST && !FUSED) {
+      // only slot 0 is read before the first even barrier (which waits for
+      // everything): wait for double stage 0's copies, issued first, and
+      // leave double stage 1's in flight (vmcnt counts in issue order); a
+      // bare barrier, since __syncthreads() would wait for all copies
+      constexpr int kLater = DmaLoader<BM, BN, true>::kCode + DmaLoader<BM, BN, true>::kScale;
+      static_assert(kLater < 64, "vmcnt range");
+      __builtin_amdgcn_s_waitcnt((kLater & 15) | ((kLater >> 4) << 14) | 0x0070);  // vmcnt(kLater) lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): direct-to-LDS copies included
+      __syncthreads();
+    }
     WavePipe<BM, BN> pipe;
     pipe.init(wave_m, wave_n, li, lh);
     pipe.template read_chunk<0, 0>(smem);
