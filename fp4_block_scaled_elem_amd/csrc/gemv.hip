@@ -9,7 +9,7 @@
 //   - a workgroup owns 16 rows of W (32 at M > 16 when the grid still has
 //     a workgroup per CU) and all of K; its four waves take the K chunks
 //     (128 elements = 256 bytes per row) in turn;
-//   - each wave has two LDS buffers, one chunk each: the chunk's 16 W rows
+//   - each wave has two LDS buffers, one chunk each: the chunk's W rows
 //     and the matching X pieces (16 rows per column tile) arrive by
 //     buffer_load ... lds, every instruction copying four rows of 256 bytes
 //     (whole cache lines), one chunk ahead of use (W's copies non-temporal
