@@ -629,8 +629,8 @@ def gemm_traffic(workload):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "multi-GPU sharding is not part of it", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is not implemented", file=sys.stderr)
         sys.exit(2)
     import torch
     import workloads
