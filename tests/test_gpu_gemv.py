@@ -110,3 +110,26 @@ def test_grouped_bit_identical_to_single_calls(M, Ns, K):
     ref = oracle.gemv_bf16_ref(workloads.bf16_bits_to_f32(xb), workloads.bf16_bits_to_f32(wbs[0]))
     r = rule_t(bf16_dev_to_f64(ys[0]), ref, bf16_out=True)
     assert r.ok, str(r)
+
+
+@pytest.mark.parametrize("M,N_big,N_small,K", [
+    (3, 4096, 4080, 1024),    # 256 vs 255 workgroups: non-temporal W copies on one side only
+    (32, 8192, 8160, 512),    # 256 vs 255 pairs of row tiles: 32-row vs 16-row workgroups
+    (20, 8192, 8160, 384),
+])
+def test_dispatch_boundaries_agree(M, N_big, N_small, K):
+    # the launch choices at these boundaries change cache policy or rows per
+    # workgroup, not arithmetic: the rows both weights share give the same bits
+    announce("gemv boundary", M, N_big, N_small, K)
+    import torch
+    import fp4_block_scaled_elem_amd as mq
+    xb = workloads.random_bf16((M, K), 700 + M, 1.0)
+    wb = workloads.random_bf16((N_big, K), 701 + K, 0.02)
+    x, w = to_dev_bf16(xb), to_dev_bf16(wb)
+    y_big = mq.decode_linear(x, w)
+    y_small = mq.decode_linear(x, w[:N_small].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(y_big[:, :N_small].contiguous().view(torch.int16), y_small.view(torch.int16))
+    ref = oracle.gemv_bf16_ref(workloads.bf16_bits_to_f32(xb), workloads.bf16_bits_to_f32(wb))
+    r = rule_t(bf16_dev_to_f64(y_big), ref, bf16_out=True)
+    assert r.ok, str(r)
