@@ -582,7 +582,7 @@ __device__ __forceinline__ float a_tensor_scale(const GemmArgs& args) {
   if (!REDUCE || args.a_given) return args.a_rec->s_t;
   __shared__ uint32_t red[kThreads / 64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint32_t np = args.a_rec->nparts;
+  const uint32_t np = min(args.a_rec->nparts, (uint32_t)MQ_AMAX_PARTS);  // never past the record
   uint32_t m = 0;
   for (uint32_t j = tid; j < np; j += kThreads) {
     uint32_t v = args.a_rec->part[j];

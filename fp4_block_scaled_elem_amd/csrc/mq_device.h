@@ -60,14 +60,9 @@ __device__ __forceinline__ uint32_t bf16_absmax_bits(const uint32_t* w) {
 // Nearest E4M3 byte to rho >= 0, ties to even, saturating at 448 (0x7E),
 // subnormals (multiples of 2^-9) kept; NaN -> 0x7E.  This is the hardware
 // fp32 -> fp8 conversion (OCP E4M3 on gfx950) of min(rho, 448) (minNum: a
-// NaN rho gives 448).  It was checked on
-// every binary32 in [0, 448) on gfx950 against the integer form: below 2^-5
-// one binary32 addition of 2^14 (ulp 2^-9) rounds rho to the multiples of
-// 2^-9 with ties to even and leaves the code in the low bits; from 2^-6 up
-// an integer round-to-nearest-even of the pattern to 3 fraction bits gives
-// exponent and mantissa together (minus 120 << 3 for the exponent bias) --
-// which in turn was checked against the plain case analysis on the same
-// range.
+// NaN rho gives 448).  tests/test_gpu_codecs.py runs this function on every
+// non-negative binary32 pattern (finite, +inf and NaN) and compares it with
+// the oracle's E4M3 rounding.
 __device__ __forceinline__ uint32_t e4m3_from_f32(float rho) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fminf(rho, 448.0f), 0.0f, 0, false) & 0xFFu;
 }
@@ -99,8 +94,9 @@ __device__ __forceinline__ float tensor_scale_from_amax(uint32_t amax_bits) {
 // The hardware fp32->fp4 conversion (scale 1: no extra power of two) rounds
 // y = x*e to the nearest E2M1 value with ties to the even code, saturates at
 // 6 and keeps the sign of y; that equals e2m1_mag(y) | signbit(x) << 3 for
-// every non-NaN binary32 y (checked exhaustively on gfx950 over all 2^32
-// patterns).  y is NaN only for x = +-0 with e = +inf (a group scale whose
+// every non-NaN binary32 y (tests/test_gpu_codecs.py runs this function on
+// all of them and compares with the oracle's E2M1 rounding).  y is NaN only
+// for x = +-0 with e = +inf (a group scale whose
 // reciprocal overflows); those elements get the sign-only code, as
 // e2m1_mag(NaN) = 0 prescribes.  That fix-up is compiled in only with OVF,
 // which callers select when the tensor scale is small enough for some
@@ -194,21 +190,12 @@ struct BoolC {
   static constexpr bool value = B;
 };
 
-// E4M3 byte -> binary16 bits (exact: every E4M3 value is a normal binary16).
-// Normal E4M3 (exponent field >= 1): same mantissa bits, exponent bias 15
-// instead of 7, i.e. (s << 7) + (8 << 10).  Subnormal E4M3 m * 2^-9 is built
-// from the small integer m with one exact multiply; no binary16 subnormal is
-// ever formed.
-__device__ __forceinline__ uint32_t e4m3_to_f16_bits(uint32_t s) {
-  if (s & 0x78u) return (s << 7) + 0x2000u;
-  _Float16 v = (_Float16)(float)s * (_Float16)0x1p-9f;
-  return (uint32_t)__builtin_bit_cast(uint16_t, v);
-}
-
 // 8 E2M1 codes (one dword) times the group scale -> 8 exact binary16 values.
 // The hardware conversion yields the E2M1 values themselves (its scale
 // operand only applies a power of two, so it is left at 1); one packed
-// binary16 multiply per pair applies the E4M3 group scale exactly.
+// binary16 multiply per pair applies the E4M3 group scale exactly.  With
+// sigma_pair below, checked for every (scale byte, code) pair against the
+// oracle's decoded values in tests/test_gpu_codecs.py.
 __device__ __forceinline__ half8_t dequant8(uint32_t codes, _Float16 sigma) {
   const half2_t s = {sigma, sigma};
   half2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s;

@@ -82,8 +82,10 @@ __global__ __launch_bounds__(kQThreads) void amax_kernel(const uint4* __restrict
 }
 
 // Reduce the partial maxima of a record; every thread gets amax's bits.
+// The count is clamped to the record's capacity: a record that no amax pass
+// wrote (a caller's mistake) then gives a wrong scale, not reads past it.
 __device__ __forceinline__ uint32_t reduce_parts(const mq_scale_rec* __restrict__ rec, uint32_t* sh) {
-  const uint32_t n = rec->nparts;
+  const uint32_t n = min(rec->nparts, (uint32_t)MQ_AMAX_PARTS);
   uint32_t m = 0;
   for (uint32_t j = threadIdx.x; j < n; j += kQThreads) {
     uint32_t v = rec->part[j];
@@ -103,7 +105,7 @@ struct RecHead {
 __device__ __forceinline__ RecHead load_rec_head(const mq_scale_rec* __restrict__ rec) {
   RecHead r;
   r.s_t = rec->s_t;
-  r.n = rec->nparts;
+  r.n = min(rec->nparts, (uint32_t)MQ_AMAX_PARTS);  // clamped as in reduce_parts
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int j = threadIdx.x + i * kQThreads;

@@ -107,9 +107,11 @@ typedef struct mq_scale_rec {
 } mq_scale_rec;
 
 /* An NVFP4 matrix of [rows][cols] elements.  HOST struct of DEVICE pointers.
- * codes  uint8 [rows][cols/2]  (8-byte aligned)
- * scales uint8 [rows][cols/16] (any alignment)
- * rec    mq_scale_rec          (16-byte aligned) */
+ * codes  uint8 [rows][cols/2]  (16-byte aligned)
+ * scales uint8 [rows][cols/16] (8-byte aligned)
+ * rec    mq_scale_rec          (16-byte aligned)
+ * Every entry point checks these alignments and returns MQ_ERR_ALIGN
+ * otherwise. */
 typedef struct mq_nvfp4 {
   uint8_t* codes;
   uint8_t* scales;
