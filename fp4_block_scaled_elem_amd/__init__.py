@@ -119,6 +119,15 @@ def lib():
     L.mq_last_error.restype = ctypes.c_char_p
     L.mq_version.argtypes = []
     L.mq_version.restype = ctypes.c_char_p
+    # test support (not declared in include/mq.h)
+    L.mq_check_codec_steps.argtypes = [ctypes.c_int32, u32, u32, vp, u32, vp]
+    L.mq_check_codec_steps.restype = ctypes.c_int32
+    L.mq_check_dequant_table.argtypes = [vp, vp]
+    L.mq_check_dequant_table.restype = ctypes.c_int32
+    L.mq_check_mfma_rate.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp, vp]
+    L.mq_check_mfma_rate.restype = ctypes.c_int32
+    L.mq_check_wall_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int32)]
+    L.mq_check_wall_clock_khz.restype = ctypes.c_int32
     _lib = L
     return L
 
@@ -406,6 +415,42 @@ def prefill_linear(x_bf16, w: NVFP4, out=None, fused: bool = False, rec=None, ke
         a = quantize(x_bf16, stream)
         mq_gemm_nvfp4_prefill(a, None, w, y, 0, stream)
     return y
+
+
+def mq_check_codec_steps(which: int, lo: int, hi: int, out, stream=None):
+    """Test support: the steps of conversion `which` (0: element code, 1:
+    E4M3 scale byte) over binary32 patterns lo..hi into `out` (int32 device
+    tensor of 1 + 2 * cap entries; out[0] = number of steps)."""
+    cap = (out.numel() - 1) // 2
+    _check(lib().mq_check_codec_steps(which, lo, hi, _dev_ptr(out, "out"), cap, _stream_ptr(stream)),
+           "mq_check_codec_steps")
+
+
+def mq_check_dequant_table(out, stream=None):
+    """Test support: binary16 operand bits of every (scale byte, code) pair
+    into `out` (int16 device tensor [128][4][16])."""
+    if out.numel() != 128 * 4 * 16:
+        raise ValueError("out must hold 128 x 4 x 16 entries")
+    _check(lib().mq_check_dequant_table(_dev_ptr(out, "out"), _stream_ptr(stream)), "mq_check_dequant_table")
+
+
+def mq_check_mfma_rate(valu_per_mfma: int, iters: int, blocks: int, sink, clocks, stream=None):
+    """Measurement support: one launch of the fp16 MFMA rate kernel (0, 4 or
+    6 VALU instructions per MFMA; `blocks` workgroups of four waves, each
+    wave iters x 32 MFMAs of 32x32x16).  sink: float32 device tensor
+    [blocks * 256]; clocks: int64 device tensor [blocks][4] (s_memtime and
+    s_memrealtime at the start and the end of each block's first wave)."""
+    if sink.numel() < blocks * 256 or clocks.numel() < blocks * 4:
+        raise ValueError("sink or clocks too small")
+    _check(lib().mq_check_mfma_rate(valu_per_mfma, iters, blocks, _dev_ptr(sink, "sink"),
+                                    _dev_ptr(clocks, "clocks"), _stream_ptr(stream)), "mq_check_mfma_rate")
+
+
+def wall_clock_khz() -> int:
+    """Rate of the constant-rate s_memrealtime counter of the current device."""
+    k = ctypes.c_int32(0)
+    _check(lib().mq_check_wall_clock_khz(ctypes.byref(k)), "mq_check_wall_clock_khz")
+    return int(k.value)
 
 
 def decode_linear(x_bf16, w_bf16, out=None, stream=None):
