@@ -47,12 +47,13 @@ MQ_SCALE_PARTIALS = 32
 MQ_PATH_DECODE_BF16 = 1
 MQ_PATH_PREFILL_NVFP4 = 2
 MQ_AMAX_PARTS = 1020
+MQ_NOALLOC_MAX_ELEMS = 1 << 26
 MQ_MAX_GROUP = 4
 REC_BYTES = 16 + 4 * MQ_AMAX_PARTS  # sizeof(mq_scale_rec) = 4096
 
 EXPORTS = ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemm_nvfp4_prefill_grouped",
            "mq_gemv_bf16_decode", "mq_gemv_bf16_decode_grouped", "mq_gemv_nvfp4_decode", "mq_rmsnorm_amax", "mq_swiglu_amax", "mq_linear_path", "mq_linear_prepare", "mq_linear_forward",
-           "mq_status_str", "mq_last_error", "mq_version")
+           "mq_gemm_nvfp4_prefill_fused_noalloc", "mq_status_str", "mq_last_error", "mq_version")
 
 
 class LibraryNotBuilt(ImportError):
@@ -113,6 +114,8 @@ def lib():
     L.mq_linear_prepare.restype = ctypes.c_int32
     L.mq_linear_forward.argtypes = [LP, vp, i64, P, vp, u32, vp]
     L.mq_linear_forward.restype = ctypes.c_int32
+    L.mq_gemm_nvfp4_prefill_fused_noalloc.argtypes = [vp, P, vp, i64, i64, i64, u32, vp]
+    L.mq_gemm_nvfp4_prefill_fused_noalloc.restype = ctypes.c_int32
     L.mq_status_str.argtypes = [ctypes.c_int32]
     L.mq_status_str.restype = ctypes.c_char_p
     L.mq_last_error.argtypes = []
@@ -256,6 +259,25 @@ def mq_gemm_nvfp4_prefill_grouped(a: NVFP4, a_bf16, ws, cs, flags: int = 0, stre
     _check(lib().mq_gemm_nvfp4_prefill_grouped(ctypes.byref(ac), _dev_ptr(a_bf16, "a_bf16"), n, wc, cp, nn,
                                                M, K, flags, _stream_ptr(stream)),
            "mq_gemm_nvfp4_prefill_grouped")
+
+
+def mq_gemm_nvfp4_prefill_fused_noalloc(a_bf16, w: NVFP4, c, flags: int = 0, stream=None):
+    """C = NVFP4(a_bf16) . W^T with the activation quantized inside the GEMM
+    into the library's own scratch buffer (no caller buffers, nothing
+    allocated; M * K <= MQ_NOALLOC_MAX_ELEMS).  Same output as
+    mq_gemm_nvfp4_prefill with MQ_A_FUSED_BF16 and caller-owned buffers."""
+    import torch
+    N, K = w.shape
+    if a_bf16.dtype != torch.bfloat16 or a_bf16.dim() != 2 or a_bf16.shape[1] != K:
+        raise ValueError("a_bf16 must be bfloat16 [M][K]")
+    M = a_bf16.shape[0]
+    want = torch.float32 if flags & MQ_OUT_F32 else torch.bfloat16
+    if c.dtype != want or tuple(c.shape) != (M, N):
+        raise ValueError(f"c must be {want} [{M}][{N}]")
+    wc = w._c()
+    _check(lib().mq_gemm_nvfp4_prefill_fused_noalloc(_dev_ptr(a_bf16, "a_bf16"), ctypes.byref(wc), _dev_ptr(c, "c"),
+                                                     M, N, K, flags, _stream_ptr(stream)),
+           "mq_gemm_nvfp4_prefill_fused_noalloc")
 
 
 def mq_gemv_bf16_decode(x_bf16, w_bf16, y_bf16, flags: int = 0, stream=None):

@@ -354,3 +354,64 @@ mq_status mq_linear_forward(const mq_linear* L, const void* x_bf16, int64_t M, c
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------ allocation-free call --
+//
+// Scratch for the quantized activation of mq_gemm_nvfp4_prefill_fused_noalloc:
+// one scale record, then A's codes and scale bytes, at fixed 256-byte
+// aligned offsets.  It is a module global: each device the library runs on
+// holds its own copy, for the life of the process.  In host code `scratch`
+// names a host-side stand-in, never the device memory: the device address
+// comes from hipGetSymbolAddress, once per device, and only that address is
+// handed to kernels.
+
+namespace {
+
+constexpr size_t kScratchRec = 0;
+constexpr size_t kScratchCodes = 4096;
+constexpr size_t kScratchScales = kScratchCodes + (size_t)MQ_NOALLOC_MAX_ELEMS / 2;
+constexpr size_t kScratchBytes = kScratchScales + (size_t)MQ_NOALLOC_MAX_ELEMS / 16;
+static_assert(sizeof(mq_scale_rec) <= kScratchCodes - kScratchRec, "record slot");
+static_assert(kScratchScales % 256 == 0 && kScratchBytes % 256 == 0, "scratch layout");
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+uint8_t* g_scratch[64] = {};  // device address of `scratch`, per device (under g_dev_mu)
+
+mq_status scratch_address(int device, uint8_t*& out) {
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (!g_scratch[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(MQ_ERR_DEVICE, "device %d: no address for the scratch buffer (%s)", device, hipGetErrorString(e));
+    }
+    g_scratch[device] = (uint8_t*)p;
+  }
+  out = g_scratch[device];
+  return MQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mq_status mq_gemm_nvfp4_prefill_fused_noalloc(const void* a_bf16, const mq_nvfp4* w, void* c, int64_t M,
+                                              int64_t N, int64_t K, uint32_t flags, void* hip_stream) {
+  if (flags & ~(MQ_OUT_F32 | MQ_A_FUSED_BF16)) return fail(MQ_ERR_INVALID, "unknown or unsupported flags 0x%x", flags);
+  if (!a_bf16 || !w || !c) return fail(MQ_ERR_INVALID, "a_bf16, w and c must not be NULL");
+  if (mq_status s = check_dims(M, K, "M", "K")) return s;
+  if (K % 16) return fail(MQ_ERR_SHAPE, "K=%lld is not a multiple of 16", (long long)K);
+  if (M * K > (int64_t)MQ_NOALLOC_MAX_ELEMS)
+    return fail(MQ_ERR_SHAPE, "M*K=%lld exceeds the scratch buffer's %lld elements", (long long)(M * K),
+                (long long)MQ_NOALLOC_MAX_ELEMS);
+  mq::DeviceInfo dev;
+  if (mq_status s = current_device(dev)) return s;
+  uint8_t* base = nullptr;
+  if (mq_status s = scratch_address(dev.device, base)) return s;
+  const mq_nvfp4 a{base + kScratchCodes, base + kScratchScales, (mq_scale_rec*)(base + kScratchRec)};
+  return mq_gemm_nvfp4_prefill(&a, a_bf16, w, c, M, N, K, flags | MQ_A_FUSED_BF16, hip_stream);
+}
+
+}  // extern "C"

@@ -378,6 +378,35 @@ mq_status mq_linear_forward(const mq_linear* L, const void* x_bf16, int64_t M,
                             const mq_nvfp4* a_work, void* y_bf16,
                             uint32_t flags, void* hip_stream);
 
+/*
+ * mq_gemm_nvfp4_prefill_fused_noalloc - mq_gemm_nvfp4_prefill with
+ *   MQ_A_FUSED_BF16 for callers that cannot allocate device memory (code
+ *   under HIP graph capture, tight serving loops, harnesses that forbid
+ *   hipMalloc): the activation's scale record and its NVFP4 copy live in a
+ *   scratch buffer inside the library instead of caller buffers.  Same
+ *   kernels and the same output, bit for bit, as
+ *     mq_gemm_nvfp4_prefill(&a, a_bf16, w, c, M, N, K,
+ *                           flags | MQ_A_FUSED_BF16, hip_stream)
+ *   with a = caller-owned codes [M][K/2], scales [M][K/16] and a record.
+ * a_bf16   DEVICE bf16 [M][K], 16-byte aligned.
+ * w, c, N  as for mq_gemm_nvfp4_prefill.
+ * M, K     M >= 1; K >= 16, K % 16 == 0; M * K <= MQ_NOALLOC_MAX_ELEMS,
+ *          else MQ_ERR_SHAPE.
+ * flags    MQ_OUT_BF16 or MQ_OUT_F32 (MQ_A_FUSED_BF16 is implied; the
+ *          tensor scale is always dynamic).
+ * The scratch buffer (MQ_NOALLOC_MAX_ELEMS * 9/16 bytes + 4 KB) is allocated
+ * by the HIP runtime when the library's code is loaded on a device and held
+ * until the process ends; the call itself allocates nothing.  Every call on
+ * one device shares that device's buffer: calls that may run at the same
+ * time on one device (different streams, or different threads without
+ * ordering) race on it and must not be made.  Nothing in it needs clearing:
+ * every byte a call reads was written earlier in the same call.
+ */
+#define MQ_NOALLOC_MAX_ELEMS 67108864 /* 2^26 */
+mq_status mq_gemm_nvfp4_prefill_fused_noalloc(const void* a_bf16, const mq_nvfp4* w,
+                                              void* c, int64_t M, int64_t N, int64_t K,
+                                              uint32_t flags, void* hip_stream);
+
 /* Static string naming a status code. */
 const char* mq_status_str(mq_status s);
 

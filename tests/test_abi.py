@@ -293,6 +293,21 @@ def _no_gpu():
 
 
 @pytest.mark.skipif(not _no_gpu(), reason="valid fake pointers would be launched on a real GPU")
+def test_noalloc_gemm_argument_errors(L):
+    f = L.mq_gemm_nvfp4_prefill_fused_noalloc
+    w = _q(P16, P16, P16)
+    assert f(None, w, P16, 4, 16, 16, 0, None) == mq.MQ_ERR_INVALID
+    assert f(P16, None, P16, 4, 16, 16, 0, None) == mq.MQ_ERR_INVALID
+    assert f(P16, w, None, 4, 16, 16, 0, None) == mq.MQ_ERR_INVALID
+    for flags in (mq.MQ_SCALE_GIVEN, mq.MQ_SCALE_PARTIALS, 64):
+        assert f(P16, w, P16, 4, 16, 16, flags, None) == mq.MQ_ERR_INVALID
+    assert f(P16, w, P16, 0, 16, 16, 0, None) == mq.MQ_ERR_SHAPE
+    assert f(P16, w, P16, 4, 16, 24, 0, None) == mq.MQ_ERR_SHAPE
+    # one row past the scratch buffer's capacity
+    assert f(P16, w, P16, mq.MQ_NOALLOC_MAX_ELEMS // 4096 + 1, 16, 4096, 0, None) == mq.MQ_ERR_SHAPE
+    assert "scratch" in mq.last_error()
+
+
 def test_valid_arguments_without_a_gpu_report_device_error(L):
     assert L.mq_quantize_nvfp4(P16, 4, 16, _q(P16, P16, P16), 0, None) == mq.MQ_ERR_DEVICE
     assert L.mq_gemm_nvfp4_prefill(_q(P16, P16, P16), None, _q(P16, P16, P16), P16, 4, 4, 16, 0,
