@@ -69,6 +69,9 @@ def parse():
                    help="only the decoder-layer prefill context measurement (NVFP4 vs BF16 linears)")
     p.add_argument("--decode-only", action="store_true",
                    help="only measure the BF16 decode GEMV at the decode shapes (one JSON line, not the step metric)")
+    p.add_argument("--peak", action="store_true",
+                   help="only measure the fp16 MFMA rate the chip sustains (MFMA only, and with 4 and 6 VALU "
+                        "instructions per MFMA as the GEMM's dequantization issues) and the clock it holds")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB) three "
                         "times, as the reference for scaling HBM byte counters")
@@ -85,6 +88,47 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration": {"bytes_read": 1 << 30, "bytes_written": 1 << 30, "launches": 3,
                                            "kernel": "torch.neg (elementwise, bf16)"}}), flush=True)
+
+
+def mfma_peak(reps=5, iters=20000, warm=10):
+    """The fp16 MFMA rate of the GEMM's register-resident inner loop (4x4
+    fragments of v_mfma_f32_32x32x16_f16 per wave, one wave per SIMD on
+    every CU, no memory traffic) with 0, 4 and 6 VALU instructions per MFMA:
+    median TFLOP/s over `reps` event-timed launches, and the clock the SIMDs
+    ran at, from each block's shader-clock and constant-rate counters
+    (s_memtime / s_memrealtime) over its run; `warm` untimed launches of each
+    variant come first (the clock ramps up over the first ~0.1 s of load).  The datasheet peak assumes
+    2.4 GHz; `peak_at_clock` is what 256 CUs x 4 SIMDs x 1024 flop/cycle give
+    at the measured clock, and `mfma_busy` the achieved share of it."""
+    import statistics
+    import torch
+    import fp4_block_scaled_elem_amd as mq
+    blocks = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros((blocks, 4), dtype=torch.int64, device="cuda")
+    khz = mq.wall_clock_khz()
+    flops = blocks * 4 * iters * 32 * 32768
+    res = {"datasheet_tflops": PEAK_F16_MFMA_TFLOPS, "cus": blocks, "wall_clock_khz": khz}
+    for v in (0, 4, 6):
+        for _ in range(warm):
+            mq.mq_check_mfma_rate(v, iters, blocks, sink, clocks)
+        ts, mhz = [], []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            mq.mq_check_mfma_rate(v, iters, blocks, sink, clocks)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+            c = clocks.cpu().numpy().astype("float64")
+            mhz.append(float(((c[:, 2] - c[:, 0]) / (c[:, 3] - c[:, 1])).mean() * khz / 1e3))
+        t = statistics.median(ts)
+        f = statistics.median(mhz)
+        at_clock = blocks * 4 * 1024 * f * 1e6 / 1e12
+        res[f"valu_per_mfma_{v}"] = {"tflops": round(flops / t / 1e12, 1), "ms": round(t * 1e3, 3),
+                                     "clock_mhz": round(f, 1), "peak_at_clock_tflops": round(at_clock, 1),
+                                     "mfma_busy": round(flops / t / 1e12 / at_clock, 4)}
+    return res
 
 
 def dev_bf16(bits):
@@ -113,6 +157,107 @@ def setup(cfg_id):
            for p in cfg.projs}
     torch.cuda.synchronize()
     return cfg, acts_host, acts, wdev, qw, qa, fa, out
+
+
+def setup_device(cfg_id, seed=0):
+    """Like setup(), but every input is drawn on the GPU with torch's seeded
+    generator (same shapes and distributions as the configuration's recipe:
+    normal or unit-variance Student-t activations with the stated share of
+    outlier columns, normal weights; not the bit patterns workloads.py
+    draws).  For the timing-only legs of the default run, where drawing the
+    long-context and 70B-slice tensors on the host would take minutes."""
+    import torch
+    import fp4_block_scaled_elem_amd as mq
+    import workloads
+    cfg = workloads.CONFIGS[cfg_id]
+    M = cfg.M[0]
+    gen = torch.Generator(device="cuda").manual_seed(10_000 * cfg_id + seed)
+
+    def draw(rows, cols, dist):
+        if dist.kind == "normal":
+            x = torch.randn((rows, cols), generator=gen, device="cuda")
+        else:  # Student-t: normal / sqrt(chi2_df / df), scaled to unit variance
+            z = torch.randn((rows, cols), generator=gen, device="cuda")
+            chi2 = torch._standard_gamma(torch.full((rows, cols), dist.df / 2.0, device="cuda"), generator=gen) * 2.0
+            x = z / torch.sqrt(chi2 / dist.df) * ((dist.df - 2.0) / dist.df) ** 0.5
+            del z, chi2
+        x *= dist.std
+        if dist.outlier_frac > 0:
+            n = int(round(dist.outlier_frac * cols))
+            idx = torch.randperm(cols, generator=gen, device="cuda")[:n]
+            x[:, idx] *= dist.outlier_factor
+        return x.to(torch.bfloat16)
+
+    acts = {a: draw(M, cfg.layer.act_k(a), cfg.act) for a in workloads.ACTS}
+    qw, wdev = {}, {}
+    for p in cfg.projs:
+        n, k = cfg.layer.proj_nk(p)
+        wdev[p] = draw(n, k, cfg.weight)
+        qw[p] = mq.quantize(wdev[p])
+    qa = {a: mq.NVFP4.empty(*acts[a].shape) for a in workloads.ACTS}
+    fa = {p: mq.NVFP4(None, None, torch.zeros(mq.REC_BYTES // 4, dtype=torch.int32, device="cuda"))
+          for p in cfg.projs}
+    out = {p: torch.empty((M, cfg.layer.proj_nk(p)[0]), dtype=torch.bfloat16, device="cuda")
+           for p in cfg.projs}
+    torch.cuda.synchronize()
+    return cfg, None, acts, wdev, qw, qa, fa, out
+
+
+def config_step_rate(cfg_id, steps, warmup, fused_form="panel"):
+    """Whole-step TFLOP/s of another prefill configuration (the long-context
+    M=32768 step with quantization fused into every GEMM, or the 70B-shaped
+    slice at M=16384), on device-drawn inputs, timed like the headline: W
+    untimed steps, then K steps between two synchronisations."""
+    import torch
+    import workloads
+    cfg, _, acts, wdev, qw, qa, fa, out = setup_device(cfg_id)
+    if cfg.fused_act_quant and fused_form == "panel":
+        fa = {p: qa[workloads.PROJ_INPUT[p]] for p in cfg.projs}
+    plan = launch_plan(cfg, "grouped")
+    for _ in range(warmup):
+        run_step(cfg, plan, acts, qw, qa, fa, out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run_step(cfg, plan, acts, qw, qa, fa, out)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    flops = cfg.flops()
+    res = {"workload": cfg.name, "M": cfg.M[0], "inputs": "drawn on the GPU (torch generator)",
+           "act_quant": f"fused-{fused_form}" if cfg.fused_act_quant else "separate",
+           "tflops": round(flops / dt / 1e12, 1), "ms_per_step": round(dt * 1e3, 4),
+           "pct_mfma_peak": round(100.0 * flops / dt / 1e12 / PEAK_F16_MFMA_TFLOPS, 2),
+           "steps": steps, "warmup": warmup}
+    del acts, wdev, qw, qa, fa, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def single_linear_latency(reps=50):
+    """The one-linear configuration (M=128, K=512, N=512, seeded inputs of
+    workloads.py): quantize the activations (amax pass + encode) and run the
+    NVFP4 GEMM, per call, in microseconds -- calls made back to back from
+    Python (eager) and the same calls captured in a HIP graph and replayed
+    (the kernels' own time).  67 MFLOP is far too little work for a
+    throughput figure; this configuration measures launch latency."""
+    import torch
+    import fp4_block_scaled_elem_amd as mq
+    import workloads
+    x = dev_bf16(workloads.activation(1))
+    qw = mq.quantize(dev_bf16(workloads.weight(1)))
+    qa = mq.NVFP4.empty(128, 512)
+    c = torch.empty((128, 512), dtype=torch.bfloat16, device="cuda")
+
+    def call(_):
+        mq.mq_quantize_nvfp4(x, qa)
+        mq.mq_gemm_nvfp4_prefill(qa, None, qw, c)
+
+    med, mn = _median_us(call, reps=reps)
+    g = _graph_us(call, c)
+    flops = 2 * 128 * 512 * 512
+    return {"workload": workloads.CONFIGS[1].name, "launches_per_call": 3, "us_median_eager": round(med, 2),
+            "us_min_eager": round(mn, 2), "us_graph": round(g, 2), "tflops_graph": round(flops / g / 1e6, 2)}
 
 
 # projections launched together (they read the same activation)
@@ -566,15 +711,25 @@ def cpu_baseline(cfg_id, acts_host, rows, wrows):
     """The oracle as it stands, on a bounded sample of the same workload:
     the first ``rows`` tokens of each activation (quantized as a tensor of
     their own) times the first ``wrows`` weight rows of every projection
-    (weights quantized beforehand, untimed, as on the GPU)."""
+    (weights quantized beforehand, untimed, as on the GPU).  The BLAS
+    library that NumPy's float64 matmul calls runs on every host CPU this
+    process may use (len(os.sched_getaffinity(0))); NumPy's elementwise
+    steps are single-threaded."""
     import numpy as np
     import oracle
     import workloads
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas_name = f"{blas.get('name', '?')} {blas.get('version', '')}".strip()
     except Exception:
-        blas = 1
+        blas_name = "unknown"
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
+        used = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        limiter, used = None, 1
     cfg = workloads.CONFIGS[cfg_id]
     wq = {}
     for p in cfg.projs:
@@ -591,10 +746,13 @@ def cpu_baseline(cfg_id, acts_host, rows, wrows):
             c = oracle.gemm_nvfp4_ref(qa, wq[p])
             flops += 2 * c.shape[0] * c.shape[1] * xs.shape[1]
         dt += time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas), "kind": "oracle",
+    if limiter is not None:
+        limiter.restore_original_limits()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(used), "kind": "oracle",
+            "host_cpus": cores, "blas": blas_name,
             "sample": (f"first {min(rows, cfg.M[0])} tokens of each activation x first {wrows} weight rows of each of "
                        f"{len(cfg.projs)} projections ({flops / 1e9:.1f} GFLOP, {dt:.1f} s; NumPy "
-                       f"elementwise steps single-threaded, float64 matmul on {blas} BLAS threads)")}
+                       f"elementwise steps single-threaded, float64 matmul on {used} {blas_name} threads)")}
 
 
 GEMM_SRC = os.path.join(ROOT, "fp4_block_scaled_elem_amd", "csrc", "gemm.hip")
@@ -638,6 +796,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.peak:
+        print(json.dumps({"mfma_peak": mfma_peak()}), flush=True)
+        return
     if args.layer:
         print(json.dumps({"layer_prefill": layer_prefill()}), flush=True)
         return
@@ -653,6 +814,13 @@ def main():
         fa = {p: qa[workloads.PROJ_INPUT[p]] for p in cfg.projs}
     flops = cfg.flops()
     plan = launch_plan(cfg, args.launches)
+
+    # The MFMA rate measurement runs first: about half a second of full MFMA
+    # load, which also brings the chip out of idle clocks before the timed
+    # region (a 20-step timed region right after idle reads about 3% below
+    # the steady state).  torch's BF16 GEMMs run after the timed region, at
+    # the same (warm) state as the NVFP4 step.
+    peak = None if args.no_extras else mfma_peak(reps=3)
 
     for _ in range(args.warmup):
         run_step(cfg, plan, acts, qw, qa, fa, out)
@@ -690,6 +858,17 @@ def main():
     phase = None if args.no_extras else phase_linear_rates()
     producer = None if (args.no_extras or cfg.fused_act_quant) else producer_fused_rates()
     bf16 = None if args.no_bf16 else bf16_reference(cfg, acts, wdev)
+    others = None
+    if not args.no_extras and args.config == 2:
+        # the other configurations, timed after the headline (device-drawn
+        # inputs for the two large ones)
+        del acts, wdev, qw, qa, fa, out
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        others = {"single_linear_m128": single_linear_latency(),
+                  "longctx_m32768_fused": config_step_rate(3, args.steps, args.warmup),
+                  "llama70b_slice_m16384": config_step_rate(5, args.steps, args.warmup),
+                  "layer_prefill_m4096": layer_prefill()}
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.config, acts_host, args.cpu_rows, args.cpu_wrows)
 
     rec = {
@@ -715,7 +894,13 @@ def main():
                      "achieved": round(gemm_tflops, 2),
                      "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / PEAK_F16_MFMA_TFLOPS, 4), "traffic": gemm_traffic(cfg.name),
-                     "launches_per_step": n_gemm, "avg_launch_ms": round(gemm_ms / n_gemm, 4)},
+                     "launches_per_step": n_gemm, "avg_launch_ms": round(gemm_ms / n_gemm, 4),
+                     "peak_measured": None if peak is None else {
+                         "mfma_only_tflops": peak["valu_per_mfma_0"]["tflops"],
+                         "with_dequant_valu_tflops": peak["valu_per_mfma_4"]["tflops"],
+                         "clock_mhz": peak["valu_per_mfma_0"]["clock_mhz"],
+                         "frac_of_mfma_only": round(gemm_tflops / peak["valu_per_mfma_0"]["tflops"], 4),
+                         "frac_of_with_dequant_valu": round(gemm_tflops / peak["valu_per_mfma_4"]["tflops"], 4)}},
         "split_ms": {"gemm": round(gemm_ms, 4), "act_quant_and_gaps": round(rest_ms, 4),
                      "step_with_events": round(ms_step_ev, 4)},
         "per_launch": launches,
@@ -727,6 +912,8 @@ def main():
         "producer_fused_act_quant": producer,
         "bf16_torch_tflops": None if bf16 is None else round(bf16, 2),
         "ratio_vs_bf16_torch": None if bf16 is None else round(value / bf16, 3),
+        "mfma_peak": peak,
+        "other_configs": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
