@@ -19,6 +19,12 @@ roofline's `traffic` field when the GEMM source is unchanged since.
 
     python profile_summary.py --counters <run_dir> <workload-name>
 
+    python profile_summary.py --peak <run_dir>
+
+<run_dir>/peak/ holds a `rocprofv3 --kernel-trace --pmc GRBM_GUI_ACTIVE` run
+of `bench.py --peak`; writes profiles/mfma_peak.txt (rate and clock of the
+fp16 MFMA rate kernel per VALU load).
+
 <run_dir> holds p1/ and p2/, two `rocprofv3 --kernel-trace --pmc ...` runs
 of the same bench.py command with the counter sets COUNTERS_P1 and
 COUNTERS_P2, and commands.txt; writes profiles/counters_<workload>.txt
@@ -53,7 +59,7 @@ def source_hash(path=GEMM_SRC) -> str:
 
 
 def short(name: str) -> str:
-    n = name.split("(")[0].replace("void ", "").replace("mq::", "")
+    n = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").replace("mq::", "")
     return n
 
 
@@ -219,8 +225,41 @@ def counters_main(run: str, workload: str):
     print(path)
 
 
+def peak_main(run: str):
+    """profiles/mfma_peak.txt from a `rocprofv3 --kernel-trace --pmc GRBM_GUI_ACTIVE` run of
+    `bench.py --peak` (the fp16 MFMA rate kernel with 0, 4 and 6 VALU per MFMA)."""
+    rows = collections.defaultdict(list)
+    for n, g, dur, c in dispatches(os.path.join(run, "peak")):
+        if "mfma_peak_kernel" in n:
+            rows[n].append((g, dur, c.get("GRBM_GUI_ACTIVE", 0.0)))
+    commands = open(os.path.join(run, "commands.txt")).read().strip()
+    lines = ["# rocprofv3: fp16 MFMA rate kernel (bench.py --peak)", "",
+             "Commands (run from the repository root on one MI355X):", "", commands,
+             "python3 profile_summary.py --peak <out>", "",
+             "Each launch: one workgroup of four waves per CU, every wave 20000 x 32 v_mfma_f32_32x32x16_f16",
+             "(32768 flop each) on register operands, with 0, 4 or 6 VALU instructions per MFMA (the",
+             "dequantization the prefill GEMM issues is 4).  clock = GRBM_GUI_ACTIVE / 8 XCDs / duration;",
+             f"peak at clock = {N_SIMD} SIMDs x 1024 flop/cycle x clock (the 2.5 PF/s datasheet figure is 2.4 GHz).", "",
+             f"{'kernel':34s} {'calls':>5s} {'avg_us':>9s} {'TFLOP/s':>8s} {'clock_GHz':>9s} {'peak@clk':>9s} {'busy%':>6s}"]
+    for n in sorted(rows):
+        r = rows[n]
+        grid = r[0][0]
+        blocks = grid // 256 if grid >= 256 else grid
+        flops = blocks * 4 * 20000 * 32 * 32768
+        us = sum(x[1] for x in r) / len(r) / 1e3
+        ghz = sum(x[2] / 8 / x[1] for x in r) / len(r)
+        tf = flops / (us * 1e-6) / 1e12
+        at = N_SIMD * 1024 * ghz * 1e9 / 1e12
+        lines.append(f"{n[:34]:34s} {len(r):5d} {us:9.1f} {tf:8.1f} {ghz:9.3f} {at:9.1f} {100 * tf / at:6.1f}")
+    path = os.path.join(ROOT, "profiles", "mfma_peak.txt")
+    open(path, "w").write("\n".join(lines) + "\n")
+    print(path)
+
+
 if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "--counters":
         counters_main(sys.argv[2], sys.argv[3])
+    elif len(sys.argv) > 1 and sys.argv[1] == "--peak":
+        peak_main(sys.argv[2])
     else:
         main()
