@@ -236,11 +236,13 @@ def config_step_rate(cfg_id, steps, warmup, fused_form="panel"):
 
 def single_linear_latency(reps=50):
     """The one-linear configuration (M=128, K=512, N=512, seeded inputs of
-    workloads.py): quantize the activations (amax pass + encode) and run the
-    NVFP4 GEMM, per call, in microseconds -- calls made back to back from
-    Python (eager) and the same calls captured in a HIP graph and replayed
-    (the kernels' own time).  67 MFLOP is far too little work for a
-    throughput figure; this configuration measures launch latency."""
+    workloads.py), per call, in microseconds: quantize the activations
+    (amax pass + encode) and run the NVFP4 GEMM, and the same linear with
+    the quantization fused into the GEMM (one launch, bit-identical output)
+    -- calls made back to back from Python (eager) and the same calls
+    captured in a HIP graph and replayed (the kernels' own time).  67 MFLOP
+    is far too little work for a throughput figure; this configuration
+    measures launch latency."""
     import torch
     import fp4_block_scaled_elem_amd as mq
     import workloads
@@ -255,9 +257,22 @@ def single_linear_latency(reps=50):
 
     med, mn = _median_us(call, reps=reps)
     g = _graph_us(call, c)
+    # the same linear with the quantization inside the GEMM: on an input this
+    # small the GEMM's workgroups also take the maximum, so it is one launch
+    rec = mq.NVFP4(None, None, torch.zeros(mq.REC_BYTES // 4, dtype=torch.int32, device="cuda"))
+    cf = torch.empty_like(c)
+    fused = lambda _: mq.mq_gemm_nvfp4_prefill(rec, x, qw, cf, mq.MQ_A_FUSED_BF16)
+    fmed, fmn = _median_us(fused, reps=reps)
+    fg = _graph_us(fused, cf)
+    torch.cuda.synchronize()
+    if not torch.equal(c.view(torch.int16), cf.view(torch.int16)):
+        raise RuntimeError("fused single-launch linear differs from quantize + GEMM")
     flops = 2 * 128 * 512 * 512
-    return {"workload": workloads.CONFIGS[1].name, "launches_per_call": 3, "us_median_eager": round(med, 2),
-            "us_min_eager": round(mn, 2), "us_graph": round(g, 2), "tflops_graph": round(flops / g / 1e6, 2)}
+    return {"workload": workloads.CONFIGS[1].name,
+            "quantize_then_gemm": {"launches": 3, "us_median_eager": round(med, 2), "us_min_eager": round(mn, 2),
+                                   "us_graph": round(g, 2), "tflops_graph": round(flops / g / 1e6, 2)},
+            "fused_one_launch": {"launches": 1, "us_median_eager": round(fmed, 2), "us_min_eager": round(fmn, 2),
+                                 "us_graph": round(fg, 2), "tflops_graph": round(flops / fg / 1e6, 2)}}
 
 
 # projections launched together (they read the same activation)

@@ -181,12 +181,16 @@ mq_status mq_gemm_nvfp4_prefill_grouped(const mq_nvfp4* a, const void* a_bf16, i
   if (mq_status s = current_device(dev)) return s;
   hipStream_t st = (hipStream_t)hip_stream;
   const bool given = flags & MQ_SCALE_GIVEN;
-  if (fused && !given && !(flags & MQ_SCALE_PARTIALS)) {
+  const bool dynamic = fused && !given && !(flags & MQ_SCALE_PARTIALS);
+  // the per-tile fused form on a small A takes the maximum inside the GEMM
+  const bool inline_amax = dynamic && !a->codes && M * K <= mq::kInlineAmaxElems;
+  if (dynamic && !inline_amax) {
     hipError_t e = mq::launch_amax(a_bf16, M * K, a->rec, dev, st);
     if (e != hipSuccess) return launched(e, "amax");
   }
   const mq::GemmOperandA A{fused ? nullptr : a->codes, fused ? nullptr : a->scales, fused ? a_bf16 : nullptr,
-                           a->rec, given, fused ? a->codes : nullptr, fused ? a->scales : nullptr};
+                           a->rec, given, fused ? a->codes : nullptr, fused ? a->scales : nullptr,
+                           inline_amax};
   return launched(mq::launch_gemm(A, gw, n_group, M, K, flags & MQ_OUT_F32, dev, st), fused ? "gemm_fused" : "gemm");
 }
 

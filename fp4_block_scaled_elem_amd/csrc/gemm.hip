@@ -69,6 +69,7 @@ struct GemmArgs {
   int M, K;
   int tiles_m, tiles_n;      // tiles_n: all groups
   int a_given;               // fused mode: take s_t from a_rec
+  int a_inline;              // fused mode, small A: every workgroup takes max|A| itself
 };
 
 // The group of column tile tn and its operands, selected with constant
@@ -576,17 +577,39 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
 
 // A's tensor scale: from the record, or (REDUCE: the fused prologue without
 // a given scale) reduced from the amax pass's partial maxima by the
-// quantizer's rule, workgroup 0 storing it in the record.
+// quantizer's rule, workgroup 0 storing it in the record.  With a_inline (A
+// small enough that every workgroup reads all of it from L2 in about a
+// microsecond) there is no amax pass: each workgroup takes max|A| itself,
+// the same maximum, so the whole fused GEMM is one launch.
 template <bool REDUCE>
 __device__ __forceinline__ float a_tensor_scale(const GemmArgs& args) {
   if (!REDUCE || args.a_given) return args.a_rec->s_t;
   __shared__ uint32_t red[kThreads / 64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint32_t np = min(args.a_rec->nparts, (uint32_t)MQ_AMAX_PARTS);  // never past the record
   uint32_t m = 0;
-  for (uint32_t j = tid; j < np; j += kThreads) {
-    uint32_t v = args.a_rec->part[j];
-    m = m > v ? m : v;
+  if (args.a_inline) {
+    const uint4* x = (const uint4*)args.a_bf16;
+    const int nvec = args.M * args.K / 8;  // at most 2^14 (host-checked)
+    for (int base = 0; base < nvec; base += 4 * kThreads) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = base + u * kThreads + tid;
+        v[u] = x[i < nvec ? i : nvec - 1];  // a repeated element leaves the maximum unchanged
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        const uint32_t a = bf16_absmax_bits<4>(w) << 16;  // binary32 bits, as the partial maxima
+        m = m > a ? m : a;
+      }
+    }
+  } else {
+    const uint32_t np = min(args.a_rec->nparts, (uint32_t)MQ_AMAX_PARTS);  // never past the record
+    for (uint32_t j = tid; j < np; j += kThreads) {
+      uint32_t v = args.a_rec->part[j];
+      m = m > v ? m : v;
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -968,6 +991,7 @@ hipError_t launch_gemm(const GemmOperandA& A, const GemmWeight* w, int ngroup, i
   GemmArgs a{};
   a.a_codes = A.codes; a.a_scales = A.scales; a.a_bf16 = A.bf16; a.a_rec = A.rec;
   a.a_given = A.given ? 1 : 0;
+  a.a_inline = A.inline_amax ? 1 : 0;
   int64_t n[kMaxGroup];
   for (int g = 0; g < ngroup; ++g) {
     a.w_codes[g] = w[g].codes; a.w_scales[g] = w[g].scales; a.w_rec[g] = w[g].rec;

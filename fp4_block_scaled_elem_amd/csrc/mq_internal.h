@@ -36,7 +36,11 @@ struct GemmOperandA {
   // launch to the quantize-once form; NULL: re-quantize per tile
   uint8_t* out_codes;
   uint8_t* out_scales;
+  // fused per-tile form with a dynamic scale and A of at most
+  // kInlineAmaxElems elements: no amax pass, every workgroup takes max|A|
+  bool inline_amax;
 };
+constexpr int64_t kInlineAmaxElems = (int64_t)1 << 17;
 
 // One weight of a (grouped) GEMM launch and its output C [M][n].
 struct GemmWeight {

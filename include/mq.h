@@ -161,7 +161,10 @@ mq_status mq_quantize_nvfp4(const void* x_bf16, int64_t rows, int64_t cols,
  *          rec->s_t must already hold A's scale, e.g. from
  *          mq_quantize_nvfp4 earlier on the same stream).  With
  *          MQ_A_FUSED_BF16, a->rec receives the amax pass of a_bf16 (or
- *          supplies s_t under MQ_SCALE_GIVEN) and a->codes / a->scales are
+ *          supplies s_t under MQ_SCALE_GIVEN; when a->codes is NULL and
+ *          M*K <= 2^17 there is no amax pass: every workgroup of the GEMM
+ *          takes max|a_bf16| itself, and a->rec receives s_t and amax_bits
+ *          only, so the whole call is one launch) and a->codes / a->scales are
  *          either both NULL (every A tile is re-quantized inside the GEMM's
  *          pipeline for each column tile) or both given, [M][K/2] and
  *          [M][K/16] bytes, 16- and 8-byte aligned: then A's NVFP4 is

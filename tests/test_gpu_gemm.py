@@ -296,3 +296,29 @@ def test_cfg2_grouped_gate_up_sampled():
         ref = oracle.gemm_nvfp4_ref(oa, oracle.quantize_nvfp4(xw, rows=cols))
         got = bf16_dev_to_f64(c[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
         _assert_rule_t(got, ref, True)
+
+
+@pytest.mark.parametrize("M,K", [(256, 512), (128, 1024), (255, 512), (257, 512), (64, 4096)])
+def test_fused_inline_amax_boundary(M, K):
+    # the per-tile fused form takes max|A| inside the GEMM when M*K <= 2^17
+    # (one launch) and runs the amax pass otherwise; the largest magnitude is
+    # planted in the last element, which the in-GEMM maximum must reach; both
+    # sides of the limit must match quantize-then-GEMM bit for bit
+    announce("gemm fused inline amax", M, K)
+    import torch
+    mq = _mq()
+    N = 300
+    xa = workloads.random_bf16((M, K), 71 + M, 1.0, "normal")
+    xa[-1, -1] = workloads.f32_to_bf16_bits(np.array([-1000.0], np.float32))[0]
+    xw = workloads.random_bf16((N, K), 72, 0.02)
+    x = to_dev_bf16(xa)
+    qw = mq.quantize(to_dev_bf16(xw))
+    qa = mq.quantize(x)
+    c_unf = _gemm(qa, qw, M, N, f32=True)
+    c_fus, a = _fused(x, qw, M, N, f32=True)
+    assert torch.equal(c_unf.view(torch.int32), c_fus.view(torch.int32))
+    rec = a.rec.cpu().numpy().view(np.uint32)
+    ref = oracle.quantize_nvfp4(xa)
+    assert int(rec[0]) == int(np.float32(ref.s_t).view(np.uint32))
+    assert int(rec[1]) == int(np.float32(1000.0).view(np.uint32))
+    _assert_rule_t(_out(c_fus), oracle.gemm_nvfp4_ref(ref, oracle.quantize_nvfp4(xw)), False)
