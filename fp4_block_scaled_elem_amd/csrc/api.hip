@@ -127,11 +127,14 @@ mq_status mq_quantize_nvfp4(const void* x_bf16, int64_t rows, int64_t cols, cons
   if (mq_status s = current_device(dev)) return s;
   hipStream_t st = (hipStream_t)hip_stream;
   const bool given = flags & MQ_SCALE_GIVEN;
-  if (!given && !(flags & MQ_SCALE_PARTIALS)) {
+  const bool dynamic = !given && !(flags & MQ_SCALE_PARTIALS);
+  const bool inline_amax = dynamic && rows * cols <= mq::kInlineAmaxElems;
+  if (dynamic && !inline_amax) {
     hipError_t e = mq::launch_amax(x_bf16, rows * cols, out->rec, dev, st);
     if (e != hipSuccess) return launched(e, "amax");
   }
-  return launched(mq::launch_quantize(x_bf16, rows * cols, out->codes, out->scales, out->rec, given, dev, st),
+  return launched(mq::launch_quantize(x_bf16, rows * cols, out->codes, out->scales, out->rec, given, dev, st,
+                                      inline_amax),
                   "quantize");
 }
 

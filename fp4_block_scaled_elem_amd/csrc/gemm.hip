@@ -590,15 +590,15 @@ __device__ __forceinline__ float a_tensor_scale(const GemmArgs& args) {
   if (args.a_inline) {
     const uint4* x = (const uint4*)args.a_bf16;
     const int nvec = args.M * args.K / 8;  // at most 2^14 (host-checked)
-    for (int base = 0; base < nvec; base += 4 * kThreads) {
-      uint4 v[4];
+    for (int base = 0; base < nvec; base += 8 * kThreads) {
+      uint4 v[8];  // eight loads in flight per lane
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int i = base + u * kThreads + tid;
         v[u] = x[i < nvec ? i : nvec - 1];  // a repeated element leaves the maximum unchanged
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
         const uint32_t a = bf16_absmax_bits<4>(w) << 16;  // binary32 bits, as the partial maxima
         m = m > a ? m : a;

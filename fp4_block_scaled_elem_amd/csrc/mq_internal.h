@@ -8,6 +8,11 @@
 
 namespace mq {
 
+// Inputs of at most this many elements take their absolute maximum inside
+// the kernel that needs it (the quantizer, or the fused GEMM's per-tile
+// form) instead of a separate amax pass: one launch fewer.
+constexpr int64_t kInlineAmaxElems = (int64_t)1 << 17;
+
 struct DeviceInfo {
   int device = -1;
   int num_cu = 0;
@@ -22,8 +27,11 @@ void log_launch(const char* kernel, unsigned grid, unsigned block, size_t lds, c
 
 hipError_t launch_amax(const void* x_bf16, int64_t nelem, mq_scale_rec* rec, const DeviceInfo& dev,
                        hipStream_t stream);
+// inline_amax (dynamic scale, nelem <= kInlineAmaxElems): no amax pass
+// before it; every workgroup takes max|x| itself.
 hipError_t launch_quantize(const void* x_bf16, int64_t nelem, uint8_t* codes, uint8_t* scales,
-                           mq_scale_rec* rec, bool given, const DeviceInfo& dev, hipStream_t stream);
+                           mq_scale_rec* rec, bool given, const DeviceInfo& dev, hipStream_t stream,
+                           bool inline_amax = false);
 // A operand of a GEMM launch: packed (codes, scales) or, fused, bf16 values
 // quantized in the kernel (rec then receives or, when given, supplies s_t).
 struct GemmOperandA {
@@ -40,7 +48,7 @@ struct GemmOperandA {
   // kInlineAmaxElems elements: no amax pass, every workgroup takes max|A|
   bool inline_amax;
 };
-constexpr int64_t kInlineAmaxElems = (int64_t)1 << 17;
+
 
 // One weight of a (grouped) GEMM launch and its output C [M][n].
 struct GemmWeight {

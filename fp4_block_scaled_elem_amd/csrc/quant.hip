@@ -131,6 +131,8 @@ __device__ __forceinline__ uint32_t reduce_rec_head(const RecHead& r, const mq_s
 // One lane owns 8 consecutive elements (one 16-byte load); the two lanes of a
 // 16-element group swap their half maxima.  Each lane works on four
 // half-groups per iteration, one stride apart, so four loads are in flight.
+// given: 0 = s_t from the amax pass's partial maxima in rec, 1 = rec->s_t as
+// set by the caller, 2 = every workgroup takes max|x| itself (small inputs).
 __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __restrict__ x, int64_t nhalf,
                                                              uint32_t* __restrict__ codes,
                                                              uint8_t* __restrict__ scales,
@@ -154,10 +156,31 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
     v[u] = ld_stream(&x[i < nhalf ? i : nhalf - 1]);
   }
   float s_t;
-  if (given) {
+  if (given == 1) {
     s_t = head.s_t;
   } else {
-    uint32_t amax = reduce_rec_head(head, rec, sh);
+    uint32_t amax;
+    if (given == 2) {
+      // small input, no amax pass: every workgroup takes max|x| itself (the
+      // same value), reading all of x, which stays in L2
+      uint32_t m = 0;
+      for (int64_t base = 0; base < nhalf; base += 8 * kQThreads) {
+        uint4 t[8];  // eight loads in flight per lane
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t i = base + u * kQThreads + threadIdx.x;
+          t[u] = x[i < nhalf ? i : nhalf - 1];  // a repeated element leaves the maximum unchanged
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t a = uint4_absmax(t[u]);
+          m = m > a ? m : a;
+        }
+      }
+      amax = block_max_u32(m, sh) << 16;  // binary32 bits, as the partial maxima
+    } else {
+      amax = reduce_rec_head(head, rec, sh);
+    }
     s_t = tensor_scale_from_amax(amax);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
       rec->s_t = s_t;
@@ -233,12 +256,14 @@ hipError_t launch_amax(const void* x_bf16, int64_t nelem, mq_scale_rec* rec, con
 }
 
 hipError_t launch_quantize(const void* x_bf16, int64_t nelem, uint8_t* codes, uint8_t* scales,
-                           mq_scale_rec* rec, bool given, const DeviceInfo& dev, hipStream_t stream) {
+                           mq_scale_rec* rec, bool given, const DeviceInfo& dev, hipStream_t stream,
+                           bool inline_amax) {
   const int64_t nhalf = nelem / 8;  // 8 elements per lane, two lanes per group
   int blocks = grid_for((nhalf + 3) / 4, kQThreads, dev.num_cu * 8);
-  log_launch("quantize_kernel", blocks, kQThreads, 0, "elements=%lld given=%d", (long long)nelem, (int)given);
+  const int mode = given ? 1 : (inline_amax ? 2 : 0);
+  log_launch("quantize_kernel", blocks, kQThreads, 0, "elements=%lld mode=%d", (long long)nelem, mode);
   hipLaunchKernelGGL(quantize_kernel, dim3(blocks), dim3(kQThreads), 0, stream,
-                     (const uint4*)x_bf16, nhalf, (uint32_t*)codes, scales, rec, given ? 1 : 0);
+                     (const uint4*)x_bf16, nhalf, (uint32_t*)codes, scales, rec, mode);
   return hipGetLastError();
 }
 

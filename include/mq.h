@@ -144,7 +144,10 @@ typedef struct mq_nvfp4 {
  * flags    MQ_SCALE_DYNAMIC, MQ_SCALE_GIVEN or MQ_SCALE_PARTIALS (out->rec's
  *          nparts and part[] already hold x's partial maxima from a producer
  *          op: s_t is derived from them, bit-identical to the dynamic case).
- * Launches: an amax pass (dynamic only), then the quantizer.
+ * Launches: an amax pass (dynamic only), then the quantizer; for
+ *          rows*cols <= 2^17 (dynamic) the quantizer alone, every workgroup
+ *          taking max|x| itself (out->rec then receives s_t and amax_bits,
+ *          not nparts / part[]).
  */
 mq_status mq_quantize_nvfp4(const void* x_bf16, int64_t rows, int64_t cols,
                             const mq_nvfp4* out, uint32_t flags,

@@ -320,5 +320,5 @@ def test_fused_inline_amax_boundary(M, K):
     rec = a.rec.cpu().numpy().view(np.uint32)
     ref = oracle.quantize_nvfp4(xa)
     assert int(rec[0]) == int(np.float32(ref.s_t).view(np.uint32))
-    assert int(rec[1]) == int(np.float32(1000.0).view(np.uint32))
+    assert int(rec[1]) == (int(xa[-1, -1]) & 0x7FFF) << 16
     _assert_rule_t(_out(c_fus), oracle.gemm_nvfp4_ref(ref, oracle.quantize_nvfp4(xw)), False)

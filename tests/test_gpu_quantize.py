@@ -131,3 +131,23 @@ def test_large_activation_sampled_rows(cfg, act):
     rows = np.random.default_rng(cfg).choice(bits.shape[0], 128, replace=False)
     rows = np.concatenate([rows, [0, bits.shape[0] - 1]])
     _check(bits, rows=rows)
+
+
+@pytest.mark.parametrize("rows,cols", [(256, 512), (1, 16), (8, 4096), (257, 512), (32, 4112)])
+def test_inline_amax_boundary(rows, cols):
+    # inputs of at most 2^17 elements are quantized in one launch, every
+    # workgroup taking max|x| itself; larger ones run the amax pass first.
+    # The largest magnitude sits in the last element; both sides of the
+    # limit must equal the oracle byte for byte.
+    announce("quantize inline amax", rows, cols)
+    import torch
+    mq = _mq()
+    x = workloads.random_bf16((rows, cols), 81 + rows, 1.0, "normal")
+    x[-1, -1] = workloads.f32_to_bf16_bits(np.array([3.0e4], np.float32))[0]
+    q = mq.quantize(to_dev_bf16(x))
+    torch.cuda.synchronize()
+    ref = oracle.quantize_nvfp4(x)
+    codes, scales, st = quantized_host(q)
+    assert st == int(np.float32(ref.s_t).view(np.uint32))
+    assert int(q.rec[1:2].cpu().numpy().view(np.uint32)[0]) == (int(x[-1, -1]) & 0x7FFF) << 16
+    assert np.array_equal(scales, ref.scales) and np.array_equal(codes, ref.codes)
