@@ -43,8 +43,12 @@ def test_log_lists_every_launch():
     announce("MQ_LOG=1")
     lines = _run({"MQ_LOG": "1"})
     kernels = [line.split()[1] for line in lines]
-    # weight and activation quantization (amax + encode each), the GEMM, the GEMV
-    assert kernels.count("amax_kernel") == 2 and kernels.count("quantize_kernel") == 2, lines
+    # weight quantization (300 x 512: amax pass + encode), activation
+    # quantization (40 x 512, at most 2^17 elements: the encode kernel takes
+    # the maximum itself, one launch), the GEMM, the GEMV
+    assert kernels.count("amax_kernel") == 1 and kernels.count("quantize_kernel") == 2, lines
+    quant = [line for line in lines if " quantize_kernel " in line]
+    assert "elements=153600 mode=0" in quant[0] and "elements=20480 mode=2" in quant[1], quant
     assert kernels.count("gemm_nvfp4_kernel") == 1 and kernels.count("gemv_bf16_kernel") == 1, lines
     gemm = next(line for line in lines if " gemm_nvfp4_kernel " in line)
     assert "M=40 K=512" in gemm and "grid=" in gemm and "lds=" in gemm
