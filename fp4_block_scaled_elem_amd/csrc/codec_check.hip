@@ -75,7 +75,7 @@ __global__ void init_counter_kernel(uint32_t* out) { out[0] = 0u; }
 __global__ void dequant_table_kernel(uint16_t* __restrict__ out) {
   const uint32_t S = threadIdx.x;
   const uint32_t dword = S * 0x01010101u;
-  const half2_t s01 = sigma_pair(dword, 0x010C000Cu), s23 = sigma_pair(dword, 0x030C020Cu);
+  const half2_t s01 = sigma_pair<false>(dword), s23 = sigma_pair<true>(dword);
   const _Float16 sig[4] = {s01[0], s01[1], s23[0], s23[1]};
 #pragma unroll
   for (int k = 0; k < 4; ++k) {

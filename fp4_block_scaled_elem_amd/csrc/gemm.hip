@@ -409,13 +409,13 @@ struct WavePipe {
   __device__ __forceinline__ void sigmas() {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      pa[0][i] = sigma_pair(sa[i], 0x010C000Cu);
-      pa[1][i] = sigma_pair(sa[i], 0x030C020Cu);
+      pa[0][i] = sigma_pair<false>(sa[i]);
+      pa[1][i] = sigma_pair<true>(sa[i]);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      pw[0][j] = sigma_pair(sw[j], 0x010C000Cu);
-      pw[1][j] = sigma_pair(sw[j], 0x030C020Cu);
+      pw[0][j] = sigma_pair<false>(sw[j]);
+      pw[1][j] = sigma_pair<true>(sw[j]);
     }
   }
   // operands of step S into operand buffer B
@@ -467,7 +467,7 @@ __device__ __forceinline__ void run_step(WavePipe<BM, BN>& p, f32x16_t (&acc)[BM
   if (S < 7) p.template dequant<(S + 1) & 7, (S + 1) & 1>();
   else p.template dequant<0, 0>();
   p.template mfma<S & 1>(acc);
-  interleave<NM, ND + (S == 7 ? 6 * (TM + TN) : 0)>();
+  interleave<NM, ND + (S == 7 ? 2 * (TM + TN) : 0)>();
   fill(S);
 }
 

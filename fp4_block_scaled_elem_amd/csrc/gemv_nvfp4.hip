@@ -112,12 +112,12 @@ __global__ __launch_bounds__(kGnWaves * 64) void gemv_nvfp4_kernel(
   };
   auto compute = [&](const GnFrag& fw, const GnFrag (&fx)[MT], bool live) __attribute__((always_inline)) {
     const uint32_t wsc = live ? fw.s : 0u;
-    const half2_t sw01 = sigma_pair(wsc, 0x010C000Cu), sw23 = sigma_pair(wsc, 0x030C020Cu);
+    const half2_t sw01 = sigma_pair<false>(wsc), sw23 = sigma_pair<true>(wsc);
     half2_t sx01[MT], sx23[MT];
 #pragma unroll
     for (int u = 0; u < MT; ++u) {
-      sx01[u] = sigma_pair(fx[u].s, 0x010C000Cu);
-      sx23[u] = sigma_pair(fx[u].s, 0x030C020Cu);
+      sx01[u] = sigma_pair<false>(fx[u].s);
+      sx23[u] = sigma_pair<true>(fx[u].s);
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {

@@ -208,16 +208,13 @@ __device__ __forceinline__ half8_t dequant8(uint32_t codes, _Float16 sigma) {
   return r;
 }
 
-// Two E4M3 scale bytes of a dword (bytes 0,1 or 2,3 by `sel`) as a binary16
-// pair, without branches: the bit pattern s<<7 read as binary16 is
-// value(s) * 2^-8 for every E4M3 byte, normal or subnormal (the formats share
-// their subnormal layout and differ by 8 in exponent bias), and one exact
-// packed multiply by 256 restores the value (binary16 subnormals are kept:
-// the kernels run with denormals enabled).
-__device__ __forceinline__ half2_t sigma_pair(uint32_t scale_dword, uint32_t sel) {
-  const uint32_t b = __builtin_amdgcn_perm(0u, scale_dword, sel);  // (s_lo << 8) | (s_hi << 24)
-  const u16x2_t h = __builtin_bit_cast(u16x2_t, b) >> (uint16_t)1;
-  return __builtin_bit_cast(half2_t, h) * half2_t{(_Float16)256.0f, (_Float16)256.0f};
+// Two E4M3 scale bytes of a dword (bytes 0,1, or 2,3 with HIGH) as a
+// binary16 pair, in one hardware fp8 -> f16 conversion (its scale operand at
+// 1 = 2^0).  Every E4M3 value, normal or subnormal, is a normal binary16
+// value, so the conversion is exact.
+template <bool HIGH>
+__device__ __forceinline__ half2_t sigma_pair(uint32_t scale_dword) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scale_dword, 1.0f, HIGH);
 }
 
 }  // namespace mq
