@@ -442,11 +442,17 @@ struct WavePipe {
 // than MFMA-first slots).  The sched_barrier at the end keeps each step a
 // scheduling region of its own, so the groups cannot pull work from later
 // steps (which would stretch register live ranges).
-template <int NMFMA, int NVALU>
+// NVMEM memory instructions (the step's direct copies) are spread evenly
+// over the MFMA slots, slot k taking floor((k+1) NVMEM / NMFMA) -
+// floor(k NVMEM / NMFMA) of them.
+template <int NMFMA, int NVALU, int NVMEM = 0>
 __device__ __forceinline__ void interleave() {
 #pragma unroll
   for (int k = 0; k < NMFMA; ++k) {
     __builtin_amdgcn_sched_group_barrier(0x002, (NVALU + NMFMA - 1) / NMFMA, 0);
+#pragma unroll
+    for (int r = k * NVMEM / NMFMA; r < (k + 1) * NVMEM / NMFMA; ++r)
+      __builtin_amdgcn_sched_group_barrier(0x060, 1, 0);  // one memory instruction
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -456,7 +462,7 @@ __device__ __forceinline__ void interleave() {
 // first chunk in step 3, scales in step 4, second chunk in step 7, each after
 // the buffer's last use in this stage), dequantization of step S+1 (or of the
 // next stage's step 0), the MFMAs of step S, and step S's part of the fills.
-template <int S, int PN, int BM, int BN, typename Fill>
+template <int S, int PN, int BM, int BN, int NVMEM = 0, typename Fill>
 __device__ __forceinline__ void run_step(WavePipe<BM, BN>& p, f32x16_t (&acc)[BM / 64][BN / 64],
                                          const uint8_t* nxt, Fill& fill) {
   constexpr int TM = BM / 64, TN = BN / 64, NM = TM * TN, ND = 8 * (TM + TN);
@@ -466,9 +472,10 @@ __device__ __forceinline__ void run_step(WavePipe<BM, BN>& p, f32x16_t (&acc)[BM
   if (S == 7) p.sigmas();  // the next stage's; this stage's were last used in step 6
   if (S < 7) p.template dequant<(S + 1) & 7, (S + 1) & 1>();
   else p.template dequant<0, 0>();
+  if constexpr (NVMEM > 0) fill(S);  // its NVMEM copies go between the MFMAs
   p.template mfma<S & 1>(acc);
-  interleave<NM, ND + (S == 7 ? 2 * (TM + TN) : 0)>();
-  fill(S);
+  interleave<NM, ND + (S == 7 ? 2 * (TM + TN) : 0), NVMEM>();
+  if constexpr (NVMEM == 0) fill(S);
 }
 
 // Epilogue.  Each 32x32 accumulator holds D = W_j . A_i^T, so lane l owns
@@ -720,6 +727,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, int tm, int tn, 
       }
     };
     const int nd = (nk + 1) / 2;  // double stages (FAST shapes have nk even)
+    // The direct copies of a double stage go out in the odd stage before it
+    // is needed: code copy j in step j % kCodeSteps and the scale copies in
+    // step kScaleStep, each placed between two of its step's MFMAs (packed
+    // path only: the fused prologue's register traffic keeps its own order).
+    // Early steps leave the copies most of a stage to land; spreading them
+    // over all eight steps measured slower.
+    constexpr int kCodeSteps = 4, kScaleStep = 4;
+    constexpr auto copies_in_step = [](int step) constexpr {
+      if (!FAST || FUSED) return 0;
+      constexpr int kc = DmaLoader<BM, BN, true>::kCode;
+      return (step < kCodeSteps && kc > step ? (kc - 1 - step) / kCodeSteps + 1 : 0) +
+             (step == kScaleStep ? DmaLoader<BM, BN, true>::kScale : 0);
+    };
 
     // prologue: double stages 0 and 1 into the two slots (stage 3, the second
     // half of slot 1, comes from the register path in stage 0), then the pipe
@@ -807,8 +827,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, int tm, int tn, 
         }
         if constexpr (FAST) {
           const bool live = d + 2 < nd;
-          if (step < 4) dma.codes(cur, d + 2, live, step, 4);
-          if (step == 4) dma.scales(cur, d + 2, live);
+          if (step < kCodeSteps) dma.codes(cur, d + 2, live, step, kCodeSteps);
+          if (step == kScaleStep) dma.scales(cur, d + 2, live);
         }
       };
       run_step<0, 1>(pipe, acc, cur, fill_even);
@@ -821,14 +841,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& args, int tm, int tn, 
       run_step<7, 1>(pipe, acc, cur, fill_even);
       __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
       __builtin_amdgcn_s_barrier();
-      run_step<0, 0>(pipe, acc, nxt, fill_odd);
-      run_step<1, 0>(pipe, acc, nxt, fill_odd);
-      run_step<2, 0>(pipe, acc, nxt, fill_odd);
-      run_step<3, 0>(pipe, acc, nxt, fill_odd);
-      run_step<4, 0>(pipe, acc, nxt, fill_odd);
-      run_step<5, 0>(pipe, acc, nxt, fill_odd);
-      run_step<6, 0>(pipe, acc, nxt, fill_odd);
-      run_step<7, 0>(pipe, acc, nxt, fill_odd);
+      // the direct copies of the packed path: interleaved with the MFMAs
+      run_step<0, 0, BM, BN, copies_in_step(0)>(pipe, acc, nxt, fill_odd);
+      run_step<1, 0, BM, BN, copies_in_step(1)>(pipe, acc, nxt, fill_odd);
+      run_step<2, 0, BM, BN, copies_in_step(2)>(pipe, acc, nxt, fill_odd);
+      run_step<3, 0, BM, BN, copies_in_step(3)>(pipe, acc, nxt, fill_odd);
+      run_step<4, 0, BM, BN, copies_in_step(4)>(pipe, acc, nxt, fill_odd);
+      run_step<5, 0, BM, BN, copies_in_step(5)>(pipe, acc, nxt, fill_odd);
+      run_step<6, 0, BM, BN, copies_in_step(6)>(pipe, acc, nxt, fill_odd);
+      run_step<7, 0, BM, BN, copies_in_step(7)>(pipe, acc, nxt, fill_odd);
       uint8_t* t = cur;
       cur = nxt;
       nxt = t;
