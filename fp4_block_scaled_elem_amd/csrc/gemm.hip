@@ -289,8 +289,8 @@ struct DmaLoader {
   static constexpr int kScale = kRows / kScaleRowsPer / 4;  // scale copies per wave
   static_assert(kCode * 32 == kRows && kScale * 4 * kScaleRowsPer == kRows, "tile rows");
   uint32_t coff[kCode], soff[kScale];
-  const uint8_t *a_c, *w_c, *a_s, *w_s;   // first row of each tile
-  int a_cb, w_cb, a_sb, w_sb;             // its valid bytes
+  // the tiles' valid rows (of A, of W): resources over exactly their bytes
+  __amdgpu_buffer_rsrc_t ra_c, rw_c, ra_s, rw_s;
   int wave;
 
   // Requires BM * K / 2 < 2^31 (checked by the host).
@@ -301,15 +301,11 @@ struct DmaLoader {
     const int ldc = K / 2, ng = K / kGroup;
     const int ma = min(BM, M - m0), nw = min(BN, N - n0);  // valid rows of the tiles
     if (WITH_A) {
-      a_c = a_codes + (int64_t)m0 * ldc;
-      a_s = a_scales + (int64_t)m0 * ng;
-      a_cb = ma * ldc;
-      a_sb = ma * ng;
+      ra_c = tile_rsrc(a_codes + (int64_t)m0 * ldc, ma * ldc);
+      ra_s = tile_rsrc(a_scales + (int64_t)m0 * ng, ma * ng);
     }
-    w_c = w_codes + (int64_t)n0 * ldc;
-    w_s = w_scales + (int64_t)n0 * ng;
-    w_cb = nw * ldc;
-    w_sb = nw * ng;
+    rw_c = tile_rsrc(w_codes + (int64_t)n0 * ldc, nw * ldc);
+    rw_s = tile_rsrc(w_scales + (int64_t)n0 * ng, nw * ng);
     // rows past the valid ones fall outside the resource and read zeros
 #pragma unroll
     for (int j = 0; j < kCode; ++j) {
@@ -325,29 +321,35 @@ struct DmaLoader {
       soff[j] = (uint32_t)(row * ng + (kScaleBytes == 16 ? 0 : (lane & 3) << 2));
     }
   }
-  // Double stage ds into `slot`; with live false (past the end) the
-  // resources cover no bytes, so the copies move no data (they write zeros).
-  // Copies j with j % nparts == part are issued (the stage spreads them).
+  // Double stage ds into `slot`; with live false (past the end) the copies
+  // go through resources of no bytes, so they move no data (they write
+  // zeros).  (The scalar offset is no help there: buffer range checks
+  // cover the lane offset only.)  Copies j with j % nparts == part are
+  // issued (the stage spreads them).  Copy j of codes holds rows 32j .. 32j
+  // + 31 of the slot (eight per wave), so whether it reads A or W is known
+  // from j.
   __device__ __forceinline__ void codes(uint8_t* slot, int ds, bool live, int part, int nparts) const {
     uint8_t* lds = slot + (WITH_A ? Smem<BM, BN>::kA : Smem<BM, BN>::kW);
-    const __amdgpu_buffer_rsrc_t ra = tile_rsrc(WITH_A ? a_c : w_c, live ? (WITH_A ? a_cb : w_cb) : 0);
-    const __amdgpu_buffer_rsrc_t rw = tile_rsrc(w_c, live ? w_cb : 0);
+    const __amdgpu_buffer_rsrc_t ra = live ? ra_c : dead(), rw = live ? rw_c : dead();
 #pragma unroll
     for (int j = 0; j < kCode; ++j) {
       if (j % nparts != part) continue;
       const int t = wave + 4 * j;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(WITH_A && 8 * t < kRA ? ra : rw, (lds_void_t*)(lds + 1024 * t), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(WITH_A && 32 * j < kRA ? ra : rw, (lds_void_t*)(lds + 1024 * t), 16,
                                                (int)coff[j], ds * kRowStride, 0, 0);
     }
   }
   __device__ __forceinline__ void scales(uint8_t* slot, int ds, bool live) const {
     uint8_t* lds = slot + (WITH_A ? Smem<BM, BN>::kAs : Smem<BM, BN>::kWs);
-    const __amdgpu_buffer_rsrc_t ra = tile_rsrc(WITH_A ? a_s : w_s, live ? (WITH_A ? a_sb : w_sb) : 0);
-    const __amdgpu_buffer_rsrc_t rw = tile_rsrc(w_s, live ? w_sb : 0);
+    const __amdgpu_buffer_rsrc_t ra = live ? ra_s : dead(), rw = live ? rw_s : dead();
 #pragma unroll
     for (int j = 0; j < kScale; ++j) {
       const int t = wave + 4 * j;
-      const __amdgpu_buffer_rsrc_t r = WITH_A && kScaleRowsPer * t < kRA ? ra : rw;
+      // copy j covers rows kScaleRowsPer * (4j + wave): all of A, all of W,
+      // or (a 128-row A tile under 64-row copies) A for some waves only
+      const bool all_a = WITH_A && kScaleRowsPer * (4 * j + 3) < kRA;
+      const bool all_w = !WITH_A || kScaleRowsPer * 4 * j >= kRA;
+      const __amdgpu_buffer_rsrc_t r = all_a ? ra : all_w ? rw : kScaleRowsPer * t < kRA ? ra : rw;
       if constexpr (kScaleBytes == 16)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds + 1024 * t), 16, (int)soff[j],
                                                  ds * kScaleStride, 0, 0);
@@ -356,6 +358,7 @@ struct DmaLoader {
                                                  ds * kScaleStride, 0, 0);
     }
   }
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t dead() { return tile_rsrc(nullptr, 0); }
 };
 
 // --------------------------------------------------------------- compute --
