@@ -131,6 +131,10 @@ def lib():
     L.mq_check_mfma_rate.restype = ctypes.c_int32
     L.mq_check_wall_clock_khz.argtypes = [ctypes.POINTER(ctypes.c_int32)]
     L.mq_check_wall_clock_khz.restype = ctypes.c_int32
+    L.mq_check_set_quant_spin_limit.argtypes = [u32]
+    L.mq_check_set_quant_spin_limit.restype = u32
+    L.mq_check_quant_gave_up.argtypes = []
+    L.mq_check_quant_gave_up.restype = u32
     _lib = L
     return L
 
@@ -454,6 +458,25 @@ def mq_check_dequant_table(out, stream=None):
     if out.numel() != 128 * 4 * 16:
         raise ValueError("out must hold 128 x 4 x 16 entries")
     _check(lib().mq_check_dequant_table(_dev_ptr(out, "out"), _stream_ptr(stream)), "mq_check_dequant_table")
+
+
+def mq_check_set_quant_spin_limit(polls: int) -> int:
+    """Test support: the single-launch quantizer's poll limit before a
+    workgroup stops waiting for the others (0: every workgroup gives up and
+    takes the maximum itself).  Returns the previous limit."""
+    old = lib().mq_check_set_quant_spin_limit(polls)
+    if old == 0xFFFFFFFF:
+        raise MQError(MQ_ERR_DEVICE, "mq_check_set_quant_spin_limit", "HIP symbol copy failed")
+    return old
+
+
+def mq_check_quant_gave_up() -> int:
+    """Test support: workgroups of the single-launch quantizer that gave up
+    waiting since the last call (the count is reset)."""
+    n = lib().mq_check_quant_gave_up()
+    if n == 0xFFFFFFFF:
+        raise MQError(MQ_ERR_DEVICE, "mq_check_quant_gave_up", "HIP symbol copy failed")
+    return n
 
 
 def mq_check_mfma_rate(valu_per_mfma: int, iters: int, blocks: int, sink, clocks, stream=None):

@@ -129,6 +129,9 @@ mq_status mq_quantize_nvfp4(const void* x_bf16, int64_t rows, int64_t cols, cons
   const bool given = flags & MQ_SCALE_GIVEN;
   const bool dynamic = !given && !(flags & MQ_SCALE_PARTIALS);
   const bool inline_amax = dynamic && rows * cols <= mq::kInlineAmaxElems;
+  if (dynamic && !inline_amax && mq::quantize_resident_pays(rows * cols, dev))
+    return launched(mq::launch_quantize_resident(x_bf16, rows * cols, out->codes, out->scales, out->rec, dev, st),
+                    "quantize");
   if (dynamic && !inline_amax) {
     hipError_t e = mq::launch_amax(x_bf16, rows * cols, out->rec, dev, st);
     if (e != hipSuccess) return launched(e, "amax");

@@ -19,6 +19,10 @@
 //                          of steps instead of 2^32 results)
 //   mq_check_dequant_table every (scale byte, code) operand value as
 //                          binary16 bits
+//
+// and two knobs of the single-launch quantizer's bounded wait, so that a test
+// can force its give-up path (mq_check_set_quant_spin_limit,
+// mq_check_quant_gave_up).
 #include "mq_device.h"
 #include "mq_internal.h"
 
@@ -120,5 +124,15 @@ int32_t mq_check_dequant_table(uint16_t* out, void* hip_stream) {
   hipLaunchKernelGGL(mq::dequant_table_kernel, dim3(1), dim3(128), 0, (hipStream_t)hip_stream, out);
   return hipGetLastError() == hipSuccess ? MQ_OK : MQ_ERR_LAUNCH;
 }
+
+// The single-launch quantizer's poll limit before a workgroup stops waiting
+// for the others and takes the maximum itself (0: no wait, every workgroup
+// gives up): returns the previous limit, ~0u on error.  Device-wide, for the
+// current device; only for tests that run nothing else meanwhile.
+uint32_t mq_check_set_quant_spin_limit(uint32_t polls) { return mq::set_rq_spin_limit(polls); }
+
+// Workgroups of the single-launch quantizer that gave up waiting since the
+// last call (the count is reset), ~0u on error.
+uint32_t mq_check_quant_gave_up(void) { return mq::take_rq_gave_up(); }
 
 }  // extern "C"

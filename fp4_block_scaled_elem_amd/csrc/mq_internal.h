@@ -32,6 +32,21 @@ hipError_t launch_amax(const void* x_bf16, int64_t nelem, mq_scale_rec* rec, con
 hipError_t launch_quantize(const void* x_bf16, int64_t nelem, uint8_t* codes, uint8_t* scales,
                            mq_scale_rec* rec, bool given, const DeviceInfo& dev, hipStream_t stream,
                            bool inline_amax = false);
+// The single-launch quantizer addresses its input through buffer
+// resources: under 4 GiB of bf16.
+constexpr int64_t kResidentMaxElems = (int64_t)1 << 31;
+// Dynamic scale in one launch: the input read once into registers, the
+// workgroups meeting at its maximum through rec (whose flags count the
+// calls: the record must be zeroed when allocated).  For the input lengths
+// where quantize_resident_pays; others take the amax pass and the encode.
+bool quantize_resident_pays(int64_t nelem, const DeviceInfo& dev);
+hipError_t launch_quantize_resident(const void* x_bf16, int64_t nelem, uint8_t* codes, uint8_t* scales,
+                                    mq_scale_rec* rec, const DeviceInfo& dev, hipStream_t stream);
+// Test support: the single-launch quantizer's poll limit (0: every
+// workgroup takes the give-up path) and the count of workgroups that gave up
+// since the last read.  Both return ~0u on a HIP error.
+uint32_t set_rq_spin_limit(uint32_t polls);
+uint32_t take_rq_gave_up();
 // A operand of a GEMM launch: packed (codes, scales) or, fused, bf16 values
 // quantized in the kernel (rec then receives or, when given, supplies s_t).
 struct GemmOperandA {

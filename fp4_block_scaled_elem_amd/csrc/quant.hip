@@ -16,7 +16,9 @@
 //      conversion of x * e, the reciprocal group scale e from a table of the
 //      128 possible values built by each workgroup.
 // Both passes are HBM-bound: 2 bytes read per element for the amax, 2 read
-// plus 0.5625 written per element for the encode.
+// plus 0.5625 written per element for the encode.  For the input lengths
+// where it pays, quantize_resident_kernel (below) does both in one launch,
+// reading the input once.
 #include "mq_device.h"
 #include "mq_internal.h"
 
@@ -235,6 +237,188 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
     run(BoolC<false>{});
 }
 
+// ------------------------------------------------- single-launch quantizer --
+//
+// The dynamic scale in one launch.  One workgroup of kRThreads per CU; lane
+// g (of T = grid x kRThreads) owns the half-groups g, g + T, g + 2T, ...; the
+// first R of them stay in registers from the maximum to the encode, so the
+// input is read from HBM once (the rest, for inputs too long for the
+// register file, is read again).  The workgroups meet at the tensor maximum
+// through the record: each stores its maximum, tagged with the call's epoch
+// in the low 16 bits (always zero in a binary32 pattern of a bf16 magnitude),
+// in its slot of part[]; one wave per workgroup reads all slots until every
+// slot carries the tag.  The epoch
+// comes from rec->flags, which every workgroup of a call increments once at
+// its start: with the record zeroed when allocated and a grid that is the
+// same for every call on a device, all workgroups of a call read values in
+// [c * grid, (c + 1) * grid) and agree on c.  Every slot is rewritten by
+// every call, so a slot carries this call's tag only once this call wrote
+// it.  The wait is bounded: a workgroup that runs out of polls (its partners
+// not resident, say) takes the maximum over the whole input itself, which
+// gives the same bits, so the result never depends on the wait.
+constexpr int kRThreads = 512;
+constexpr int kRMaxResident = 48;  // uint4 per lane kept in registers at most
+
+__device__ uint32_t g_rq_spin_limit = 1u << 16;  // polls before a workgroup gives up (0: never wait)
+__device__ uint32_t g_rq_gave_up = 0;             // workgroups that gave up, for tests
+
+template <int NT>
+__device__ __forceinline__ uint32_t block_max_n(uint32_t v, uint32_t* sh) {
+  v = wave_max_u32(v);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) r = r > sh[i] ? r : sh[i];
+  __syncthreads();
+  return r;
+}
+
+// Operands through buffer resources: a lane's half-group j sits at the
+// lane's fixed offset plus a scalar offset j x T, so the R resident
+// half-groups cost no address registers, and offsets past the input read
+// zeros (which leave the maximum unchanged) and drop stores.  Requires the
+// input under 4 GiB (host-checked).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rq_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);  // raw, 32-bit format
+}
+
+template <int R>
+__global__ __launch_bounds__(kRThreads, 1) void quantize_resident_kernel(const uint4* __restrict__ x, uint32_t nhalf,
+                                                                         int J, uint32_t* __restrict__ codes,
+                                                                         uint8_t* __restrict__ scales,
+                                                                         mq_scale_rec* __restrict__ rec) {
+  __shared__ uint32_t sh[kRThreads / 64];
+  __shared__ float recip[128];
+  __shared__ uint32_t tag_sh;
+  __shared__ uint32_t amax_sh;
+  __shared__ int ok_sh;
+  const uint32_t G = gridDim.x;  // <= kRThreads, host-checked
+  const uint32_t T = G * kRThreads;
+  const uint32_t g0 = blockIdx.x * kRThreads + threadIdx.x;
+  const uint32_t limit = g_rq_spin_limit;
+  const __amdgpu_buffer_rsrc_t rx = rq_rsrc(x, nhalf * 16u);
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&rec->flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    tag_sh = (old / G) % 65535u + 1u;  // 1..65535: never the zero of an untagged maximum
+  }
+  auto load = [&](uint32_t j) __attribute__((always_inline)) {
+    const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(g0 * 16u), (int)(j * T * 16u), 2 /* nt */);
+    return make_uint4(t[0], t[1], t[2], t[3]);
+  };
+  // every resident half-group in flight at once
+  uint4 v[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) v[j] = load(j);
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const uint32_t a = uint4_absmax(v[j]);
+    m = m > a ? m : a;
+  }
+  for (int j = R; j < J; ++j) {
+    const uint32_t a = uint4_absmax(load(j));
+    m = m > a ? m : a;
+  }
+  // Up to 32 resident half-groups the encode reuses their maxima from here;
+  // with more, it recomputes them (keeping them live across the wait would
+  // spill).
+  if constexpr (R > 32) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) asm volatile("" : "+v"(v[j].x), "+v"(v[j].y), "+v"(v[j].z), "+v"(v[j].w));
+  }
+  m = block_max_n<kRThreads>(m, sh);  // its barriers also publish tag_sh
+  const uint32_t tag = tag_sh;
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&rec->part[blockIdx.x], (m << 16) | tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // wave 0 reads the slots: lane l those of index l mod 64
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int ok = limit != 0;
+    uint32_t mx = 0;
+    for (uint32_t polls = 0; ok;) {
+      bool mine = true;
+      mx = 0;
+#pragma unroll
+      for (int k = 0; k < kRThreads / 64; ++k) {
+        const uint32_t slot = (uint32_t)(lane + 64 * k);
+        if (slot < G) {
+          const uint32_t q = __hip_atomic_load(&rec->part[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          mine = mine && (q & 0xFFFFu) == tag;
+          const uint32_t v = q & 0xFFFF0000u;
+          mx = mx > v ? mx : v;
+        }
+      }
+      if (__all(mine)) break;
+      if (++polls > limit) ok = 0;
+      else __builtin_amdgcn_s_sleep(1);
+    }
+    mx = wave_max_u32(mx);
+    if (lane == 0) {
+      ok_sh = ok;
+      amax_sh = mx;
+    }
+  }
+  __syncthreads();
+  const int ok = ok_sh;
+  uint32_t amax = amax_sh;
+  if (!ok) {
+    // gave up: the maximum of the whole input, read by this workgroup alone
+    uint32_t w = 0;
+    for (uint32_t base = 0; base < nhalf; base += 8 * kRThreads) {
+      uint4 t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const u32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((base + u * kRThreads + threadIdx.x) * 16u),
+                                                                0, 0);
+        t[u] = make_uint4(q[0], q[1], q[2], q[3]);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t a = uint4_absmax(t[u]);
+        w = w > a ? w : a;
+      }
+    }
+    amax = block_max_n<kRThreads>(w, sh) << 16;
+    if (threadIdx.x == 0) atomicAdd(&g_rq_gave_up, 1u);
+  }
+  const float s_t = tensor_scale_from_amax(amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    rec->s_t = s_t;
+    rec->amax_bits = amax;
+    rec->nparts = 0;  // part[] holds tagged maxima, not partials a consumer may reduce
+  }
+  const GroupScaleTab tab = group_scale_tab<kRThreads>(s_t, recip);
+  const __amdgpu_buffer_rsrc_t rc = rq_rsrc(codes, nhalf * 4u);
+  const __amdgpu_buffer_rsrc_t rs = rq_rsrc(scales, nhalf / 2u);
+  const bool even = (g0 & 1u) == 0;  // T is even: the same for all of the lane's half-groups
+  // No branches on the range: past the input the loads read zeros and the
+  // stores are dropped, and both lanes of every group meet at the swap of
+  // their half maxima.
+  auto run = [&](auto ovf_c) __attribute__((always_inline)) {
+    constexpr bool OVF = decltype(ovf_c)::value;
+    auto encode = [&](const uint4& t, uint32_t j) __attribute__((always_inline)) {
+      const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+      uint32_t am = uint4_absmax(t);
+      const uint32_t other = __shfl_xor(am, 1, 64);
+      am = am > other ? am : other;
+      float e;
+      const uint32_t S = group_scale(am, tab, e);
+      __builtin_amdgcn_raw_buffer_store_b32(encode8<OVF>(w, e), rc, (int)(g0 * 4u), (int)(j * T * 4u), 0);
+      if (even) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)S, rs, (int)(g0 / 2u), (int)(j * T / 2u), 0);
+    };
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (j < J) encode(v[j], j);
+    for (int j = R; j < J; ++j) encode(load(j), j);
+  };
+  if (tab.ovf)
+    run(BoolC<true>{});
+  else
+    run(BoolC<false>{});
+}
+
 static int grid_for(int64_t items, int threads, int max_blocks) {
   int64_t b = (items + threads - 1) / threads;
   if (b > max_blocks) b = max_blocks;
@@ -267,4 +451,59 @@ hipError_t launch_quantize(const void* x_bf16, int64_t nelem, uint8_t* codes, ui
   return hipGetLastError();
 }
 
+// Lanes' shares of the input, in half-groups, for which the single launch
+// pays (measured on MI355X against the amax pass + encode): from 17, where
+// reading the input once outweighs the wait at the maximum (about 2.5 us),
+// to 56, where the part beyond the 48 kept in registers is read twice.
+constexpr int64_t kResidentMinJ = 17, kResidentMaxJ = 56;
+
+static int resident_grid(const DeviceInfo& dev) { return dev.num_cu < kRThreads ? dev.num_cu : kRThreads; }
+
+static int64_t resident_share(int64_t nelem, const DeviceInfo& dev) {
+  const int64_t T = (int64_t)resident_grid(dev) * kRThreads;
+  return (nelem / 8 + T - 1) / T;
+}
+
+bool quantize_resident_pays(int64_t nelem, const DeviceInfo& dev) {
+  const int64_t J = resident_share(nelem, dev);
+  return nelem < kResidentMaxElems && J >= kResidentMinJ && J <= kResidentMaxJ;
+}
+
+// One workgroup per CU (at most kRThreads of them, a grid that is the same
+// for every call on the device) and R = 32 or 48 registers' worth of
+// half-groups per lane, the rest (up to kResidentMaxJ) read twice.
+hipError_t launch_quantize_resident(const void* x_bf16, int64_t nelem, uint8_t* codes, uint8_t* scales,
+                                    mq_scale_rec* rec, const DeviceInfo& dev, hipStream_t stream) {
+  if (!quantize_resident_pays(nelem, dev)) return hipErrorInvalidValue;  // the caller checks first
+  const int G = resident_grid(dev);
+  const int64_t J = resident_share(nelem, dev);
+  const int R = J <= 32 ? 32 : kRMaxResident;
+  log_launch("quantize_resident_kernel", G, kRThreads, 0, "elements=%lld R=%d J=%lld", (long long)nelem, R,
+             (long long)J);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(G), dim3(kRThreads), 0, stream, (const uint4*)x_bf16, (uint32_t)(nelem / 8),
+                       (int)J, (uint32_t*)codes, scales, rec);
+  };
+  if (R == 32)
+    go(quantize_resident_kernel<32>);
+  else
+    go(quantize_resident_kernel<kRMaxResident>);
+  return hipGetLastError();
+}
+
+uint32_t set_rq_spin_limit(uint32_t polls) {
+  uint32_t old = 0;
+  if (hipMemcpyFromSymbol(&old, HIP_SYMBOL(g_rq_spin_limit), sizeof(old)) != hipSuccess) return ~0u;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(g_rq_spin_limit), &polls, sizeof(polls)) != hipSuccess) return ~0u;
+  return old;
+}
+
+uint32_t take_rq_gave_up() {
+  uint32_t n = 0, zero = 0;
+  if (hipMemcpyFromSymbol(&n, HIP_SYMBOL(g_rq_gave_up), sizeof(n)) != hipSuccess) return ~0u;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(g_rq_gave_up), &zero, sizeof(zero)) != hipSuccess) return ~0u;
+  return n;
+}
+
 }  // namespace mq
+

@@ -93,11 +93,17 @@ typedef int32_t mq_status;
  * s_t       binary32 decode scale of the tensor (read by the GEMM epilogue).
  * amax_bits bit pattern of max|x| that s_t came from (0 when given).
  * nparts    number of valid entries in part[] (written by the amax pass).
- * flags     reserved, 0.
+ * flags     call counter of the single-launch quantizer (mq_quantize_nvfp4),
+ *           whose workgroups meet at the tensor maximum through it; only
+ *           that kernel reads or writes it.
  * part[]    per-workgroup maxima of |x| as binary32 bit patterns; written by
- *           the amax pass and reduced by whichever kernel consumes the scale.
- * The record needs no initialisation: every field a call reads was written
- * earlier in the same call, except s_t under MQ_SCALE_GIVEN (caller-set). */
+ *           the amax pass (or the single-launch quantizer) and reduced by
+ *           whichever kernel consumes the scale.
+ * Zero the record once when allocating it (flags must start at 0); no call
+ * needs it re-initialised afterwards: every other field a call reads was
+ * written earlier in the same call, except s_t under MQ_SCALE_GIVEN
+ * (caller-set).  One record serves one call at a time: calls that share a
+ * record must be ordered (same stream, or synchronised). */
 typedef struct mq_scale_rec {
   float s_t;
   uint32_t amax_bits;
@@ -144,10 +150,17 @@ typedef struct mq_nvfp4 {
  * flags    MQ_SCALE_DYNAMIC, MQ_SCALE_GIVEN or MQ_SCALE_PARTIALS (out->rec's
  *          nparts and part[] already hold x's partial maxima from a producer
  *          op: s_t is derived from them, bit-identical to the dynamic case).
- * Launches: an amax pass (dynamic only), then the quantizer; for
- *          rows*cols <= 2^17 (dynamic) the quantizer alone, every workgroup
+ * Launches: given scale or partials, the encode alone.  Dynamic scale:
+ *          for rows*cols <= 2^17 the encode alone too, every workgroup
  *          taking max|x| itself (out->rec then receives s_t and amax_bits,
- *          not nparts / part[]).
+ *          not nparts / part[]).  Where each lane of a grid of one
+ *          512-thread workgroup per CU holds 17 to 56 groups of 8 elements
+ *          (on 256 CUs: 2^24 < rows*cols <= 56 * 2^20), one launch: the
+ *          lanes keep their share of x in registers, the workgroups meet at
+ *          the tensor maximum through out->rec (part[] and flags; a bounded
+ *          wait: a workgroup whose partners are not resident in time reads
+ *          all of x for the maximum itself, same result; nparts is left 0),
+ *          then encode.  Otherwise an amax pass, then the encode.
  */
 mq_status mq_quantize_nvfp4(const void* x_bf16, int64_t rows, int64_t cols,
                             const mq_nvfp4* out, uint32_t flags,

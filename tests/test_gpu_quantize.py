@@ -151,3 +151,119 @@ def test_inline_amax_boundary(rows, cols):
     assert st == int(np.float32(ref.s_t).view(np.uint32))
     assert int(q.rec[1:2].cpu().numpy().view(np.uint32)[0]) == (int(x[-1, -1]) & 0x7FFF) << 16
     assert np.array_equal(scales, ref.scales) and np.array_equal(codes, ref.codes)
+
+
+# ------------------------------------------------ single-launch quantizer --
+#
+# Dynamic-scale inputs of 17 to 56 half-groups (8 elements) per lane of a
+# grid of one 512-thread workgroup per CU (on 256 CUs: above 16.8M and up to
+# 58.7M elements) are quantized in one launch, each lane keeping up to 32 or
+# 48 of its half-groups in registers from the maximum to the encode (the
+# rest read twice), the workgroups meeting at the tensor maximum through
+# epoch-tagged slots of the record (rec->flags counts the workgroups'
+# starts: it grows by the grid per call).  Other lengths take the amax pass
+# and the encode, and leave rec->flags alone.
+
+
+def _num_cu():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def _share(rows, cols):
+    t = min(_num_cu(), 512) * 512
+    return -(-(rows * cols // 8) // t)
+
+
+def _rec_words(q):
+    return q.rec.cpu().numpy().view(np.uint32)
+
+
+def _sampled_check(q, x, what):
+    rows = np.unique(np.concatenate([np.random.default_rng(x.shape[0] + x.shape[1]).choice(x.shape[0], 96),
+                                     [0, x.shape[0] - 1]]))
+    ref = oracle.quantize_nvfp4(x, rows=rows)
+    codes, scales, st = quantized_host(q)
+    assert st == int(np.float32(ref.s_t).view(np.uint32)), f"{what}: tensor scale"
+    assert np.array_equal(codes[rows], ref.codes), f"{what}: codes"
+    assert np.array_equal(scales[rows], ref.scales), f"{what}: scale bytes"
+    return ref
+
+
+@pytest.mark.parametrize("rows,cols", [(4096, 4096), (2999, 7184), (4096, 8192), (4096, 8208), (4096, 11264),
+                                       (4096, 14336), (4096, 14352), (8192, 8192)])
+def test_single_launch_lengths(rows, cols):
+    # on 256 CUs: 16 (two passes), 21 (ragged), 32, 33 (ragged, 48 kept),
+    # 44, 56 (8 read twice) and 57, 64 (two passes) half-groups per lane
+    announce("quantize single launch", rows, cols)
+    import torch
+    mq = _mq()
+    x = workloads.random_bf16((rows, cols), 300 + rows + cols, 1.0, "lognormal_mixed")
+    q = mq.NVFP4.empty(rows, cols)
+    mq.mq_quantize_nvfp4(to_dev_bf16(x), q)
+    torch.cuda.synchronize()
+    _sampled_check(q, x, f"{rows}x{cols}")
+    w = _rec_words(q)
+    assert int(w[1]) == int((x & 0x7FFF).max()) << 16, "amax_bits"
+    single = 17 <= _share(rows, cols) <= 56
+    if single:
+        assert int(w[2]) == 0, "no partial maxima are left for a consumer"
+        assert int((w[4:4 + _num_cu()] & 0xFFFF0000).max()) == int(w[1]), "the slots reduce to amax"
+        assert int(w[3]) == _num_cu(), "every workgroup counts the call once"
+    else:
+        assert int(w[3]) == 0 and 1 <= int(w[2]) <= mq.MQ_AMAX_PARTS, "the amax pass's partial maxima"
+    assert mq.mq_check_quant_gave_up() == 0
+
+
+def test_single_launch_forced_give_up():
+    # With no polls allowed every workgroup stops waiting at once and reads
+    # the whole input for its maximum: the same bytes, only slower.
+    announce("quantize single launch, forced give-up")
+    import torch
+    mq = _mq()
+    mq.mq_check_quant_gave_up()
+    x = workloads.random_bf16((4096, 6144), 71, 3.0, "normal")
+    assert 17 <= _share(*x.shape) <= 56
+    q = mq.NVFP4.empty(*x.shape)
+    old = mq.mq_check_set_quant_spin_limit(0)
+    try:
+        mq.mq_quantize_nvfp4(to_dev_bf16(x), q)
+        torch.cuda.synchronize()
+    finally:
+        mq.mq_check_set_quant_spin_limit(old)
+    assert mq.mq_check_quant_gave_up() == _num_cu()
+    _sampled_check(q, x, "forced give-up")
+    # and the next call on the same record waits normally again
+    y = workloads.random_bf16((4096, 6144), 72, 0.5, "normal")
+    mq.mq_quantize_nvfp4(to_dev_bf16(y), q)
+    torch.cuda.synchronize()
+    assert mq.mq_check_quant_gave_up() == 0
+    _sampled_check(q, y, "after forced give-up")
+
+
+def test_single_launch_epochs_on_one_record():
+    # Successive calls on one record, each with a smaller maximum than the
+    # last (a slot read from an earlier call would raise the scale), with a
+    # producer's partial maxima written into the same record in between.
+    announce("quantize single launch, repeated calls on one record")
+    import torch
+    mq = _mq()
+    rows, cols = 4096, 5120
+    assert 17 <= _share(rows, cols) <= 56
+    q = mq.NVFP4.empty(rows, cols)
+    g = to_dev_bf16(workloads.random_bf16((cols,), 9, 1.0, "normal"))
+    y = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    calls = 0
+    for i in range(5):
+        x = workloads.random_bf16((rows, cols), 400 + i, 64.0 / 2 ** i, "normal")
+        mq.mq_quantize_nvfp4(to_dev_bf16(x), q)
+        calls += 1
+        torch.cuda.synchronize()
+        _sampled_check(q, x, f"call {i}")
+        if i % 2 == 0:
+            # partial maxima (untagged) over the slots, then their consumer
+            mq.mq_rmsnorm_amax(to_dev_bf16(x), g, y, q)
+            mq.mq_quantize_nvfp4(y, q, mq.MQ_SCALE_PARTIALS)
+            torch.cuda.synchronize()
+    assert int(_rec_words(q)[3]) == calls * _num_cu()
+    assert mq.mq_check_quant_gave_up() == 0
