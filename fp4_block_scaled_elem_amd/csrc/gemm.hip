@@ -515,6 +515,11 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[BM / 64][BN / 64]
   const int cl = tid % kLanesRow, rl0 = tid / kLanesRow;
   const int n = n0 + 4 * cl;
   const bool vec = (N & 3) == 0 && n + 3 < N;
+  // full tiles: 16-byte pieces, BN * E / 16 of them per row
+  constexpr int kLanesRow16 = BN * E / 16;
+  constexpr int kRowsIter16 = kThreads / kLanesRow16;
+  const int c16 = tid % kLanesRow16, rl16 = tid / kLanesRow16;
+  const bool full = m0 + BM <= M && n0 + BN <= N && (N * E) % 16 == 0;
   __syncthreads();  // every wave is done with the operand ring
 #pragma unroll
   for (int fm = 0; fm < TM; ++fm) {
@@ -538,30 +543,44 @@ __device__ __forceinline__ void epilogue(const f32x16_t (&acc)[BM / 64][BN / 64]
       }
     }
     __syncthreads();
+    if (full) {
+      // whole tile inside C (the common case): every lane stores 8 (bf16) or
+      // 4 (binary32) consecutive columns, 16 bytes, with no bounds checks
 #pragma unroll
-    for (int it = 0; it < 64 / kRowsIter; ++it) {
-      const int lr = it * kRowsIter + rl0;
-      const int m = m0 + (lr >> 5) * (BM / 2) + fm * 32 + (lr & 31);
-      if (m >= M) continue;
-      const uint8_t* src = buf + lr * P + cl * W;
-      const int64_t off = (int64_t)m * N + n;
-      if (OUT_F32) {
-        const f32x4_t v = *(const f32x4_t*)src;
-        if (vec) {
-          __builtin_nontemporal_store(v, (f32x4_t*)((float*)c + off));
+      for (int it = 0; it < 64 / kRowsIter16; ++it) {
+        const int lr = it * kRowsIter16 + rl16;
+        const int m = m0 + (lr >> 5) * (BM / 2) + fm * 32 + (lr & 31);
+        const uint8_t* src = buf + lr * P + c16 * 16;  // 8-byte aligned (the pitch is padded by 8)
+        const u32x2_t lo = *(const u32x2_t*)src, hi = *(const u32x2_t*)(src + 8);
+        const u32x4_t v = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        __builtin_nontemporal_store(v, (u32x4_t*)((uint8_t*)c + ((int64_t)m * N + n0) * E + c16 * 16));
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < 64 / kRowsIter; ++it) {
+        const int lr = it * kRowsIter + rl0;
+        const int m = m0 + (lr >> 5) * (BM / 2) + fm * 32 + (lr & 31);
+        if (m >= M) continue;
+        const uint8_t* src = buf + lr * P + cl * W;
+        const int64_t off = (int64_t)m * N + n;
+        if (OUT_F32) {
+          const f32x4_t v = *(const f32x4_t*)src;
+          if (vec) {
+            __builtin_nontemporal_store(v, (f32x4_t*)((float*)c + off));
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (n + q < N) ((float*)c)[off + q] = v[q];
+          }
         } else {
+          const u32x2_t v = *(const u32x2_t*)src;
+          if (vec) {
+            __builtin_nontemporal_store(v, (u32x2_t*)((uint16_t*)c + off));
+          } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (n + q < N) ((float*)c)[off + q] = v[q];
-        }
-      } else {
-        const u32x2_t v = *(const u32x2_t*)src;
-        if (vec) {
-          __builtin_nontemporal_store(v, (u32x2_t*)((uint16_t*)c + off));
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (n + q < N) ((uint16_t*)c)[off + q] = (uint16_t)(v[q >> 1] >> (16 * (q & 1)));
+            for (int q = 0; q < 4; ++q)
+              if (n + q < N) ((uint16_t*)c)[off + q] = (uint16_t)(v[q >> 1] >> (16 * (q & 1)));
+          }
         }
       }
     }
