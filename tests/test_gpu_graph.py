@@ -77,6 +77,35 @@ def test_prefill_quantize_and_gemm_replay():
         assert _same(c, ce), f"replay {r}: gemm output"
 
 
+def test_single_launch_quantizer_replay():
+    # The single-launch quantizer (inputs of 17 to 56 half-groups per lane,
+    # here 4096 x 5120 on 256 CUs) takes its barrier epoch from the record on
+    # the device, so every replay of a captured call is a new epoch.  Each
+    # replay's input has a smaller maximum than the last (a slot left from an
+    # earlier epoch would raise the scale), and an eager call on the same
+    # record runs between replays.
+    announce("graph: single-launch quantizer")
+    import torch
+    mq = _mq()
+    M, K = 4096, 5120
+    x = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    x.copy_(to_dev_bf16(workloads.random_bf16((M, K), 40, 64.0)))
+    qa = mq.NVFP4.empty(M, K)
+    g = _capture(lambda: mq.mq_quantize_nvfp4(x, qa))
+    for r in range(REPLAYS):
+        xr = to_dev_bf16(workloads.random_bf16((M, K), 41 + r, 32.0 / 4 ** r))
+        x.copy_(xr)
+        g.replay()
+        qe = mq.quantize(xr)
+        torch.cuda.synchronize()
+        assert _same(qa.codes, qe.codes) and _same(qa.scales, qe.scales), f"replay {r}: quantization"
+        assert _same(qa.rec[:1], qe.rec[:1]), f"replay {r}: tensor scale"
+        # an eager call on the captured record between replays
+        mq.mq_quantize_nvfp4(to_dev_bf16(workloads.random_bf16((M, K), 60 + r, 100.0)), qa)
+    torch.cuda.synchronize()
+    assert mq.mq_check_quant_gave_up() == 0
+
+
 @pytest.mark.parametrize("form", ["tile", "panel"])
 def test_fused_prologue_gemm_replay(form):
     # tile: A re-quantized per column tile; panel: quantized once per
