@@ -314,7 +314,7 @@ constexpr int kGv2Waves = 8;
 
 template <int NTILE>
 __device__ __forceinline__ void lds_read_chunk64(const uint32_t (&a)[2], u32x4_t (&v)[2][NTILE]) {
-  static_assert(NTILE == 3 || NTILE == 4, "tiles per chunk");
+  static_assert(NTILE == 3 || NTILE == 4 || NTILE == 6, "tiles per chunk");
   if constexpr (NTILE == 3) {
     u32x4_t a0, a1, a2, b0, b1, b2;
     asm volatile(
@@ -326,7 +326,7 @@ __device__ __forceinline__ void lds_read_chunk64(const uint32_t (&a)[2], u32x4_t
         : "memory");
     v[0][0] = a0; v[0][1] = a1; v[0][2] = a2;
     v[1][0] = b0; v[1][1] = b1; v[1][2] = b2;
-  } else {
+  } else if constexpr (NTILE == 4) {
     u32x4_t a0, a1, a2, a3, b0, b1, b2, b3;
     asm volatile(
         "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:2048\n\t"
@@ -339,14 +339,28 @@ __device__ __forceinline__ void lds_read_chunk64(const uint32_t (&a)[2], u32x4_t
         : "memory");
     v[0][0] = a0; v[0][1] = a1; v[0][2] = a2; v[0][3] = a3;
     v[1][0] = b0; v[1][1] = b1; v[1][2] = b2; v[1][3] = b3;
+  } else {
+    u32x4_t a0, a1, a2, a3, a4, a5, b0, b1, b2, b3, b4, b5;
+    asm volatile(
+        "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:2048\n\tds_read_b128 %2, %12 offset:4096\n\t"
+        "ds_read_b128 %3, %12 offset:6144\n\tds_read_b128 %4, %12 offset:8192\n\tds_read_b128 %5, %12 offset:10240\n\t"
+        "ds_read_b128 %6, %13\n\tds_read_b128 %7, %13 offset:2048\n\tds_read_b128 %8, %13 offset:4096\n\t"
+        "ds_read_b128 %9, %13 offset:6144\n\tds_read_b128 %10, %13 offset:8192\n\tds_read_b128 %11, %13 offset:10240\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(a4), "=&v"(a5), "=&v"(b0), "=&v"(b1), "=&v"(b2),
+          "=&v"(b3), "=&v"(b4), "=&v"(b5)
+        : "v"(a[0]), "v"(a[1])
+        : "memory");
+    v[0][0] = a0; v[0][1] = a1; v[0][2] = a2; v[0][3] = a3; v[0][4] = a4; v[0][5] = a5;
+    v[1][0] = b0; v[1][1] = b1; v[1][2] = b2; v[1][3] = b3; v[1][4] = b4; v[1][5] = b5;
   }
 }
 
-template <int WT>
-constexpr int gv2_lds_bytes() { return kGv2Waves * 2 * (WT + 2) * kGv2Tile; }
+template <int WT, int NW>
+constexpr int gv2_lds_bytes() { return NW * 2 * (WT + 2) * kGv2Tile; }
 
-template <bool GROUPED, bool NT, int WT>
-__global__ __launch_bounds__(kGv2Waves * 64) void gemv_bf16_m32_kernel(const uint16_t* __restrict__ x,
+template <bool GROUPED, bool NT, int WT, int NW = kGv2Waves>
+__global__ __launch_bounds__(NW * 64) void gemv_bf16_m32_kernel(const uint16_t* __restrict__ x,
                                                                      GvGroups grp, int M, int K, int rotate) {
   constexpr int MT = 2;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -375,13 +389,19 @@ __global__ __launch_bounds__(kGv2Waves * 64) void gemv_bf16_m32_kernel(const uin
   }
   uint8_t* ring = lds + wave * 2 * kBufBytes;
   const int nchunks = K / kGv2Chunk;
-  const int mine = nchunks > wave ? (nchunks - wave + kGv2Waves - 1) / kGv2Waves : 0;
-  const int rot = rotate && mine > 0 ? (n0 >> 5) % mine : 0;  // as in gemv_bf16_kernel
+  const int mine = nchunks > wave ? (nchunks - wave + NW - 1) / NW : 0;
+  // NW < kGv2Waves: each wave stands for VW of the kGv2Waves waves of the
+  // other form (its chunks alternate between them, each with its own
+  // accumulators), and the partial sums are added in that form's order, so
+  // every output is bit-identical to it (no chunk rotation in this form)
+  constexpr int VW = kGv2Waves / NW;
+  static_assert(VW * NW == kGv2Waves, "waves");
+  const int rot = VW == 1 && rotate && mine > 0 ? (n0 >> 5) % mine : 0;  // as in gemv_bf16_kernel
   auto copy = [&](int t, uint8_t* dst) __attribute__((always_inline)) {
     const bool live = t < mine;
     int tr = t + rot;
     tr = tr < mine ? tr : tr - mine;
-    const int k0 = (wave + kGv2Waves * tr) * kGv2Chunk;
+    const int k0 = (wave + NW * tr) * kGv2Chunk;
     const __amdgpu_buffer_rsrc_t rw =
         __builtin_amdgcn_make_buffer_rsrc((void*)wtile, 0, live ? wbytes : 0, kGvBufferWord3);
     const __amdgpu_buffer_rsrc_t rx =
@@ -397,11 +417,13 @@ __global__ __launch_bounds__(kGv2Waves * 64) void gemv_bf16_m32_kernel(const uin
                                                live ? k0 * 2 : 0, 0, 0);
   };
 
-  f32x4_t acc[WT][MT];
+  f32x4_t acc[VW][WT][MT];
 #pragma unroll
-  for (int t = 0; t < WT; ++t)
+  for (int s = 0; s < VW; ++s)
 #pragma unroll
-    for (int u = 0; u < MT; ++u) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < WT; ++t)
+#pragma unroll
+      for (int u = 0; u < MT; ++u) acc[s][t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // one chunk ahead through two alternating buffers, as gemv_bf16_kernel
   uint8_t* cur = ring;
@@ -409,42 +431,50 @@ __global__ __launch_bounds__(kGv2Waves * 64) void gemv_bf16_m32_kernel(const uin
   copy(0, cur);
   constexpr int kWait = kCopies;
   static_assert(kWait < 64, "vmcnt range");
-  for (int t = 0; t < mine; ++t) {
-    copy(t + 1, nxt);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (kWait & 15) | ((kWait >> 4) << 14));  // vmcnt(kWait)
-    uint32_t ad[2];
+  for (int t0 = 0; t0 < mine; t0 += VW) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      ad[q] = (uint32_t)(uintptr_t)(cur + i * kGv2RowBytes + (((4 * q + h) ^ ((i >> 1) & 7)) << 4));
-    u32x4_t v[2][NTILE];
-    lds_read_chunk64<NTILE>(ad, v);
+    for (int s = 0; s < VW; ++s) {
+      const int t = t0 + s;
+      if (VW > 1 && t >= mine) break;  // the same for the whole wave
+      copy(t + 1, nxt);
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (kWait & 15) | ((kWait >> 4) << 14));  // vmcnt(kWait)
+      uint32_t ad[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+      for (int q = 0; q < 2; ++q)
+        ad[q] = (uint32_t)(uintptr_t)(cur + i * kGv2RowBytes + (((4 * q + h) ^ ((i >> 1) & 7)) << 4));
+      u32x4_t v[2][NTILE];
+      lds_read_chunk64<NTILE>(ad, v);
 #pragma unroll
-      for (int tt = 0; tt < WT; ++tt)
+      for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int u = 0; u < MT; ++u)
-          acc[tt][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, v[q][tt]),
-                                                              __builtin_bit_cast(bf16x8_t, v[q][WT + u]),
-                                                              acc[tt][u], 0, 0, 0);
-    uint8_t* done = cur;
-    cur = nxt;
-    nxt = done;
+        for (int tt = 0; tt < WT; ++tt)
+#pragma unroll
+          for (int u = 0; u < MT; ++u)
+            acc[s][tt][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, v[q][tt]),
+                                                                   __builtin_bit_cast(bf16x8_t, v[q][WT + u]),
+                                                                   acc[s][tt][u], 0, 0, 0);
+      uint8_t* done = cur;
+      cur = nxt;
+      nxt = done;
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): no copy still writes the ring
   __syncthreads();
   constexpr int kPairs = WT * MT;
-  f32x4_t* red = (f32x4_t*)lds;  // [wave][WT * MT][64]
+  f32x4_t* red = (f32x4_t*)lds;  // [wave of the eight-wave form][WT * MT][64]
+  static_assert(kGv2Waves * kPairs * 64 * 16 <= gv2_lds_bytes<WT, NW>(), "reduction fits the ring");
 #pragma unroll
-  for (int t = 0; t < WT; ++t)
+  for (int s = 0; s < VW; ++s)
 #pragma unroll
-    for (int u = 0; u < MT; ++u) red[(wave * kPairs + t * MT + u) * 64 + lane] = acc[t][u];
+    for (int t = 0; t < WT; ++t)
+#pragma unroll
+      for (int u = 0; u < MT; ++u) red[((wave + NW * s) * kPairs + t * MT + u) * 64 + lane] = acc[s][t][u];
   __syncthreads();
-  // wave p finishes W tile p / MT against X tile p % MT
-  if (wave < kPairs) {
-    const int t = wave / MT, u = wave % MT;
-    f32x4_t sum = red[wave * 64 + lane];
-    for (int v2 = 1; v2 < kGv2Waves; ++v2) sum += red[(v2 * kPairs + wave) * 64 + lane];
+  // wave p finishes W tile p / MT against X tile p % MT (p = wave, wave + NW, ...)
+  for (int p = wave; p < kPairs; p += NW) {
+    const int t = p / MT, u = p % MT;
+    f32x4_t sum = red[p * 64 + lane];
+    for (int v2 = 1; v2 < kGv2Waves; ++v2) sum += red[(v2 * kPairs + p) * 64 + lane];
     const int m = (lane & 15) + 16 * u;
     if (m < M) {
 #pragma unroll
@@ -583,30 +613,29 @@ static hipError_t launch_ring_nt(const void* x, const GvGroups& g, int tiles, in
                              : launch_ring<MT, GROUPED, false, WT>(x, g, tiles, M, K, dev.device, stream);
 }
 
-template <bool GROUPED, bool NT, int WT>
+template <bool GROUPED, bool NT, int WT, int NW = kGv2Waves>
 static hipError_t launch_m32(const void* x, const GvGroups& g, int tiles, int64_t M, int64_t K, int dev,
                              hipStream_t stream) {
-  auto kern = gemv_bf16_m32_kernel<GROUPED, NT, WT>;
-  constexpr int lds = gv2_lds_bytes<WT>();
+  auto kern = gemv_bf16_m32_kernel<GROUPED, NT, WT, NW>;
+  constexpr int lds = gv2_lds_bytes<WT, NW>();
   static bool attr_done[64] = {};  // benign race: the call is idempotent
   if (dev < 0 || dev >= 64 || !attr_done[dev]) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < 64) attr_done[dev] = true;
   }
-  log_launch("gemv_bf16_m32_kernel", tiles, kGv2Waves * 64, lds,
+  log_launch("gemv_bf16_m32_kernel", tiles, NW * 64, lds,
              "row_tiles=%d grouped=%d nt=%d M=%lld K=%lld groups=%d", WT, (int)GROUPED, (int)NT, (long long)M,
              (long long)K, g.ngroup);
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kGv2Waves * 64), lds, stream, (const uint16_t*)x, g, (int)M,
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(NW * 64), lds, stream, (const uint16_t*)x, g, (int)M,
                      (int)K, K >= kGvRotateK ? 1 : 0);
   return hipGetLastError();
 }
-
-template <bool GROUPED, int WT>
+template <bool GROUPED, int WT, int NW = kGv2Waves>
 static hipError_t launch_m32_nt(const void* x, const GvGroups& g, int tiles, int64_t M, int64_t K,
                                 const DeviceInfo& dev, hipStream_t stream) {
-  return tiles >= dev.num_cu ? launch_m32<GROUPED, true, WT>(x, g, tiles, M, K, dev.device, stream)
-                             : launch_m32<GROUPED, false, WT>(x, g, tiles, M, K, dev.device, stream);
+  return tiles >= dev.num_cu ? launch_m32<GROUPED, true, WT, NW>(x, g, tiles, M, K, dev.device, stream)
+                             : launch_m32<GROUPED, false, WT, NW>(x, g, tiles, M, K, dev.device, stream);
 }
 
 template <bool GROUPED>
@@ -637,9 +666,15 @@ hipError_t launch_gemv_grouped(const void* x, const GemvWeight* w, int ngroup, i
   // At M > 16 a workgroup takes 32 W rows when that still leaves a workgroup
   // for every CU: twice the W bytes in flight per CU, half the X bytes per W
   // byte.  Smaller grids keep 16 rows (more workgroups).
-  int64_t rows = 0;
-  for (int k = 0; k < ngroup; ++k) rows += (w[k].n + 31) / 32;
-  const int wt = ring && M > 16 && rows >= dev.num_cu ? 2 : 1;
+  int64_t rows = 0, rows64 = 0;
+  for (int k = 0; k < ngroup; ++k) {
+    rows += (w[k].n + 31) / 32;
+    rows64 += (w[k].n + 63) / 64;
+  }
+  int wt = ring && M > 16 && rows >= dev.num_cu ? 2 : 1;
+  // wide weights at M > 16 and K below the rotation length: 64 W rows per
+  // four-wave workgroup, X read once per 64 W rows
+  if (ring && M > 16 && K < kGvRotateK && rows64 * 4 >= (int64_t)dev.num_cu * 3) wt = 4;
   GvGroups g{};
   int tiles = 0;
   for (int k = 0; k < ngroup; ++k) {
@@ -653,15 +688,17 @@ hipError_t launch_gemv_grouped(const void* x, const GemvWeight* w, int ngroup, i
   if (ngroup == 1) {
     if (!ring) return launch_ragged<false>(x, g, tiles, M, K, dev, stream);
     if (M <= 16) return launch_ring_nt<1, false>(x, g, tiles, M, K, dev, stream);
-    if (K < kGvRotateK) return wt == 2 ? launch_m32_nt<false, 2>(x, g, tiles, M, K, dev, stream)
-                                       : launch_m32_nt<false, 1>(x, g, tiles, M, K, dev, stream);
+    if (K < kGvRotateK) return wt == 4   ? launch_m32_nt<false, 4, 4>(x, g, tiles, M, K, dev, stream)
+                               : wt == 2 ? launch_m32_nt<false, 2>(x, g, tiles, M, K, dev, stream)
+                                         : launch_m32_nt<false, 1>(x, g, tiles, M, K, dev, stream);
     return wt == 2 ? launch_ring_nt<2, false, 2>(x, g, tiles, M, K, dev, stream)
                    : launch_ring_nt<2, false>(x, g, tiles, M, K, dev, stream);
   }
   if (!ring) return launch_ragged<true>(x, g, tiles, M, K, dev, stream);
   if (M <= 16) return launch_ring_nt<1, true>(x, g, tiles, M, K, dev, stream);
-  if (K < kGvRotateK) return wt == 2 ? launch_m32_nt<true, 2>(x, g, tiles, M, K, dev, stream)
-                                     : launch_m32_nt<true, 1>(x, g, tiles, M, K, dev, stream);
+  if (K < kGvRotateK) return wt == 4   ? launch_m32_nt<true, 4, 4>(x, g, tiles, M, K, dev, stream)
+                             : wt == 2 ? launch_m32_nt<true, 2>(x, g, tiles, M, K, dev, stream)
+                                       : launch_m32_nt<true, 1>(x, g, tiles, M, K, dev, stream);
   return wt == 2 ? launch_ring_nt<2, true, 2>(x, g, tiles, M, K, dev, stream)
                  : launch_ring_nt<2, true>(x, g, tiles, M, K, dev, stream);
 }

@@ -116,6 +116,10 @@ def test_grouped_bit_identical_to_single_calls(M, Ns, K):
     (3, 4096, 4080, 1024),    # 256 vs 255 workgroups: non-temporal W copies on one side only
     (32, 8192, 8160, 512),    # 256 vs 255 pairs of row tiles: 32-row vs 16-row workgroups
     (20, 8192, 8160, 384),
+    # on 256 CUs: 192 vs 191 tiles of 64 rows: four-wave 64-row workgroups
+    # (each wave standing for two of the eight-wave form) vs 32-row ones
+    (32, 12288, 12224, 1024),
+    (17, 12288, 12224, 4096),
 ])
 def test_dispatch_boundaries_agree(M, N_big, N_small, K):
     # the launch choices at these boundaries change cache policy or rows per
