@@ -241,9 +241,9 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
 //
 // The dynamic scale in one launch.  One workgroup of kRThreads per CU; lane
 // g (of T = grid x kRThreads) owns the half-groups g, g + T, g + 2T, ...; the
-// first R of them stay in registers from the maximum to the encode, so the
-// input is read from HBM once (the rest, for inputs too long for the
-// register file, is read again).  The workgroups meet at the tensor maximum
+// first R of them stay in registers from the maximum to the encode (the
+// next ones, for inputs too long for the register file, in LDS), so the
+// input is read from HBM once.  The workgroups meet at the tensor maximum
 // through the record: each stores its maximum, tagged with the call's epoch
 // in the low 16 bits (always zero in a binary32 pattern of a bf16 magnitude),
 // in its slot of part[]; one wave per workgroup reads all slots until every
@@ -258,6 +258,8 @@ __global__ __launch_bounds__(kQThreads) void quantize_kernel(const uint4* __rest
 // gives the same bits, so the result never depends on the wait.
 constexpr int kRThreads = 512;
 constexpr int kRMaxResident = 48;  // uint4 per lane kept in registers at most
+constexpr int kRHeldLds = 16;      // and beyond them, per lane, in LDS (128 KB per workgroup)
+typedef __attribute__((address_space(3))) void rq_lds_t;
 
 __device__ uint32_t g_rq_spin_limit = 1u << 16;  // polls before a workgroup gives up (0: never wait)
 __device__ uint32_t g_rq_gave_up = 0;             // workgroups that gave up, for tests
@@ -275,20 +277,25 @@ __device__ __forceinline__ uint32_t block_max_n(uint32_t v, uint32_t* sh) {
   return r;
 }
 
-// Operands through buffer resources: a lane's half-group j sits at the
-// lane's fixed offset plus a scalar offset j x T, so the R resident
-// half-groups cost no address registers, and offsets past the input read
-// zeros (which leave the maximum unchanged) and drop stores.  Requires the
-// input under 4 GiB (host-checked).
+// Operands through buffer resources: a lane's half-group j sits at lane
+// offset (g + j x T) x 16, formed just before each access (so the R
+// resident half-groups cost no address registers), and lane offsets past the
+// input read zeros (which leave the maximum unchanged) and drop stores.  The
+// whole offset is the lane's: the range check covers it, not only the part
+// of a scalar offset.  Requires the input under 4 GiB (host-checked).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rq_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);  // raw, 32-bit format
 }
 
-template <int R>
+// HOLD: the half-groups R .. R + kRHeldLds - 1 of a lane wait in LDS
+// (dynamic LDS, direct-to-LDS copies, 1 KB per wave and half-group) instead
+// of being read again for the encode.
+template <int R, bool HOLD>
 __global__ __launch_bounds__(kRThreads, 1) void quantize_resident_kernel(const uint4* __restrict__ x, uint32_t nhalf,
                                                                          int J, uint32_t* __restrict__ codes,
                                                                          uint8_t* __restrict__ scales,
                                                                          mq_scale_rec* __restrict__ rec) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t held[];  // [kRHeldLds][waves][64 lanes][16 B]
   __shared__ uint32_t sh[kRThreads / 64];
   __shared__ float recip[128];
   __shared__ uint32_t tag_sh;
@@ -304,22 +311,44 @@ __global__ __launch_bounds__(kRThreads, 1) void quantize_resident_kernel(const u
     tag_sh = (old / G) % 65535u + 1u;  // 1..65535: never the zero of an untagged maximum
   }
   auto load = [&](uint32_t j) __attribute__((always_inline)) {
-    const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(g0 * 16u), (int)(j * T * 16u), 2 /* nt */);
+    const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((g0 + j * T) * 16u), 0, 2 /* nt */);
     return make_uint4(t[0], t[1], t[2], t[3]);
   };
   // every resident half-group in flight at once
   uint4 v[R];
 #pragma unroll
   for (int j = 0; j < R; ++j) v[j] = load(j);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto held_at = [&](int k) __attribute__((always_inline)) {
+    return held + ((k * (kRThreads / 64) + wave_u) * 64) * 16;  // the wave's 1 KB for half-group R + k
+  };
+  if constexpr (HOLD) {
+    // past the input the copies write zeros (and are never encoded)
+#pragma unroll
+    for (int k = 0; k < kRHeldLds; ++k)
+      if (R + k < J)  // the same for the whole grid
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (rq_lds_t*)held_at(k), 16, (int)((g0 + (R + k) * T) * 16u), 0,
+                                               0, 2 /* nt */);
+  }
   uint32_t m = 0;
 #pragma unroll
   for (int j = 0; j < R; ++j) {
     const uint32_t a = uint4_absmax(v[j]);
     m = m > a ? m : a;
   }
-  for (int j = R; j < J; ++j) {
-    const uint32_t a = uint4_absmax(load(j));
-    m = m > a ? m : a;
+  if constexpr (HOLD) {
+#pragma unroll
+    for (int k = 0; k < kRHeldLds; ++k) {
+      if (R + k >= J) break;
+      const uint32_t a = uint4_absmax(*(const uint4*)(held_at(k) + lane * 16));
+      m = m > a ? m : a;
+    }
+  } else {
+    for (int j = R; j < J; ++j) {
+      const uint32_t a = uint4_absmax(load(j));
+      m = m > a ? m : a;
+    }
   }
   // Up to 32 resident half-groups the encode reuses their maxima from here;
   // with more, it recomputes them (keeping them live across the wait would
@@ -405,13 +434,20 @@ __global__ __launch_bounds__(kRThreads, 1) void quantize_resident_kernel(const u
       am = am > other ? am : other;
       float e;
       const uint32_t S = group_scale(am, tab, e);
-      __builtin_amdgcn_raw_buffer_store_b32(encode8<OVF>(w, e), rc, (int)(g0 * 4u), (int)(j * T * 4u), 0);
-      if (even) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)S, rs, (int)(g0 / 2u), (int)(j * T / 2u), 0);
+      const uint32_t h = g0 + j * T;
+      __builtin_amdgcn_raw_buffer_store_b32(encode8<OVF>(w, e), rc, (int)(h * 4u), 0, 0);
+      if (even) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)S, rs, (int)(h / 2u), 0, 0);
     };
 #pragma unroll
     for (int j = 0; j < R; ++j)
       if (j < J) encode(v[j], j);
-    for (int j = R; j < J; ++j) encode(load(j), j);
+    if constexpr (HOLD) {
+#pragma unroll
+      for (int k = 0; k < kRHeldLds; ++k)
+        if (R + k < J) encode(*(const uint4*)(held_at(k) + lane * 16), R + k);
+    } else {
+      for (int j = R; j < J; ++j) encode(load(j), j);
+    }
   };
   if (tab.ovf)
     run(BoolC<true>{});
@@ -454,8 +490,9 @@ hipError_t launch_quantize(const void* x_bf16, int64_t nelem, uint8_t* codes, ui
 // Lanes' shares of the input, in half-groups, for which the single launch
 // pays (measured on MI355X against the amax pass + encode): from 17, where
 // reading the input once outweighs the wait at the maximum (about 2.5 us),
-// to 56, where the part beyond the 48 kept in registers is read twice.
-constexpr int64_t kResidentMinJ = 17, kResidentMaxJ = 56;
+// to the 48 kept in registers plus the 16 held in LDS.
+constexpr int64_t kResidentMinJ = 17, kResidentMaxJ = 64;
+static_assert(kResidentMaxJ <= kRMaxResident + kRHeldLds, "the longest share is held in registers and LDS");
 
 static int resident_grid(const DeviceInfo& dev) { return dev.num_cu < kRThreads ? dev.num_cu : kRThreads; }
 
@@ -471,7 +508,7 @@ bool quantize_resident_pays(int64_t nelem, const DeviceInfo& dev) {
 
 // One workgroup per CU (at most kRThreads of them, a grid that is the same
 // for every call on the device) and R = 32 or 48 registers' worth of
-// half-groups per lane, the rest (up to kResidentMaxJ) read twice.
+// half-groups per lane, beyond 48 the rest (up to kResidentMaxJ) in LDS.
 hipError_t launch_quantize_resident(const void* x_bf16, int64_t nelem, uint8_t* codes, uint8_t* scales,
                                     mq_scale_rec* rec, const DeviceInfo& dev, hipStream_t stream) {
   if (!quantize_resident_pays(nelem, dev)) return hipErrorInvalidValue;  // the caller checks first
@@ -480,14 +517,25 @@ hipError_t launch_quantize_resident(const void* x_bf16, int64_t nelem, uint8_t* 
   const int R = J <= 32 ? 32 : kRMaxResident;
   log_launch("quantize_resident_kernel", G, kRThreads, 0, "elements=%lld R=%d J=%lld", (long long)nelem, R,
              (long long)J);
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(G), dim3(kRThreads), 0, stream, (const uint4*)x_bf16, (uint32_t)(nelem / 8),
+  auto go = [&](auto kern, int lds) {
+    hipLaunchKernelGGL(kern, dim3(G), dim3(kRThreads), lds, stream, (const uint4*)x_bf16, (uint32_t)(nelem / 8),
                        (int)J, (uint32_t*)codes, scales, rec);
   };
-  if (R == 32)
-    go(quantize_resident_kernel<32>);
-  else
-    go(quantize_resident_kernel<kRMaxResident>);
+  if (R == 32) {
+    go(quantize_resident_kernel<32, false>, 0);
+  } else if (J <= kRMaxResident) {
+    go(quantize_resident_kernel<kRMaxResident, false>, 0);
+  } else {
+    auto kern = quantize_resident_kernel<kRMaxResident, true>;
+    constexpr int lds = kRHeldLds * kRThreads * 16;
+    static bool attr_done[64] = {};  // benign race: the call is idempotent
+    if (dev.device < 0 || dev.device >= 64 || !attr_done[dev.device]) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e != hipSuccess) return e;
+      if (dev.device >= 0 && dev.device < 64) attr_done[dev.device] = true;
+    }
+    go(kern, lds);
+  }
   return hipGetLastError();
 }
 

@@ -154,9 +154,9 @@ typedef struct mq_nvfp4 {
  *          for rows*cols <= 2^17 the encode alone too, every workgroup
  *          taking max|x| itself (out->rec then receives s_t and amax_bits,
  *          not nparts / part[]).  Where each lane of a grid of one
- *          512-thread workgroup per CU holds 17 to 56 groups of 8 elements
- *          (on 256 CUs: 2^24 < rows*cols <= 56 * 2^20), one launch: the
- *          lanes keep their share of x in registers, the workgroups meet at
+ *          512-thread workgroup per CU holds 17 to 64 groups of 8 elements
+ *          (on 256 CUs: 2^24 < rows*cols <= 2^26), one launch: the lanes
+ *          keep their share of x in registers (and LDS), the workgroups meet at
  *          the tensor maximum through out->rec (part[] and flags; a bounded
  *          wait: a workgroup whose partners are not resident in time reads
  *          all of x for the maximum itself, same result; nparts is left 0),

@@ -78,7 +78,7 @@ def test_prefill_quantize_and_gemm_replay():
 
 
 def test_single_launch_quantizer_replay():
-    # The single-launch quantizer (inputs of 17 to 56 half-groups per lane,
+    # The single-launch quantizer (inputs of 17 to 64 half-groups per lane,
     # here 4096 x 5120 on 256 CUs) takes its barrier epoch from the record on
     # the device, so every replay of a captured call is a new epoch.  Each
     # replay's input has a smaller maximum than the last (a slot left from an

@@ -23,13 +23,14 @@ PAT = 0xA5
 
 
 class Guarded:
-    """A view of `shape` and `dtype` inside a guarded byte buffer."""
+    """A view of `shape` and `dtype` inside a guarded byte buffer (`tail`
+    guard bytes after it, G before)."""
 
-    def __init__(self, shape, dtype, fill=None):
+    def __init__(self, shape, dtype, fill=None, tail=G):
         import torch
         n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
         self.n = n
-        self.buf = torch.full((G + n + G,), PAT, dtype=torch.uint8, device="cuda")
+        self.buf = torch.full((G + n + tail,), PAT, dtype=torch.uint8, device="cuda")
         self.t = self.buf[G:G + n].view(dtype).view(*shape)
         if fill is not None:
             self.t.view(torch.uint8).fill_(fill)
@@ -55,6 +56,30 @@ def _nvfp4(rows, cols):
 
 def _all_intact(gs):
     return all(g.intact() for g in gs)
+
+
+@pytest.mark.parametrize("rows,cols", [(2999, 7184), (4000, 14336)])
+def test_single_launch_quantizer_stays_inside_its_buffers(rows, cols):
+    # ragged shares of 21 (32 kept in registers) and 55 (48 in registers, the
+    # rest held in LDS) half-groups per lane on 256 CUs: the lanes past the
+    # input in the last share compute codes that must be dropped, not
+    # written up to hundreds of KB past the buffers, hence the 1 MB tail guards
+    announce("guards single-launch quantizer", rows, cols)
+    import torch
+    import fp4_block_scaled_elem_amd as mq
+    x = to_dev_bf16(workloads.random_bf16((rows, cols), 90, 1.0, "lognormal_mixed"))
+    c = Guarded((rows, cols // 2), torch.uint8, tail=1 << 20)
+    sc = Guarded((rows, cols // 16), torch.uint8, tail=1 << 20)
+    r = Guarded((mq.REC_BYTES // 4,), torch.int32, fill=0)
+    q = mq.NVFP4(c.t, sc.t, r.t)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        mq.mq_quantize_nvfp4(x, q)
+    st.synchronize()
+    assert _all_intact([c, sc, r])
+    ref = mq.quantize(x)
+    torch.cuda.synchronize()
+    assert torch.equal(c.t, ref.codes) and torch.equal(sc.t, ref.scales)
 
 
 @pytest.mark.parametrize("M,N,K", [(37, 300, 272), (300, 520, 512), (129, 17, 4112)])
