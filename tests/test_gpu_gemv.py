@@ -89,6 +89,9 @@ def test_deterministic():
     (17, (1000, 33), 4112),               # K % 128 != 0: the register-path kernel
     # 32 W rows per workgroup in the grouped launch, 16 in the single calls
     (32, (5000, 3300), 4096), (17, (8200, 48), 1024),
+    # on 256 CUs: 64 W rows on four waves in the grouped launch, 32 and 16
+    # rows on eight waves in the single calls
+    (24, (8192, 4096), 1024),
 ])
 def test_grouped_bit_identical_to_single_calls(M, Ns, K):
     # one launch over several weights that read the same X: every output is
