@@ -243,7 +243,8 @@ def single_linear_latency(reps=50):
     -- calls made back to back from Python (eager) and the same calls
     captured in a HIP graph and replayed (the kernels' own time).  67 MFLOP
     is far too little work for a throughput figure; this configuration
-    measures launch latency."""
+    measures launch latency.  On 128 rows the GEMM is the small-problem
+    kernel (K split over each workgroup's waves, 256 workgroups)."""
     import torch
     import fp4_block_scaled_elem_amd as mq
     import workloads
@@ -265,11 +266,18 @@ def single_linear_latency(reps=50):
     fused = lambda _: mq.mq_gemm_nvfp4_prefill(rec, x, qw, cf, mq.MQ_A_FUSED_BF16)
     fmed, fmn = _median_us(fused, reps=reps)
     fg = _graph_us(fused, cf)
+    # the GEMM alone on the already quantized activation
+    cg = torch.empty_like(c)
+    gemm_only = lambda _: mq.mq_gemm_nvfp4_prefill(qa, None, qw, cg)
+    gg = _graph_us(gemm_only, cg)
     torch.cuda.synchronize()
     if not torch.equal(c.view(torch.int16), cf.view(torch.int16)):
         raise RuntimeError("fused single-launch linear differs from quantize + GEMM")
+    if not torch.equal(c.view(torch.int16), cg.view(torch.int16)):
+        raise RuntimeError("GEMM on the quantized activation differs from quantize + GEMM")
     flops = 2 * 128 * 512 * 512
     return {"workload": workloads.CONFIGS[1].name,
+            "gemm_only": {"launches": 1, "us_graph": round(gg, 2), "tflops_graph": round(flops / gg / 1e6, 2)},
             "quantize_then_gemm": {"launches": 2, "us_median_eager": round(med, 2), "us_min_eager": round(mn, 2),
                                    "us_graph": round(g, 2), "tflops_graph": round(flops / g / 1e6, 2)},
             "fused_one_launch": {"launches": 1, "us_median_eager": round(fmed, 2), "us_min_eager": round(fmn, 2),

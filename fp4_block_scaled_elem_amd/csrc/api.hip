@@ -189,7 +189,10 @@ mq_status mq_gemm_nvfp4_prefill_grouped(const mq_nvfp4* a, const void* a_bf16, i
   const bool given = flags & MQ_SCALE_GIVEN;
   const bool dynamic = fused && !given && !(flags & MQ_SCALE_PARTIALS);
   // the per-tile fused form on a small A takes the maximum inside the GEMM
-  const bool inline_amax = dynamic && !a->codes && M * K <= mq::kInlineAmaxElems;
+  // (the quantize-once form's tiled kernels read partial maxima; the small-
+  // problem kernel takes the maximum itself in every A form)
+  const bool inline_amax =
+      dynamic && M * K <= mq::kInlineAmaxElems && (!a->codes || mq::gemm_small_rows(M));
   if (dynamic && !inline_amax) {
     hipError_t e = mq::launch_amax(a_bf16, M * K, a->rec, dev, st);
     if (e != hipSuccess) return launched(e, "amax");

@@ -610,7 +610,9 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
 // small enough that every workgroup reads all of it from L2 in about a
 // microsecond) there is no amax pass: each workgroup takes max|A| itself,
 // the same maximum, so the whole fused GEMM is one launch.
-template <bool REDUCE>
+// LOADS: loads in flight per lane while taking max|A| (the small-problem
+// kernel has the registers for 16; the tiled kernels keep 8).
+template <bool REDUCE, int LOADS = 8>
 __device__ __forceinline__ float a_tensor_scale(const GemmArgs& args) {
   if (!REDUCE || args.a_given) return args.a_rec->s_t;
   __shared__ uint32_t red[kThreads / 64];
@@ -619,15 +621,15 @@ __device__ __forceinline__ float a_tensor_scale(const GemmArgs& args) {
   if (args.a_inline) {
     const uint4* x = (const uint4*)args.a_bf16;
     const int nvec = args.M * args.K / 8;  // at most 2^14 (host-checked)
-    for (int base = 0; base < nvec; base += 8 * kThreads) {
-      uint4 v[8];  // eight loads in flight per lane
+    for (int base = 0; base < nvec; base += LOADS * kThreads) {
+      uint4 v[LOADS];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < LOADS; ++u) {
         const int i = base + u * kThreads + tid;
         v[u] = x[i < nvec ? i : nvec - 1];  // a repeated element leaves the maximum unchanged
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < LOADS; ++u) {
         const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
         const uint32_t a = bf16_absmax_bits<4>(w) << 16;  // binary32 bits, as the partial maxima
         m = m > a ? m : a;
@@ -933,6 +935,275 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_panel_kernel(GemmArgs args, 
   }
 }
 
+// ------------------------------------------------------------- small GEMM --
+//
+// Problems too small to fill the CUs with 128- or 256-row tiles (a short
+// prompt's M rows; chosen by row count alone, gemm_small_rows): a workgroup
+// owns 16 * WT rows of W and 16 * MT rows of A, its four waves take the K
+// chunks (128 elements) in turn, and their partial tiles are summed through
+// LDS in wave order (deterministic).  The arithmetic is the tiled kernel's (exact
+// binary16 operands g * sigma, binary32 accumulation, the sum scaled by
+// fp32(s_tA * s_tW) and rounded to nearest-even bf16), here on
+// v_mfma_f32_16x16x32_f16: lane (i, h) holds row i's chunk elements
+// 32h .. 32h + 31 (groups 2h and 2h + 1, eight elements per MFMA step) of
+// both operands, so the K order is the same for A and W.  A comes packed,
+// or (FUSED) as bf16 that each workgroup quantizes in registers by the
+// quantizer's rules; with WRITE_A the workgroups of the first W tile also
+// store A's NVFP4 (standard layout).  The summation order differs from the
+// tiled kernel's: results agree with it within the GEMM tolerance, and with
+// this kernel bit for bit across the A forms, groupings and streams.
+constexpr int kSmChunk = 128;                      // K elements per chunk
+constexpr int kSmWaves = kThreads / 64;            // four: the chunks of K in turn
+constexpr int kSmallMaxRows = 128;                 // gemm_small_rows
+
+// One operand row's share of a chunk for one lane: 4 code dwords (steps
+// 0..3) and the scale bytes of its two groups (bits 0..15).
+struct SmFrag {
+  uint32_t c[4];
+  uint32_t s;
+};
+// The same share as bf16 values (fused A): 32 elements, two per word.
+struct SmRaw {
+  uint4 v[4];
+};
+template <bool FUSED> struct SmA { typedef SmFrag T; };
+template <> struct SmA<true> { typedef SmRaw T; };
+
+// Loads of a valid row (rows past M or N are clamped by the caller: they
+// only feed outputs that are never stored).  FAST: K % 128 == 0, whole
+// 16-byte pieces; otherwise group by group, groups past K loaded from a
+// clamped index and zeroed by a select (zero codes and scales add nothing).
+template <bool FAST>
+__device__ __forceinline__ SmFrag sm_load_packed(const uint8_t* __restrict__ codes,
+                                                 const uint8_t* __restrict__ scales, int row, int K, int chunk,
+                                                 int h) {
+  SmFrag f;
+  const int g0 = chunk * (kSmChunk / 16) + 2 * h;  // first group of the lane
+  const uint8_t* crow = codes + (int64_t)row * (K / 2);
+  const uint8_t* srow = scales + (int64_t)row * (K / 16);
+  if constexpr (FAST) {
+    const u32x4_t a = *(const u32x4_t*)(crow + g0 * 8);
+    f.c[0] = a[0]; f.c[1] = a[1]; f.c[2] = a[2]; f.c[3] = a[3];
+    f.s = *(const uint16_t*)(srow + g0);
+  } else {
+    const int G = K / 16;
+    f.s = 0u;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const bool ok = g0 + g < G;
+      const int gc = ok ? g0 + g : G - 1;
+      const u32x2_t v = *(const u32x2_t*)(crow + gc * 8);
+      const uint32_t sb = srow[gc];
+      f.c[2 * g] = ok ? v[0] : 0u;
+      f.c[2 * g + 1] = ok ? v[1] : 0u;
+      f.s |= (ok ? sb : 0u) << (8 * g);
+    }
+  }
+  return f;
+}
+
+template <bool FAST>
+__device__ __forceinline__ SmRaw sm_load_bf16(const void* __restrict__ x, int row, int K, int chunk, int h) {
+  SmRaw r;
+  const int g0 = chunk * (kSmChunk / 16) + 2 * h;
+  const uint4* xr = (const uint4*)((const uint16_t*)x + (int64_t)row * K);  // two uint4 per group
+  if constexpr (FAST) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r.v[q] = xr[2 * g0 + q];
+  } else {
+    const int G = K / 16;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const bool ok = g0 + g < G;
+      const int gc = ok ? g0 + g : G - 1;
+      const uint4 a = xr[2 * gc], b = xr[2 * gc + 1];
+      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      r.v[2 * g] = ok ? a : z;
+      r.v[2 * g + 1] = ok ? b : z;
+    }
+  }
+  return r;
+}
+
+// The quantizer's encoding of the lane's two groups (zeroed groups past K
+// get scale byte 0 and zero codes).
+template <bool OVF>
+__device__ __forceinline__ SmFrag sm_quantize(const SmRaw& r, const GroupScaleTab& tab) {
+  SmFrag f;
+  f.s = 0u;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const uint32_t w[8] = {r.v[2 * g].x,     r.v[2 * g].y,     r.v[2 * g].z,     r.v[2 * g].w,
+                           r.v[2 * g + 1].x, r.v[2 * g + 1].y, r.v[2 * g + 1].z, r.v[2 * g + 1].w};
+    const uint32_t S = quantize_group16<OVF>(w, tab, f.c[2 * g], f.c[2 * g + 1]);
+    f.s |= S << (8 * g);
+  }
+  return f;
+}
+
+template <int WT, int MT, bool FAST, bool OUT_F32, bool FUSED, bool WRITE_A>
+__global__ __launch_bounds__(kThreads) void gemm_small_kernel(GemmArgs args) {
+  typedef typename SmA<FUSED>::T AFrag;
+  constexpr int NT = WT * MT;  // 16x16 output tiles per workgroup
+  __shared__ f32x4_t red[kSmWaves][NT][64];
+  __shared__ float recip_tab[128];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int i = lane & 15, h = lane >> 4;
+  const int tn = blockIdx.x % args.tiles_n, tm = blockIdx.x / args.tiles_n;
+  const GroupView grp = group_of(args, tn);
+  const int N = grp.N, K = args.K, M = args.M;
+  const int n0 = (tn - grp.tn0) * 16 * WT, m0 = tm * 16 * MT;
+  int wrow[WT], arow[MT];
+#pragma unroll
+  for (int w = 0; w < WT; ++w) wrow[w] = min(n0 + 16 * w + i, N - 1);
+#pragma unroll
+  for (int u = 0; u < MT; ++u) arow[u] = min(m0 + 16 * u + i, M - 1);
+  const int nchunks = (K + kSmChunk - 1) / kSmChunk;
+  const int mine = nchunks > wave ? (nchunks - wave + kSmWaves - 1) / kSmWaves : 0;  // this wave's chunks
+  // the first W tiles' workgroups store A's NVFP4 (each A row once)
+  const bool store_a = WRITE_A && tn == 0;
+
+  f32x4_t acc[WT][MT];
+#pragma unroll
+  for (int w = 0; w < WT; ++w)
+#pragma unroll
+    for (int u = 0; u < MT; ++u) acc[w][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // chunk t of this wave.  Past the last chunk it re-reads that chunk (the
+  // loads stay unconditional, so waiting for one chunk never waits for the
+  // next); compute then zeroes W's scales, and the chunk adds nothing.
+  auto chunk_of = [&](int t) __attribute__((always_inline)) { return wave + kSmWaves * min(t, mine - 1); };
+  auto load = [&](int t, SmFrag (&fw)[WT], AFrag (&fa)[MT]) __attribute__((always_inline)) {
+    const int c = chunk_of(t);
+#pragma unroll
+    for (int w = 0; w < WT; ++w) fw[w] = sm_load_packed<FAST>(grp.w_codes, grp.w_scales, wrow[w], K, c, h);
+#pragma unroll
+    for (int u = 0; u < MT; ++u) {
+      if constexpr (FUSED)
+        fa[u] = sm_load_bf16<FAST>(args.a_bf16, arow[u], K, c, h);
+      else
+        fa[u] = sm_load_packed<FAST>(args.a_codes, args.a_scales, arow[u], K, c, h);
+    }
+  };
+  // the first chunk's operands go out before the tensor scale is known:
+  // their latency overlaps the maximum (fused) and the table build
+  SmFrag aw[WT], bw[WT];
+  AFrag ax[MT], bx[MT];
+  if (mine > 0) load(0, aw, ax);
+  const float s_ta = a_tensor_scale<FUSED, 16>(args);
+  GroupScaleTab gtab{};
+  if constexpr (FUSED) gtab = group_scale_tab<kThreads>(s_ta, recip_tab);
+  auto run = [&](auto ovf_c) __attribute__((always_inline)) {
+    constexpr bool OVF = decltype(ovf_c)::value;
+    auto compute = [&](const SmFrag (&fw)[WT], const AFrag (&fa)[MT], int t) __attribute__((always_inline)) {
+      const bool live = t < mine;
+      SmFrag qa[MT];
+#pragma unroll
+      for (int u = 0; u < MT; ++u) {
+        if constexpr (FUSED) {
+          qa[u] = sm_quantize<OVF>(fa[u], gtab);
+          if (store_a && live && m0 + 16 * u + i < M) {
+            const int g0 = chunk_of(t) * (kSmChunk / 16) + 2 * h;
+            uint8_t* crow = (uint8_t*)args.a_codes + (int64_t)arow[u] * (K / 2);
+            uint8_t* srow = (uint8_t*)args.a_scales + (int64_t)arow[u] * (K / 16);
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+              if (g0 + g < K / 16) {
+                *(u32x2_t*)(crow + (g0 + g) * 8) = u32x2_t{qa[u].c[2 * g], qa[u].c[2 * g + 1]};
+                srow[g0 + g] = (uint8_t)(qa[u].s >> (8 * g));
+              }
+            }
+          }
+        } else {
+          qa[u] = fa[u];
+        }
+      }
+      half2_t sw[WT], sa[MT];
+#pragma unroll
+      for (int w = 0; w < WT; ++w) sw[w] = sigma_pair<false>(live ? fw[w].s : 0u);
+#pragma unroll
+      for (int u = 0; u < MT; ++u) sa[u] = sigma_pair<false>(qa[u].s);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        half8_t ao[MT];
+#pragma unroll
+        for (int u = 0; u < MT; ++u) ao[u] = dequant8(qa[u].c[q], sa[u][q >> 1]);
+#pragma unroll
+        for (int w = 0; w < WT; ++w) {
+          const half8_t wo = dequant8(fw[w].c[q], sw[w][q >> 1]);
+#pragma unroll
+          for (int u = 0; u < MT; ++u) acc[w][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wo, ao[u], acc[w][u], 0, 0, 0);
+        }
+      }
+    };
+    // two register buffers in turn, one chunk ahead; an odd share ends on a
+    // zeroed chunk
+    if (mine > 0) {
+      for (int t = 0; t < mine; t += 2) {
+        load(t + 1, bw, bx);
+        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before this chunk's math
+        compute(aw, ax, t);
+        load(t + 2, aw, ax);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(bw, bx, t + 1);
+      }
+    }
+  };
+  if constexpr (FUSED) {
+    if (gtab.ovf)
+      run(BoolC<true>{});
+    else
+      run(BoolC<false>{});
+  } else {
+    run(BoolC<false>{});
+  }
+#pragma unroll
+  for (int w = 0; w < WT; ++w)
+#pragma unroll
+    for (int u = 0; u < MT; ++u) red[wave][w * MT + u][lane] = acc[w][u];
+  __syncthreads();
+  // wave v finishes output tiles v, v + 4, ...: the waves' partials in wave
+  // order.  In tile (w, u) lane l holds rows 4 (l >> 4) .. + 3 of W tile w
+  // (output columns) for row l & 15 of A tile u (output row).
+  const float scale = s_ta * grp.w_rec->s_t;
+  for (int tile = wave; tile < NT; tile += kSmWaves) {
+    const int w = tile / MT, u = tile - w * MT;
+    f32x4_t s = red[0][tile][lane];
+#pragma unroll
+    for (int v = 1; v < kSmWaves; ++v) s += red[v][tile][lane];
+    const f32x4_t r = s * scale;
+    const int m = m0 + 16 * u + i;
+    const int n = n0 + 16 * w + 4 * h;
+    if (m < M) {
+      const int64_t off = (int64_t)m * N + n;
+      const bool vec = (N & 3) == 0 && n + 3 < N;
+      if constexpr (OUT_F32) {
+        float* c = (float*)grp.c;
+        if (vec) {
+          *(f32x4_t*)(c + off) = r;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (n + q < N) c[off + q] = r[q];
+        }
+      } else {
+        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+        typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+        const bf16x4_t b = __builtin_convertvector(r, bf16x4_t);
+        uint16_t* c = (uint16_t*)grp.c;
+        if (vec) {
+          *(bf16x4_t*)(c + off) = b;
+        } else {
+          const u16x4_t bb = __builtin_bit_cast(u16x4_t, b);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (n + q < N) c[off + q] = bb[q];
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host --
 
 constexpr int kMaxDevices = 64;
@@ -1007,6 +1278,77 @@ static hipError_t dispatch_flags(const GemmArgs& a, bool out_f32, int d, hipStre
   return out_f32 ? launch_cfg<BM, BN, false, true, FUSED>(a, d, s) : launch_cfg<BM, BN, false, false, FUSED>(a, d, s);
 }
 
+bool gemm_small_rows(int64_t M) { return M <= kSmallMaxRows; }
+
+template <int WT, int MT, bool FAST, bool OUT_F32, bool FUSED, bool WRITE_A>
+static hipError_t launch_small_cfg(const GemmArgs& a0, hipStream_t stream) {
+  GemmArgs a = a0;
+  a.tiles_m = (a.M + 16 * MT - 1) / (16 * MT);
+  int tn = 0;
+  for (int g = 0; g < a.ngroup; ++g) {
+    tn += (a.n[g] + 16 * WT - 1) / (16 * WT);
+    a.tn_end[g] = tn;
+  }
+  a.tiles_n = tn;
+  const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
+  log_launch("gemm_small_kernel", (unsigned)grid, kThreads, 0,
+             "w_rows_per_wg=%d a_rows_per_wg=%d fast=%d out_f32=%d fused=%d write_a=%d M=%d K=%d tiles=%dx%d "
+             "groups=%d",
+             16 * WT, 16 * MT, (int)FAST, (int)OUT_F32, (int)FUSED, (int)WRITE_A, a.M, a.K, a.tiles_m, a.tiles_n,
+             a.ngroup);
+  hipLaunchKernelGGL((gemm_small_kernel<WT, MT, FAST, OUT_F32, FUSED, WRITE_A>), dim3((unsigned)grid),
+                     dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int WT, int MT, bool FAST, bool OUT_F32>
+static hipError_t launch_small_form(const GemmArgs& a, bool fused, bool write_a, hipStream_t s) {
+  if (!fused) return launch_small_cfg<WT, MT, FAST, OUT_F32, false, false>(a, s);
+  if (write_a) return launch_small_cfg<WT, MT, FAST, OUT_F32, true, true>(a, s);
+  return launch_small_cfg<WT, MT, FAST, OUT_F32, true, false>(a, s);
+}
+
+template <int WT, int MT>
+static hipError_t launch_small_wm(const GemmArgs& a, bool fast, bool out_f32, bool fused, bool write_a,
+                                  hipStream_t s) {
+  if (fast)
+    return out_f32 ? launch_small_form<WT, MT, true, true>(a, fused, write_a, s)
+                   : launch_small_form<WT, MT, true, false>(a, fused, write_a, s);
+  return out_f32 ? launch_small_form<WT, MT, false, true>(a, fused, write_a, s)
+                 : launch_small_form<WT, MT, false, false>(a, fused, write_a, s);
+}
+
+// Tiles per workgroup: as many W and A tiles (up to 4 x 4: fewer operand
+// re-reads through L2, fewer dequantizations per MFMA) as still leave a
+// workgroup per CU; below that, the smallest, so that a latency-bound
+// problem spreads over as many CUs as it can.  The tile counts do not
+// change any output element's summation order (that is fixed by the K
+// chunks and the wave order), so every choice gives the same bits.
+static hipError_t launch_small(const GemmArgs& a, const int64_t* n, int ngroup, bool fast, bool out_f32, bool fused,
+                               bool write_a, int num_cu, hipStream_t s) {
+  int wt = 4, mt = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 4;
+  auto grid = [&](int w, int m) {
+    int64_t t = 0;
+    for (int g = 0; g < ngroup; ++g) t += (n[g] + 16 * w - 1) / (16 * w);
+    return t * ((a.M + 16 * m - 1) / (16 * m));
+  };
+  while (grid(wt, mt) < num_cu && (wt > 1 || mt > 1)) {
+    if (wt >= mt) wt /= 2;
+    else mt /= 2;
+  }
+  switch (wt * 8 + mt) {
+    case 4 * 8 + 4: return launch_small_wm<4, 4>(a, fast, out_f32, fused, write_a, s);
+    case 4 * 8 + 2: return launch_small_wm<4, 2>(a, fast, out_f32, fused, write_a, s);
+    case 4 * 8 + 1: return launch_small_wm<4, 1>(a, fast, out_f32, fused, write_a, s);
+    case 2 * 8 + 4: return launch_small_wm<2, 4>(a, fast, out_f32, fused, write_a, s);
+    case 2 * 8 + 2: return launch_small_wm<2, 2>(a, fast, out_f32, fused, write_a, s);
+    case 2 * 8 + 1: return launch_small_wm<2, 1>(a, fast, out_f32, fused, write_a, s);
+    case 1 * 8 + 4: return launch_small_wm<1, 4>(a, fast, out_f32, fused, write_a, s);
+    case 1 * 8 + 2: return launch_small_wm<1, 2>(a, fast, out_f32, fused, write_a, s);
+    default: return launch_small_wm<1, 1>(a, fast, out_f32, fused, write_a, s);
+  }
+}
+
 // Tile shape: estimated time = rounds of workgroups over the CUs x tile
 // area / relative efficiency.  Smaller wave tiles dequantize more operand
 // fragments per MFMA; the efficiencies are measured MI355X rates relative to
@@ -1043,6 +1385,17 @@ hipError_t launch_gemm(const GemmOperandA& A, const GemmWeight* w, int ngroup, i
   }
   a.ngroup = ngroup;
   a.M = (int)M; a.K = (int)K;
+  if (gemm_small_rows(M)) {
+    // whole chunks of K take 16-byte loads (bases are 16-byte aligned and
+    // scale rows then even-sized)
+    const bool fast = K % kSmChunk == 0;
+    const bool fused = A.bf16 != nullptr, write_a = fused && A.out_codes;
+    if (write_a) {
+      a.a_codes = A.out_codes;
+      a.a_scales = A.out_scales;
+    }
+    return launch_small(a, n, ngroup, fast, out_f32, fused, write_a, dev.num_cu, stream);
+  }
   if (A.bf16 && A.out_codes) {
     // fused, A's NVFP4 kept: quantize once per panel, or (other shapes) the
     // standalone encode pass into the same buffers and the plain GEMM

@@ -74,6 +74,9 @@ struct GemmWeight {
   int64_t n;
 };
 
+// Row counts (M) that the small-problem GEMM kernel takes, in every A form:
+// 16 or 32 A rows and 16 W rows per workgroup, K split over its waves.
+bool gemm_small_rows(int64_t M);
 hipError_t launch_gemm(const GemmOperandA& a, const GemmWeight* w, int ngroup, int64_t M, int64_t K, bool out_f32,
                        const DeviceInfo& dev, hipStream_t stream);
 hipError_t launch_gemv(const void* x, const void* w, void* y, int64_t M, int64_t N, int64_t K,

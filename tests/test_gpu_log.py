@@ -45,13 +45,15 @@ def test_log_lists_every_launch():
     kernels = [line.split()[1] for line in lines]
     # weight quantization (300 x 512: amax pass + encode), activation
     # quantization (40 x 512, at most 2^17 elements: the encode kernel takes
-    # the maximum itself, one launch), the GEMM, the GEMV
+    # the maximum itself, one launch), the GEMM (40 rows: the small-problem
+    # kernel: on so few tiles one 16-row W tile and one 16-row A tile per
+    # workgroup, 19 x 3 of them), the GEMV
     assert kernels.count("amax_kernel") == 1 and kernels.count("quantize_kernel") == 2, lines
     quant = [line for line in lines if " quantize_kernel " in line]
     assert "elements=153600 mode=0" in quant[0] and "elements=20480 mode=2" in quant[1], quant
-    assert kernels.count("gemm_nvfp4_kernel") == 1 and kernels.count("gemv_bf16_kernel") == 1, lines
-    gemm = next(line for line in lines if " gemm_nvfp4_kernel " in line)
-    assert "M=40 K=512" in gemm and "grid=" in gemm and "lds=" in gemm
+    assert kernels.count("gemm_small_kernel") == 1 and kernels.count("gemv_bf16_kernel") == 1, lines
+    gemm = next(line for line in lines if " gemm_small_kernel " in line)
+    assert "M=40 K=512" in gemm and "tiles=3x19" in gemm and "grid=57 " in gemm and "lds=" in gemm
 
 
 def test_log_is_silent_by_default():
