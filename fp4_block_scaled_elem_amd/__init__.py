@@ -86,6 +86,10 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise LibraryNotBuilt(
             f"{LIB_PATH} is missing: build it with `python -m fp4_block_scaled_elem_amd.build`")
+    # torch first: its HIP runtime and the one libmq.so links against share a
+    # soname, so whichever loads first serves the process; loaded first, the
+    # library's copy leaves torch's device state invisible to the library
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     i64, u32, vp = ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p
     P = ctypes.POINTER(_NVFP4C)
@@ -135,6 +139,8 @@ def lib():
     L.mq_check_set_quant_spin_limit.restype = u32
     L.mq_check_quant_gave_up.argtypes = []
     L.mq_check_quant_gave_up.restype = u32
+    L.mq_check_set_panel_min_tiles.argtypes = [ctypes.c_int32]
+    L.mq_check_set_panel_min_tiles.restype = ctypes.c_int32
     _lib = L
     return L
 
@@ -477,6 +483,13 @@ def mq_check_quant_gave_up() -> int:
     if n == 0xFFFFFFFF:
         raise MQError(MQ_ERR_DEVICE, "mq_check_quant_gave_up", "HIP symbol copy failed")
     return n
+
+
+def mq_check_set_panel_min_tiles(tiles: int) -> int:
+    """Test support: the column tiles per panel sharer from which the fused
+    quantize-once GEMM takes its panel form (default 4; 1 forces it wherever
+    K allows).  Returns the previous value."""
+    return int(lib().mq_check_set_panel_min_tiles(tiles))
 
 
 def mq_check_mfma_rate(valu_per_mfma: int, iters: int, blocks: int, sink, clocks, stream=None):

@@ -20,9 +20,10 @@
 //   mq_check_dequant_table every (scale byte, code) operand value as
 //                          binary16 bits
 //
-// and two knobs of the single-launch quantizer's bounded wait, so that a test
+// two knobs of the single-launch quantizer's bounded wait, so that a test
 // can force its give-up path (mq_check_set_quant_spin_limit,
-// mq_check_quant_gave_up).
+// mq_check_quant_gave_up), and the fused GEMM's panel-form threshold
+// (mq_check_set_panel_min_tiles).
 #include "mq_device.h"
 #include "mq_internal.h"
 
@@ -134,5 +135,10 @@ uint32_t mq_check_set_quant_spin_limit(uint32_t polls) { return mq::set_rq_spin_
 // Workgroups of the single-launch quantizer that gave up waiting since the
 // last call (the count is reset), ~0u on error.
 uint32_t mq_check_quant_gave_up(void) { return mq::take_rq_gave_up(); }
+
+// The column tiles per panel sharer from which the fused quantize-once GEMM
+// takes its panel form (1: wherever K allows, so that tests reach it at
+// small shapes); returns the previous value.  Process-wide.
+int32_t mq_check_set_panel_min_tiles(int32_t tiles) { return mq::set_panel_min_tiles(tiles); }
 
 }  // extern "C"

@@ -27,6 +27,8 @@
 // scales and first operands are prepared inside the current stage, so the
 // MFMA stream only pauses at the one barrier per stage.  The K order inside
 // a stage is permuted identically for A and W (the sum is unchanged).
+#include <atomic>
+
 #include "mq_device.h"
 #include "mq_internal.h"
 
@@ -941,17 +943,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_panel_kernel(GemmArgs args, 
 // prompt's M rows; chosen by row count alone, gemm_small_rows): a workgroup
 // owns 16 * WT rows of W and 16 * MT rows of A, its four waves take the K
 // chunks (128 elements) in turn, and their partial tiles are summed through
-// LDS in wave order (deterministic).  The arithmetic is the tiled kernel's (exact
-// binary16 operands g * sigma, binary32 accumulation, the sum scaled by
-// fp32(s_tA * s_tW) and rounded to nearest-even bf16), here on
+// LDS in wave order (deterministic).  The arithmetic is the tiled kernel's
+// (exact binary16 operands g * sigma, binary32 accumulation, the sum scaled
+// by fp32(s_tA * s_tW) and rounded to nearest-even bf16), here on
 // v_mfma_f32_16x16x32_f16: lane (i, h) holds row i's chunk elements
 // 32h .. 32h + 31 (groups 2h and 2h + 1, eight elements per MFMA step) of
 // both operands, so the K order is the same for A and W.  A comes packed,
 // or (FUSED) as bf16 that each workgroup quantizes in registers by the
-// quantizer's rules; with WRITE_A the workgroups of the first W tile also
-// store A's NVFP4 (standard layout).  The summation order differs from the
-// tiled kernel's: results agree with it within the GEMM tolerance, and with
-// this kernel bit for bit across the A forms, groupings and streams.
+// quantizer's rules; with WRITE_A the workgroups also store A's NVFP4
+// (standard layout), each chunk of it once.  The summation order differs
+// from the tiled kernel's: results agree with it within the GEMM
+// tolerance, and with this kernel bit for bit across the A forms,
+// groupings and streams.
 constexpr int kSmChunk = 128;                      // K elements per chunk
 constexpr int kSmWaves = kThreads / 64;            // four: the chunks of K in turn
 constexpr int kSmallMaxRows = 128;                 // gemm_small_rows
@@ -1060,8 +1063,9 @@ __global__ __launch_bounds__(kThreads) void gemm_small_kernel(GemmArgs args) {
   for (int u = 0; u < MT; ++u) arow[u] = min(m0 + 16 * u + i, M - 1);
   const int nchunks = (K + kSmChunk - 1) / kSmChunk;
   const int mine = nchunks > wave ? (nchunks - wave + kSmWaves - 1) / kSmWaves : 0;  // this wave's chunks
-  // the first W tiles' workgroups store A's NVFP4 (each A row once)
-  const bool store_a = WRITE_A && tn == 0;
+  // A's NVFP4 is stored once: chunk c of an A tile by the workgroup of W
+  // tile c mod tiles_n (spread over the grid, so that no workgroup waits
+  // for all of a row's stores)
 
   f32x4_t acc[WT][MT];
 #pragma unroll
@@ -1102,15 +1106,21 @@ __global__ __launch_bounds__(kThreads) void gemm_small_kernel(GemmArgs args) {
       for (int u = 0; u < MT; ++u) {
         if constexpr (FUSED) {
           qa[u] = sm_quantize<OVF>(fa[u], gtab);
-          if (store_a && live && m0 + 16 * u + i < M) {
+          if (WRITE_A && live && chunk_of(t) % args.tiles_n == tn && m0 + 16 * u + i < M) {
             const int g0 = chunk_of(t) * (kSmChunk / 16) + 2 * h;
             uint8_t* crow = (uint8_t*)args.a_codes + (int64_t)arow[u] * (K / 2);
             uint8_t* srow = (uint8_t*)args.a_scales + (int64_t)arow[u] * (K / 16);
+            if constexpr (FAST) {
+              // whole chunks: 16-byte aligned codes, 2-byte aligned scales
+              *(u32x4_t*)(crow + g0 * 8) = u32x4_t{qa[u].c[0], qa[u].c[1], qa[u].c[2], qa[u].c[3]};
+              *(uint16_t*)(srow + g0) = (uint16_t)qa[u].s;
+            } else {
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
-              if (g0 + g < K / 16) {
-                *(u32x2_t*)(crow + (g0 + g) * 8) = u32x2_t{qa[u].c[2 * g], qa[u].c[2 * g + 1]};
-                srow[g0 + g] = (uint8_t)(qa[u].s >> (8 * g));
+              for (int g = 0; g < 2; ++g) {
+                if (g0 + g < K / 16) {
+                  *(u32x2_t*)(crow + (g0 + g) * 8) = u32x2_t{qa[u].c[2 * g], qa[u].c[2 * g + 1]};
+                  srow[g0 + g] = (uint8_t)(qa[u].s >> (8 * g));
+                }
               }
             }
           }
@@ -1371,6 +1381,25 @@ static int pick_tile(int64_t M, const int64_t* N, int ngroup, int64_t K, int num
   return best;
 }
 
+// The quantize-once form runs one fused tile per sharer of a panel, which
+// takes about 1.4 plain tiles' time: it pays only where each sharer goes on
+// to enough plain tiles (measured at M = 32768: 4 tiles per sharer 6.6%, 8
+// tiles 0.5-3% behind the separate encode pass + plain GEMM; at M = 4096
+// and below, with one tile per sharer, up to 3.7x behind).  Elsewhere the
+// call takes the separate path, whose output is bit-identical.
+static std::atomic<int> g_panel_min_tiles{4};
+
+int set_panel_min_tiles(int tiles) { return g_panel_min_tiles.exchange(tiles); }
+
+static bool panel_pays(int64_t M, const int64_t* n, int ngroup, int num_cu) {
+  const int64_t tiles_m = (M + 255) / 256;
+  int64_t tn = 0;
+  for (int g = 0; g < ngroup; ++g) tn += (n[g] + 255) / 256;
+  int64_t per = num_cu / tiles_m;
+  per = per < 1 ? 1 : (per > tn ? tn : per);
+  return (tn + per - 1) / per >= g_panel_min_tiles.load();
+}
+
 hipError_t launch_gemm(const GemmOperandA& A, const GemmWeight* w, int ngroup, int64_t M, int64_t K, bool out_f32,
                        const DeviceInfo& dev, hipStream_t stream) {
   GemmArgs a{};
@@ -1397,11 +1426,12 @@ hipError_t launch_gemm(const GemmOperandA& A, const GemmWeight* w, int ngroup, i
     return launch_small(a, n, ngroup, fast, out_f32, fused, write_a, dev.num_cu, stream);
   }
   if (A.bf16 && A.out_codes) {
-    // fused, A's NVFP4 kept: quantize once per panel, or (other shapes) the
-    // standalone encode pass into the same buffers and the plain GEMM
+    // fused, A's NVFP4 kept: quantize once per panel, or (other shapes, and
+    // where the panel form does not pay) the standalone encode pass into the
+    // same buffers and the plain GEMM
     bool fast = fast_shape(K) && ((uintptr_t)A.out_codes & 15) == 0 && ((uintptr_t)A.out_scales & 15) == 0;
     for (int g = 0; g < ngroup; ++g) fast = fast && ((uintptr_t)a.w_scales[g] & 15) == 0;
-    if (fast)
+    if (fast && panel_pays(M, n, ngroup, dev.num_cu))
       return out_f32 ? launch_panel<true>(a, A.out_codes, A.out_scales, dev, stream)
                      : launch_panel<false>(a, A.out_codes, A.out_scales, dev, stream);
     hipError_t e = launch_quantize(A.bf16, M * K, A.out_codes, A.out_scales, A.rec, A.given, dev, stream);

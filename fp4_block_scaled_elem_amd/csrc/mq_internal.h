@@ -74,6 +74,10 @@ struct GemmWeight {
   int64_t n;
 };
 
+// Test support: the column tiles each sharer of a 256-row panel must get for
+// the fused quantize-once launch to take the panel form (default 4; 1 forces
+// it wherever K allows); returns the previous value.
+int set_panel_min_tiles(int tiles);
 // Row counts (M) that the small-problem GEMM kernel takes, in every A form:
 // 16 or 32 A rows and 16 W rows per workgroup, K split over its waves.
 bool gemm_small_rows(int64_t M);

@@ -11,6 +11,13 @@ against the oracle here too.  Shapes cover one tile per workgroup, several
 panels with a ragged last one, the loop over several column tiles per
 workgroup (M = 32768: two workgroups per panel), ragged K (the fallback),
 grouped launches, a given tensor scale and a producer's partial maxima.
+
+By default the library takes the panel form only where each workgroup of a
+panel gets at least four column tiles (M of about 16384 and more); these
+tests lower that threshold to one tile (a test-support knob) so that the
+panel kernel runs at their small shapes, and one test checks the default
+routing of a small panel count (the separate path) against the forced panel
+form, bit for bit.
 """
 
 import numpy as np
@@ -27,6 +34,14 @@ pytestmark = pytest.mark.gpu
 def _mq():
     import fp4_block_scaled_elem_amd as mq
     return mq
+
+
+@pytest.fixture(autouse=True)
+def _panel_form_everywhere():
+    mq = _mq()
+    old = mq.mq_check_set_panel_min_tiles(1)
+    yield
+    mq.mq_check_set_panel_min_tiles(old)
 
 
 def _run_panel(x, ws, M, f32=False, flags=0, a=None):
@@ -193,3 +208,23 @@ def test_linear_fused_with_work_buffers_takes_the_panel_form():
     torch.cuda.synchronize()
     assert _same(y, y2)
     assert _same_quantization(aw, qa)
+
+
+@pytest.mark.parametrize("M,Ns,K", [(256, (4096,), 4096), (1000, (520, 300), 1024)])
+def test_default_routing_matches_forced_panel_form(M, Ns, K):
+    # one or two 256-row panels: with the default threshold the call takes
+    # the encode pass and the plain GEMM (far faster there); its output and
+    # A's bytes equal the forced panel form's and the standalone quantizer's
+    announce("panel threshold: default vs forced", M, Ns, K)
+    mq = _mq()
+    x = to_dev_bf16(workloads.random_bf16((M, K), 90 + M, 1.0, "lognormal_mixed"))
+    ws = [mq.quantize(to_dev_bf16(workloads.random_bf16((n, K), 91 + g, 0.02))) for g, n in enumerate(Ns)]
+    cs_forced, a_forced = _run_panel(x, ws, M)
+    old = mq.mq_check_set_panel_min_tiles(4)
+    try:
+        cs_default, a_default = _run_panel(x, ws, M)
+    finally:
+        mq.mq_check_set_panel_min_tiles(old)
+    qa = mq.quantize(x)
+    assert all(_same(c1, c2) for c1, c2 in zip(cs_forced, cs_default))
+    assert _same_quantization(a_forced, qa) and _same_quantization(a_default, qa)

@@ -120,7 +120,13 @@ def test_fused_prologue_gemm_replay(form):
     c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     rec = torch.zeros(mq.REC_BYTES // 4, dtype=torch.int32, device="cuda")
     keep = mq.NVFP4.empty(M, K) if form == "panel" else None
-    g = _capture(lambda: mq.prefill_linear(x, w, out=c, fused=True, rec=rec, keep_a=keep))
+    # one panel of two column tiles: the panel form only when forced (by
+    # default this shape takes the encode pass and the plain GEMM)
+    old = mq.mq_check_set_panel_min_tiles(1)
+    try:
+        g = _capture(lambda: mq.prefill_linear(x, w, out=c, fused=True, rec=rec, keep_a=keep))
+    finally:
+        mq.mq_check_set_panel_min_tiles(old)
     for r in range(REPLAYS):
         xr = to_dev_bf16(workloads.random_bf16((M, K), 20 + r, 0.5 + r, "lognormal_mixed"))
         x.copy_(xr)

@@ -6,8 +6,9 @@ Its output must equal, bit for bit, what the existing entry point
 mq_gemm_nvfp4_prefill with MQ_A_FUSED_BF16 writes with caller-owned buffers
 (the same kernels run), over two calls in a row on the shared buffer, the
 second smaller than the first, in both forms the fused path takes (the
-quantize-once panel form for K % 256 == 0, the encode pass then the plain
-GEMM otherwise) and both output types; one case is also held to the oracle.
+quantize-once panel form, forced at these sizes through a test knob, and the
+encode pass then the plain GEMM, the default here and for ragged K) and
+both output types; one case is also held to the oracle.
 """
 
 import numpy as np
@@ -48,8 +49,16 @@ def _case(M, N, K, seed, f32=False):
 @pytest.mark.parametrize("f32", [False, True], ids=["bf16", "f32"])
 def test_two_calls_second_smaller(f32):
     announce("noalloc two calls", "f32" if f32 else "bf16")
-    xa, xw, c = _case(1000, 520, 1024, 11, f32)      # quantize-once form, 4 panels
-    _case(300, 300, 512, 12, f32)                     # smaller, same form
+    mq = _mq()
+    # at these sizes the library takes the encode pass and the plain GEMM by
+    # default; the threshold knob forces the panel form for the first two
+    old = mq.mq_check_set_panel_min_tiles(1)
+    try:
+        xa, xw, c = _case(1000, 520, 1024, 11, f32)  # quantize-once panel form, 4 panels
+        _case(300, 300, 512, 12, f32)                 # smaller, same form
+    finally:
+        mq.mq_check_set_panel_min_tiles(old)
+    _case(1000, 520, 1024, 14, f32)                   # default: encode pass, then the plain GEMM
     _case(130, 200, 272, 13, f32)                     # ragged K: encode pass, then the plain GEMM
     if not f32:
         r = rule_t(bf16_dev_to_f64(c), oracle.gemm_nvfp4_ref(oracle.quantize_nvfp4(xa), oracle.quantize_nvfp4(xw)),
