@@ -67,6 +67,8 @@ def parse():
     p.add_argument("--cpu-wrows", type=int, default=4096, help="weight rows per projection in the CPU sample")
     p.add_argument("--layer", action="store_true",
                    help="only the decoder-layer prefill context measurement (NVFP4 vs BF16 linears)")
+    p.add_argument("--single-linear", action="store_true",
+                   help="only the one-linear configuration (M=128, K=N=512): per-call latency of each form")
     p.add_argument("--decode-only", action="store_true",
                    help="only measure the BF16 decode GEMV at the decode shapes (one JSON line, not the step metric)")
     p.add_argument("--peak", action="store_true",
@@ -825,6 +827,9 @@ def main():
         return
     if args.layer:
         print(json.dumps({"layer_prefill": layer_prefill()}), flush=True)
+        return
+    if args.single_linear:
+        print(json.dumps({"single_linear_m128": single_linear_latency()}), flush=True)
         return
     if args.decode_only:
         gemv = decode_gemv_rates()

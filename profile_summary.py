@@ -29,6 +29,12 @@ fp16 MFMA rate kernel per VALU load).
 of the same bench.py command with the counter sets COUNTERS_P1 and
 COUNTERS_P2, and commands.txt; writes profiles/counters_<workload>.txt
 (MFMA, VALU and LDS counters per kind of launch).
+
+    python profile_summary.py --trace <run_dir> <workload-name>
+
+<run_dir>/ktcsv/ holds a --kernel-trace --stats --output-format csv run and
+commands.txt its command; writes profiles/kernels_<workload>.txt (kernel
+durations only).
 """
 
 from __future__ import annotations
@@ -48,7 +54,7 @@ GEMM_SRC = os.path.join(ROOT, "fp4_block_scaled_elem_amd", "csrc", "gemm.hip")
 
 # the prefill GEMM's kernels: one tile per workgroup, and the fused
 # prologue's quantize-once form
-GEMM_KERNELS = ("gemm_nvfp4_kernel", "gemm_panel_kernel")
+GEMM_KERNELS = ("gemm_nvfp4_kernel", "gemm_panel_kernel", "gemm_small_kernel")
 
 
 def source_hash(path=GEMM_SRC) -> str:
@@ -72,6 +78,24 @@ def pmc(db_dir: str):
                 "select kernel_name, grid_size, counter_name, value from counters_collection"):
             out[(short(name), grid, cnt)].append(val)
     return out
+
+
+def trace_main(run: str, workload: str):
+    """Kernel durations only (a --kernel-trace --stats run in <run>/ktcsv)."""
+    stats = list(csv.DictReader(open(glob.glob(os.path.join(run, "ktcsv", "**", "*kernel_stats.csv"),
+                                               recursive=True)[0])))
+    commands = open(os.path.join(run, "commands.txt")).read().strip()
+    lines = [f"# rocprofv3 summary: {workload}", "",
+             "Command (run from the repository root on one MI355X):", "", commands, "",
+             f"gemm.hip code digest (sha256[:16], comments and whitespace ignored) = {source_hash()}", "",
+             "## Kernel trace (--kernel-trace --stats)", "",
+             f"{'kernel':72s} {'calls':>5s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'share%':>7s}"]
+    for r in stats:
+        lines.append(f"{short(r['Name'])[:72]:72s} {int(r['Calls']):5d} {float(r['AverageNs'])/1e3:9.2f} "
+                     f"{float(r['MinNs'])/1e3:9.2f} {float(r['MaxNs'])/1e3:9.2f} {float(r['Percentage']):7.2f}")
+    path = os.path.join(ROOT, "profiles", f"kernels_{workload}.txt")
+    open(path, "w").write("\n".join(lines) + "\n")
+    print(path)
 
 
 def main():
@@ -259,6 +283,8 @@ def peak_main(run: str):
 if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "--counters":
         counters_main(sys.argv[2], sys.argv[3])
+    elif len(sys.argv) > 1 and sys.argv[1] == "--trace":
+        trace_main(sys.argv[2], sys.argv[3])
     elif len(sys.argv) > 1 and sys.argv[1] == "--peak":
         peak_main(sys.argv[2])
     else:
