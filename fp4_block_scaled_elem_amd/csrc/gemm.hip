@@ -1331,7 +1331,9 @@ static hipError_t launch_small_wm(const GemmArgs& a, bool fast, bool out_f32, bo
 // Tiles per workgroup: as many W and A tiles (up to 4 x 4: fewer operand
 // re-reads through L2, fewer dequantizations per MFMA) as still leave a
 // workgroup per CU; below that, the smallest, so that a latency-bound
-// problem spreads over as many CUs as it can.  The tile counts do not
+// problem spreads over as many CUs as it can.  Halving the larger count
+// first reaches 4x4, 2x4, 2x2, 1x2, 1x1 (M > 32), 4x2, 2x2, 1x2, 1x1
+// (17..32 rows) or 4x1, 2x1, 1x1 (M <= 16).  The tile counts do not
 // change any output element's summation order (that is fixed by the K
 // chunks and the wave order), so every choice gives the same bits.
 static hipError_t launch_small(const GemmArgs& a, const int64_t* n, int ngroup, bool fast, bool out_f32, bool fused,
@@ -1353,7 +1355,6 @@ static hipError_t launch_small(const GemmArgs& a, const int64_t* n, int ngroup, 
     case 2 * 8 + 4: return launch_small_wm<2, 4>(a, fast, out_f32, fused, write_a, s);
     case 2 * 8 + 2: return launch_small_wm<2, 2>(a, fast, out_f32, fused, write_a, s);
     case 2 * 8 + 1: return launch_small_wm<2, 1>(a, fast, out_f32, fused, write_a, s);
-    case 1 * 8 + 4: return launch_small_wm<1, 4>(a, fast, out_f32, fused, write_a, s);
     case 1 * 8 + 2: return launch_small_wm<1, 2>(a, fast, out_f32, fused, write_a, s);
     default: return launch_small_wm<1, 1>(a, fast, out_f32, fused, write_a, s);
   }

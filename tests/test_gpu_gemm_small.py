@@ -194,3 +194,72 @@ def test_cfg1_single_linear_one_launch_every_form():
     assert np.array_equal(keep.codes.cpu().numpy(), oa.codes)
     assert np.array_equal(keep.scales.cpu().numpy(), oa.scales)
     _rule_t(_out(y_sep), oracle.gemm_nvfp4_ref(oa, ow), True)
+
+
+# (M, N, K) -> (W rows, A rows) per workgroup the tile choice takes on 256
+# CUs: every reachable combination, with ragged N (a W tile group cut short)
+# and ragged K among them
+TILE_CASES = [
+    ((128, 8192, 256), (64, 64)), ((128, 8232, 272), (64, 64)), ((128, 4096, 256), (32, 64)),
+    ((128, 2048, 256), (32, 32)), ((100, 2056, 512), (32, 32)), ((32, 16384, 256), (64, 32)),
+    ((16, 16384, 256), (64, 16)), ((8, 8192, 256), (32, 16)), ((5, 8200, 144), (32, 16)),
+]
+
+
+@pytest.mark.parametrize("shape,rows", TILE_CASES, ids=[f"{m}x{n}x{k}" for (m, n, k), _ in TILE_CASES])
+def test_small_every_tile_choice(shape, rows):
+    # packed, fused and quantize-once forms bit for bit, the stored A bytes,
+    # and rule T on sampled output columns against the oracle
+    M, N, K = shape
+    announce("gemm small tiles", M, N, K, rows)
+    import torch
+    mq = _mq()
+    xa = workloads.random_bf16((M, K), 700 + N, 1.0, "lognormal_mixed")
+    xw = workloads.random_bf16((N, K), 701 + N, 0.02)
+    oa = oracle.quantize_nvfp4(xa)
+    qa = upload_nvfp4(oa)
+    qw = mq.quantize(to_dev_bf16(xw))
+    x = to_dev_bf16(xa)
+    c_packed, c_fused, c_once = _c(M, N, False), _c(M, N, False), _c(M, N, False)
+    mq.mq_gemm_nvfp4_prefill(qa, None, qw, c_packed, 0)
+    mq.mq_gemm_nvfp4_prefill(mq.NVFP4(None, None, _rec()), x, qw, c_fused, mq.MQ_A_FUSED_BF16)
+    a_once = mq.NVFP4.empty(M, K)
+    mq.mq_gemm_nvfp4_prefill(a_once, x, qw, c_once, mq.MQ_A_FUSED_BF16)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(c_packed), _bits(c_fused)) and torch.equal(_bits(c_packed), _bits(c_once))
+    assert np.array_equal(a_once.codes.cpu().numpy(), oa.codes)
+    assert np.array_equal(a_once.scales.cpu().numpy(), oa.scales)
+    rng = np.random.default_rng(N)
+    cols = np.unique(np.concatenate([rng.choice(N, 700, replace=False), [0, N - 1]]))
+    ref = oracle.gemm_nvfp4_ref(oa, oracle.quantize_nvfp4(xw, rows=cols))
+    got = bf16_dev_to_f64(c_packed[:, torch.from_numpy(cols).cuda()])
+    _rule_t(got, ref, True)
+
+
+def test_tile_choice_as_logged():
+    # MQ_LOG names each launch's workgroup rows: the cases above reach the
+    # combinations they are listed with (a child process: the flag is read
+    # once per process)
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    shapes = [s for s, _ in TILE_CASES]
+    script = (
+        "import sys; sys.path.insert(0, {root!r})\n"
+        "import torch\nimport fp4_block_scaled_elem_amd as mq\n"
+        "for M, N, K in {shapes!r}:\n"
+        "    qa = mq.quantize(torch.randn(M, K, device='cuda').to(torch.bfloat16))\n"
+        "    qw = mq.quantize(torch.randn(N, K, device='cuda').to(torch.bfloat16))\n"
+        "    c = torch.empty((M, N), dtype=torch.bfloat16, device='cuda')\n"
+        "    mq.mq_gemm_nvfp4_prefill(qa, None, qw, c, 0)\n"
+        "torch.cuda.synchronize()\nprint('done', flush=True)\n").format(root=root, shapes=shapes)
+    env = dict(os.environ, MQ_LOG="1")
+    r = subprocess.run([sys.executable, "-c", script], env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "done" in r.stdout, r.stderr[-2000:]
+    got = []
+    for line in r.stderr.splitlines():
+        if line.startswith("mq: gemm_small_kernel "):
+            f = dict(kv.split("=") for kv in line.split()[2:] if "=" in kv)
+            got.append((int(f["w_rows_per_wg"]), int(f["a_rows_per_wg"])))
+    assert got == [rows for _, rows in TILE_CASES], got
