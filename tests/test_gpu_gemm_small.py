@@ -243,6 +243,9 @@ def test_tile_choice_as_logged():
     import os
     import subprocess
     import sys
+    import torch
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the expected choices are those of a 256-CU MI355X")
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     shapes = [s for s, _ in TILE_CASES]
     script = (
