@@ -172,23 +172,30 @@ mq_status mq_quantize_nvfp4(const void* x_bf16, int64_t rows, int64_t cols,
  *   Deployment, prefill workers).  Every product uses the exact dequantized
  *   operands g*sigma; accumulation is binary32; the result is multiplied by
  *   s_tA*s_tW and rounded to nearest-even bf16 (or stored as binary32 with
- *   MQ_OUT_F32).  No bias.
+ *   MQ_OUT_F32).  No bias.  Up to M = 128 every form of the call runs one
+ *   small-problem kernel that splits K over its waves (its sums are ordered
+ *   differently from the tiled kernel's, so results for M <= 128 and M > 128
+ *   agree within the GEMM tolerance, not bit for bit; at any one M every
+ *   form, grouping and stream gives the same bits).
  * a        HOST pointer to the quantized activations (codes, scales, rec;
  *          rec->s_t must already hold A's scale, e.g. from
  *          mq_quantize_nvfp4 earlier on the same stream).  With
  *          MQ_A_FUSED_BF16, a->rec receives the amax pass of a_bf16 (or
- *          supplies s_t under MQ_SCALE_GIVEN; when a->codes is NULL and
- *          M*K <= 2^17 there is no amax pass: every workgroup of the GEMM
- *          takes max|a_bf16| itself, and a->rec receives s_t and amax_bits
- *          only, so the whole call is one launch) and a->codes / a->scales are
+ *          supplies s_t under MQ_SCALE_GIVEN; when M*K <= 2^17 and either
+ *          a->codes is NULL or M <= 128 there is no amax pass: every
+ *          workgroup of the GEMM takes max|a_bf16| itself, and a->rec
+ *          receives s_t and amax_bits only, so the whole call is one launch)
+ *          and a->codes / a->scales are
  *          either both NULL (every A tile is re-quantized inside the GEMM's
  *          pipeline for each column tile) or both given, [M][K/2] and
  *          [M][K/16] bytes, 16- and 8-byte aligned: then A's NVFP4 is
  *          written there (the bytes mq_quantize_nvfp4 writes) and each
  *          workgroup quantizes the 256-row panel of A it reads once, in its
  *          first tile, and copies it from there for its other tiles (the
- *          faster form for long activations; shapes outside the direct-copy
- *          path run the encode pass into the buffers, then the plain GEMM).
+ *          form for long activations, taken where each panel's workgroups
+ *          get at least four column tiles; other shapes, and those outside
+ *          the direct-copy path, run the encode pass into the buffers, then
+ *          the plain GEMM, with the same result).
  *          Nothing else may read or write those buffers during the call.
  * a_bf16   DEVICE bf16 [M][K], 16-byte aligned; only with MQ_A_FUSED_BF16,
  *          else must be NULL.  The fused path computes exactly the codes
