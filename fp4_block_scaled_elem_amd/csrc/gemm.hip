@@ -1044,8 +1044,11 @@ __device__ __forceinline__ SmFrag sm_quantize(const SmRaw& r, const GroupScaleTa
   return f;
 }
 
+// Packed A: registers held to two workgroups per CU (more waves to hide the
+// loads' latency: 128 x 28672 x 4096 71.9 -> 67.7 us); the fused forms keep
+// the whole register file (held to two, they spill: 64 -> 96 us).
 template <int WT, int MT, bool FAST, bool OUT_F32, bool FUSED, bool WRITE_A>
-__global__ __launch_bounds__(kThreads) void gemm_small_kernel(GemmArgs args) {
+__global__ __launch_bounds__(kThreads, FUSED ? 1 : 2) void gemm_small_kernel(GemmArgs args) {
   typedef typename SmA<FUSED>::T AFrag;
   constexpr int NT = WT * MT;  // 16x16 output tiles per workgroup
   __shared__ f32x4_t red[kSmWaves][NT][64];
@@ -1313,9 +1316,15 @@ static hipError_t launch_small_cfg(const GemmArgs& a0, hipStream_t stream) {
 
 template <int WT, int MT, bool FAST, bool OUT_F32>
 static hipError_t launch_small_form(const GemmArgs& a, bool fused, bool write_a, hipStream_t s) {
-  if (!fused) return launch_small_cfg<WT, MT, FAST, OUT_F32, false, false>(a, s);
-  if (write_a) return launch_small_cfg<WT, MT, FAST, OUT_F32, true, true>(a, s);
-  return launch_small_cfg<WT, MT, FAST, OUT_F32, true, false>(a, s);
+  if constexpr (MT > 2) {
+    // the fused forms take at most two A tiles (launch_small)
+    if (fused) return hipErrorInvalidValue;
+    return launch_small_cfg<WT, MT, FAST, OUT_F32, false, false>(a, s);
+  } else {
+    if (!fused) return launch_small_cfg<WT, MT, FAST, OUT_F32, false, false>(a, s);
+    if (write_a) return launch_small_cfg<WT, MT, FAST, OUT_F32, true, true>(a, s);
+    return launch_small_cfg<WT, MT, FAST, OUT_F32, true, false>(a, s);
+  }
 }
 
 template <int WT, int MT>
@@ -1333,12 +1342,16 @@ static hipError_t launch_small_wm(const GemmArgs& a, bool fast, bool out_f32, bo
 // workgroup per CU; below that, the smallest, so that a latency-bound
 // problem spreads over as many CUs as it can.  Halving the larger count
 // first reaches 4x4, 2x4, 2x2, 1x2, 1x1 (M > 32), 4x2, 2x2, 1x2, 1x1
-// (17..32 rows) or 4x1, 2x1, 1x1 (M <= 16).  The tile counts do not
-// change any output element's summation order (that is fixed by the K
-// chunks and the wave order), so every choice gives the same bits.
+// (17..32 rows) or 4x1, 2x1, 1x1 (M <= 16).  The fused forms, whose
+// workgroups also quantize their A rows, start from two A tiles (measured
+// 18-26% faster at 128 x 4096 x 4096, 64 x 14336 x 4096 and
+// 128 x 4096 x 14336, 9% slower at 128 x 14336 x 4096; packed A is 35%
+// slower that way at the wide weights).  The tile counts do not change
+// any output element's summation order (that is fixed by the K chunks and
+// the wave order), so every choice gives the same bits.
 static hipError_t launch_small(const GemmArgs& a, const int64_t* n, int ngroup, bool fast, bool out_f32, bool fused,
                                bool write_a, int num_cu, hipStream_t s) {
-  int wt = 4, mt = a.M <= 16 ? 1 : a.M <= 32 ? 2 : 4;
+  int wt = 4, mt = a.M <= 16 ? 1 : (a.M <= 32 || fused) ? 2 : 4;
   auto grid = [&](int w, int m) {
     int64_t t = 0;
     for (int g = 0; g < ngroup; ++g) t += (n[g] + 16 * w - 1) / (16 * w);

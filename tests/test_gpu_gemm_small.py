@@ -197,17 +197,20 @@ def test_cfg1_single_linear_one_launch_every_form():
 
 
 # (M, N, K) -> (W rows, A rows) per workgroup the tile choice takes on 256
-# CUs: every reachable combination, with ragged N (a W tile group cut short)
-# and ragged K among them
+# CUs for packed A, then for the fused forms (at most two A tiles): every
+# reachable combination, with ragged N (a W tile group cut short) and ragged
+# K among them
 TILE_CASES = [
-    ((128, 8192, 256), (64, 64)), ((128, 8232, 272), (64, 64)), ((128, 4096, 256), (32, 64)),
-    ((128, 2048, 256), (32, 32)), ((100, 2056, 512), (32, 32)), ((32, 16384, 256), (64, 32)),
-    ((16, 16384, 256), (64, 16)), ((8, 8192, 256), (32, 16)), ((5, 8200, 144), (32, 16)),
+    ((128, 8192, 256), (64, 64), (64, 32)), ((128, 8232, 272), (64, 64), (64, 32)),
+    ((128, 4096, 256), (32, 64), (64, 32)), ((128, 2048, 256), (32, 32), (32, 32)),
+    ((100, 2056, 512), (32, 32), (32, 32)), ((32, 16384, 256), (64, 32), (64, 32)),
+    ((16, 16384, 256), (64, 16), (64, 16)), ((8, 8192, 256), (32, 16), (32, 16)),
+    ((5, 8200, 144), (32, 16), (32, 16)),
 ]
 
 
-@pytest.mark.parametrize("shape,rows", TILE_CASES, ids=[f"{m}x{n}x{k}" for (m, n, k), _ in TILE_CASES])
-def test_small_every_tile_choice(shape, rows):
+@pytest.mark.parametrize("shape,rows,fused_rows", TILE_CASES, ids=[f"{m}x{n}x{k}" for (m, n, k), _, _ in TILE_CASES])
+def test_small_every_tile_choice(shape, rows, fused_rows):
     # packed, fused and quantize-once forms bit for bit, the stored A bytes,
     # and rule T on sampled output columns against the oracle
     M, N, K = shape
@@ -238,8 +241,8 @@ def test_small_every_tile_choice(shape, rows):
 
 def test_tile_choice_as_logged():
     # MQ_LOG names each launch's workgroup rows: the cases above reach the
-    # combinations they are listed with (a child process: the flag is read
-    # once per process)
+    # combinations they are listed with, packed and fused (a child process:
+    # the flag is read once per process)
     import os
     import subprocess
     import sys
@@ -247,15 +250,17 @@ def test_tile_choice_as_logged():
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the expected choices are those of a 256-CU MI355X")
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    shapes = [s for s, _ in TILE_CASES]
+    shapes = [s for s, _, _ in TILE_CASES]
     script = (
         "import sys; sys.path.insert(0, {root!r})\n"
         "import torch\nimport fp4_block_scaled_elem_amd as mq\n"
         "for M, N, K in {shapes!r}:\n"
-        "    qa = mq.quantize(torch.randn(M, K, device='cuda').to(torch.bfloat16))\n"
+        "    x = torch.randn(M, K, device='cuda').to(torch.bfloat16)\n"
+        "    qa = mq.quantize(x)\n"
         "    qw = mq.quantize(torch.randn(N, K, device='cuda').to(torch.bfloat16))\n"
         "    c = torch.empty((M, N), dtype=torch.bfloat16, device='cuda')\n"
         "    mq.mq_gemm_nvfp4_prefill(qa, None, qw, c, 0)\n"
+        "    mq.prefill_linear(x, qw, out=c, fused=True)\n"
         "torch.cuda.synchronize()\nprint('done', flush=True)\n").format(root=root, shapes=shapes)
     env = dict(os.environ, MQ_LOG="1")
     r = subprocess.run([sys.executable, "-c", script], env=env, capture_output=True, text=True, timeout=300)
@@ -265,4 +270,5 @@ def test_tile_choice_as_logged():
         if line.startswith("mq: gemm_small_kernel "):
             f = dict(kv.split("=") for kv in line.split()[2:] if "=" in kv)
             got.append((int(f["w_rows_per_wg"]), int(f["a_rows_per_wg"])))
-    assert got == [rows for _, rows in TILE_CASES], got
+    want = [r for _, packed, fused in TILE_CASES for r in (packed, fused)]
+    assert got == want, got
