@@ -552,8 +552,10 @@ def producer_fused_rates(reps=50):
     For each: the producer with its partial maxima (GB/s over its bytes: 2
     read + 2 written per element for RMSNorm, 4 + 2 for SwiGLU), then the
     quantization of its output by the two-pass quantizer and by the encode
-    pass alone from the producer's partials (bit-identical results).  Inputs
-    rotate over copies past the Infinity Cache."""
+    pass alone from the producer's partials (bit-identical results); for
+    RMSNorm also the op fused with the quantization, whose bf16 output never
+    goes to HBM (the same codes).  Inputs rotate over copies past the
+    Infinity Cache."""
     import torch
     import fp4_block_scaled_elem_amd as mq
     res = {}
@@ -579,6 +581,14 @@ def producer_fused_rates(reps=50):
         res[name] = {"producer_us": round(tp, 2), "producer_GBps": round(nbytes / tp / 1e3, 1),
                      "quant_two_pass_us": round(t2, 2), "quant_from_partials_us": round(t1, 2),
                      "saved_us": round(t2 - t1, 2)}
+        if not swiglu:
+            # the RMSNorm fused with quantization (its bf16 output never
+            # stored): 2 + 2 + 0.5625 bytes per element over its two passes
+            qf = mq.NVFP4.empty(rows, cols)
+            tf, _ = _median_us(lambda r: mq.mq_rmsnorm_quantize_nvfp4(ins[r % ncopy], g, qf), reps=reps)
+            fbytes = rows * cols * 4.5625
+            res[name].update({"fused_to_nvfp4_us": round(tf, 2), "fused_to_nvfp4_GBps": round(fbytes / tf / 1e3, 1),
+                              "producer_then_quant_us": round(tp + t1, 2)})
         del ins
     return res
 

@@ -14,6 +14,7 @@ Entry points (same names as the C ABI in include/mq.h):
     mq_gemv_bf16_decode_grouped(x_bf16, ws_bf16: [tensor], ys_bf16: [tensor], flags=0, stream=None)
     mq_gemv_nvfp4_decode(x: NVFP4, w: NVFP4, y_bf16, flags=0, stream=None)
     mq_rmsnorm_amax(x_bf16, gamma_bf16, y_bf16, rec, eps=1e-5, flags=0, stream=None)
+    mq_rmsnorm_quantize_nvfp4(x_bf16, gamma_bf16, out: NVFP4, eps=1e-5, flags=0, stream=None)
     mq_swiglu_amax(a_bf16, b_bf16, y_bf16, rec, flags=0, stream=None)
     mq_linear_path / mq_linear_prepare / mq_linear_forward (through ``Linear``)
 
@@ -52,7 +53,7 @@ MQ_MAX_GROUP = 4
 REC_BYTES = 16 + 4 * MQ_AMAX_PARTS  # sizeof(mq_scale_rec) = 4096
 
 EXPORTS = ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemm_nvfp4_prefill_grouped",
-           "mq_gemv_bf16_decode", "mq_gemv_bf16_decode_grouped", "mq_gemv_nvfp4_decode", "mq_rmsnorm_amax", "mq_swiglu_amax", "mq_linear_path", "mq_linear_prepare", "mq_linear_forward",
+           "mq_gemv_bf16_decode", "mq_gemv_bf16_decode_grouped", "mq_gemv_nvfp4_decode", "mq_rmsnorm_amax", "mq_rmsnorm_quantize_nvfp4", "mq_swiglu_amax", "mq_linear_path", "mq_linear_prepare", "mq_linear_forward",
            "mq_gemm_nvfp4_prefill_fused_noalloc", "mq_status_str", "mq_last_error", "mq_version")
 
 
@@ -109,6 +110,8 @@ def lib():
     L.mq_gemv_nvfp4_decode.restype = ctypes.c_int32
     L.mq_rmsnorm_amax.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_float, u32, vp]
     L.mq_rmsnorm_amax.restype = ctypes.c_int32
+    L.mq_rmsnorm_quantize_nvfp4.argtypes = [vp, vp, i64, i64, ctypes.c_float, P, u32, vp]
+    L.mq_rmsnorm_quantize_nvfp4.restype = ctypes.c_int32
     L.mq_swiglu_amax.argtypes = [vp, vp, vp, vp, i64, i64, u32, vp]
     L.mq_swiglu_amax.restype = ctypes.c_int32
     LP = ctypes.POINTER(_LinearC)
@@ -357,6 +360,22 @@ def mq_rmsnorm_amax(x_bf16, gamma_bf16, y_bf16, rec, eps: float = 1e-5, flags: i
     rows, cols = x_bf16.shape
     _check(lib().mq_rmsnorm_amax(_dev_ptr(x_bf16, "x"), _dev_ptr(gamma_bf16, "gamma"), _dev_ptr(y_bf16, "y"),
                                  _rec_ptr(rec), rows, cols, eps, flags, _stream_ptr(stream)), "mq_rmsnorm_amax")
+
+
+def mq_rmsnorm_quantize_nvfp4(x_bf16, gamma_bf16, out: NVFP4, eps: float = 1e-5, flags: int = 0, stream=None):
+    """out = NVFP4(RMSNorm(x) * gamma), the bf16 RMSNorm output never
+    stored (bit-identical to mq_rmsnorm_amax then MQ_SCALE_PARTIALS)."""
+    import torch
+    if x_bf16.dtype != torch.bfloat16 or x_bf16.dim() != 2 or gamma_bf16.dtype != torch.bfloat16 \
+            or tuple(gamma_bf16.shape) != (x_bf16.shape[1],):
+        raise ValueError("x bfloat16 [rows][cols] and gamma bfloat16 [cols]")
+    rows, cols = x_bf16.shape
+    if out.shape != (rows, cols):
+        raise ValueError(f"out is {out.shape}, x is {(rows, cols)}")
+    oc = out._c()
+    _check(lib().mq_rmsnorm_quantize_nvfp4(_dev_ptr(x_bf16, "x"), _dev_ptr(gamma_bf16, "gamma"), rows, cols, eps,
+                                           ctypes.byref(oc), flags, _stream_ptr(stream)),
+           "mq_rmsnorm_quantize_nvfp4")
 
 
 def mq_swiglu_amax(a_bf16, b_bf16, y_bf16, rec, flags: int = 0, stream=None):

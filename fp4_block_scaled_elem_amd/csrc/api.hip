@@ -277,6 +277,25 @@ mq_status mq_rmsnorm_amax(const void* x_bf16, const void* gamma_bf16, void* y_bf
                   "rmsnorm_amax");
 }
 
+mq_status mq_rmsnorm_quantize_nvfp4(const void* x_bf16, const void* gamma_bf16, int64_t rows, int64_t cols,
+                                    float eps, const mq_nvfp4* out, uint32_t flags, void* hip_stream) {
+  if (flags) return fail(MQ_ERR_INVALID, "unknown flags 0x%x", flags);
+  if (!x_bf16 || !gamma_bf16 || !out) return fail(MQ_ERR_INVALID, "x, gamma and out must not be NULL");
+  if (!out->codes || !out->scales || !out->rec)
+    return fail(MQ_ERR_INVALID, "out->codes, scales and rec must not be NULL");
+  if (mq_status s = check_dims(rows, cols, "rows", "cols")) return s;
+  if (cols % 16) return fail(MQ_ERR_SHAPE, "cols=%lld is not a multiple of 16", (long long)cols);
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(MQ_ERR_INVALID, "eps must be finite and >= 0");
+  if (!aligned(x_bf16, 16) || !aligned(gamma_bf16, 16) || !aligned(out->codes, 16) || !aligned(out->scales, 8) ||
+      !aligned(out->rec, 16))
+    return fail(MQ_ERR_ALIGN, "x, gamma and codes need 16-byte, scales 8-byte, rec 16-byte alignment");
+  mq::DeviceInfo dev;
+  if (mq_status s = current_device(dev)) return s;
+  return launched(mq::launch_rmsnorm_quantize(x_bf16, gamma_bf16, rows, cols, eps, out->codes, out->scales, out->rec,
+                                              dev, (hipStream_t)hip_stream),
+                  "rmsnorm_quantize");
+}
+
 mq_status mq_swiglu_amax(const void* a_bf16, const void* b_bf16, void* y_bf16, mq_scale_rec* rec, int64_t rows,
                          int64_t cols, uint32_t flags, void* hip_stream) {
   if (flags) return fail(MQ_ERR_INVALID, "unknown flags 0x%x", flags);

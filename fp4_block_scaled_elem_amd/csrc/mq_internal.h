@@ -111,6 +111,11 @@ hipError_t launch_gemv_nvfp4(const GemvNvfp4Args& a, hipStream_t stream);
 
 hipError_t launch_rmsnorm_amax(const void* x, const void* g, void* y, int64_t rows, int64_t cols, float eps,
                                mq_scale_rec* rec, const DeviceInfo& dev, hipStream_t stream);
+// RMSNorm fused with NVFP4 quantization: y's partial maxima into rec (y not
+// stored), then y recomputed and encoded into codes and scales, s_t into rec.
+hipError_t launch_rmsnorm_quantize(const void* x, const void* g, int64_t rows, int64_t cols, float eps,
+                                   uint8_t* codes, uint8_t* scales, mq_scale_rec* rec, const DeviceInfo& dev,
+                                   hipStream_t stream);
 hipError_t launch_swiglu_amax(const void* a, const void* b, void* y, int64_t n, mq_scale_rec* rec,
                               const DeviceInfo& dev, hipStream_t stream);
 

@@ -17,7 +17,11 @@
 //   swiglu_amax_kernel   y = bf16(silu(a) * b), silu(a) = a / (1 + exp(-a)),
 //                        elementwise, 16-byte loads.
 // Both are HBM-bound: 2 bytes read and 2 written per element (RMSNorm),
-// 4 read and 2 written (SwiGLU).  Their outputs are rounded binary32 results, not bit-identical
+// 4 read and 2 written (SwiGLU).  The RMSNorm also comes fused with the
+// quantization, when y feeds only the linears (the q/k/v and gate/up
+// inputs): a first pass takes the maxima without storing y, a second
+// recomputes y and encodes it (rmsnorm_encode_kernel), so y never goes to
+// HBM: 2 + 2.5625 bytes per element instead of 2 + 2 + 2.5625.  Their outputs are rounded binary32 results, not bit-identical
 // to any other order of evaluation; the maxima they emit are those of the
 // exact bf16 values they store.
 #include "mq_device.h"
@@ -92,6 +96,9 @@ __device__ __forceinline__ float sumsq_piece(uint4 v) {
   return ss;
 }
 
+// STORE false: the maxima alone (the first pass of the RMSNorm fused with
+// quantization, whose second pass recomputes y).
+template <bool STORE>
 __global__ __launch_bounds__(kRThreads) void rmsnorm_amax_kernel(const uint4* __restrict__ x,
                                                                  const uint4* __restrict__ g,
                                                                  uint4* __restrict__ y, int64_t rows, int cols,
@@ -102,30 +109,75 @@ __global__ __launch_bounds__(kRThreads) void rmsnorm_amax_kernel(const uint4* __
   const int pieces = cols / 8;
   const float inv_cols = 1.0f / (float)cols;
   uint32_t am = 0;  // max bf16 magnitude bits written by this lane
-  for (int64_t r = (int64_t)blockIdx.x * kWaves + wave; r < rows; r += (int64_t)gridDim.x * kWaves) {
-    const uint4* xr = x + r * pieces;
-    uint4* yr = y + r * pieces;
-    if (pieces <= 64 * kRowPieces) {
-      uint4 v[kRowPieces];
-      float ss = 0.0f;
+  const int64_t rstride = (int64_t)gridDim.x * kWaves;
+  const int64_t r0 = (int64_t)blockIdx.x * kWaves + wave;
+  if (!STORE && pieces <= 64 * kRowPieces) {
+    // maxima only (the fused quantization's first pass): rows one ahead
+    // (the next row's loads go out before this row's math), gamma loaded
+    // once per wave, and x read through the caches, where the second pass
+    // finds it
+    uint4 gv[kRowPieces], v[kRowPieces];
+    auto load_row = [&](int64_t row, uint4 (&dst)[kRowPieces]) __attribute__((always_inline)) {
+      const uint4* xr = x + row * pieces;
 #pragma unroll
       for (int k = 0; k < kRowPieces; ++k) {
         const int p = lane + 64 * k;
-        v[k] = p < pieces ? ld_stream(&xr[p]) : make_uint4(0, 0, 0, 0);
+        dst[k] = (p < pieces && row < rows) ? xr[p] : make_uint4(0, 0, 0, 0);
       }
+    };
+#pragma unroll
+    for (int k = 0; k < kRowPieces; ++k) {
+      const int p = lane + 64 * k;
+      gv[k] = p < pieces ? g[p] : make_uint4(0, 0, 0, 0);
+    }
+    load_row(r0, v);
+    for (int64_t r = r0; r < rows; r += rstride) {
+      uint4 nv[kRowPieces];
+      load_row(r + rstride, nv);
+      float ss = 0.0f;
 #pragma unroll
       for (int k = 0; k < kRowPieces; ++k) ss += sumsq_piece(v[k]);
       const float rstd = 1.0f / sqrtf(wave_sum_f32(ss) * inv_cols + eps);
 #pragma unroll
       for (int k = 0; k < kRowPieces; ++k) {
         const int p = lane + 64 * k;
-        if (p < pieces) yr[p] = rms_piece(v[k], g[p], rstd, am);
+        if (p < pieces) (void)rms_piece(v[k], gv[k], rstd, am);
       }
-    } else {
-      float ss = 0.0f;
-      for (int p = lane; p < pieces; p += 64) ss += sumsq_piece(xr[p]);
-      const float rstd = 1.0f / sqrtf(wave_sum_f32(ss) * inv_cols + eps);
-      for (int p = lane; p < pieces; p += 64) yr[p] = rms_piece(xr[p], g[p], rstd, am);
+#pragma unroll
+      for (int k = 0; k < kRowPieces; ++k) v[k] = nv[k];
+    }
+  } else {
+    for (int64_t r = r0; r < rows; r += rstride) {
+      const uint4* xr = x + r * pieces;
+      uint4* yr = y + r * pieces;
+      if (pieces <= 64 * kRowPieces) {
+        uint4 v[kRowPieces];
+        float ss = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kRowPieces; ++k) {
+          const int p = lane + 64 * k;
+          v[k] = p < pieces ? ld_stream(&xr[p]) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < kRowPieces; ++k) ss += sumsq_piece(v[k]);
+        const float rstd = 1.0f / sqrtf(wave_sum_f32(ss) * inv_cols + eps);
+#pragma unroll
+        for (int k = 0; k < kRowPieces; ++k) {
+          const int p = lane + 64 * k;
+          if (p < pieces) {
+            const uint4 o = rms_piece(v[k], g[p], rstd, am);
+            if constexpr (STORE) yr[p] = o;
+          }
+        }
+      } else {
+        float ss = 0.0f;
+        for (int p = lane; p < pieces; p += 64) ss += sumsq_piece(xr[p]);
+        const float rstd = 1.0f / sqrtf(wave_sum_f32(ss) * inv_cols + eps);
+        for (int p = lane; p < pieces; p += 64) {
+          const uint4 o = rms_piece(xr[p], g[p], rstd, am);
+          if constexpr (STORE) yr[p] = o;
+        }
+      }
     }
   }
   const uint32_t m = block_max_bits<kRThreads>(am, shm);
@@ -133,6 +185,113 @@ __global__ __launch_bounds__(kRThreads) void rmsnorm_amax_kernel(const uint4* __
     rec->part[blockIdx.x] = m << 16;
     if (blockIdx.x == 0) rec->nparts = gridDim.x;
   }
+}
+
+// Second pass of the RMSNorm fused with NVFP4 quantization: the tensor
+// scale from the first pass's partial maxima (as the encode pass reduces
+// them), then every row's y recomputed exactly as rmsnorm_amax_kernel
+// computes it (the same functions in the same order, so the same bf16
+// values) and encoded as the quantizer's encode pass encodes a half-group
+// per lane: a row's pieces 2q and 2q + 1 (one 16-element group) sit in
+// lanes 2j and 2j + 1, which swap their half maxima.  y itself is never
+// stored.
+template <bool OVF>
+__device__ __forceinline__ void encode_piece(uint4 yv, int64_t h, const GroupScaleTab& tab,
+                                             uint32_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const uint32_t w[4] = {yv.x, yv.y, yv.z, yv.w};
+  uint32_t am = bf16_absmax_bits<4>(w);
+  const uint32_t other = __shfl_xor(am, 1, 64);
+  am = am > other ? am : other;
+  float e;
+  const uint32_t S = group_scale(am, tab, e);
+  codes[h] = encode8<OVF>(w, e);
+  if ((h & 1) == 0) scales[h >> 1] = (uint8_t)S;
+}
+
+__global__ __launch_bounds__(kRThreads) void rmsnorm_encode_kernel(const uint4* __restrict__ x,
+                                                                   const uint4* __restrict__ g, int64_t rows,
+                                                                   int cols, float eps,
+                                                                   uint32_t* __restrict__ codes,
+                                                                   uint8_t* __restrict__ scales,
+                                                                   mq_scale_rec* __restrict__ rec) {
+  __shared__ uint32_t shm[kRThreads / 64];
+  __shared__ float recip[128];
+  constexpr int kWaves = kRThreads / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int pieces = cols / 8;  // even: a group never straddles two lanes' rows
+  const float inv_cols = 1.0f / (float)cols;
+  const int64_t rstride = (int64_t)gridDim.x * kWaves;
+  int64_t r = (int64_t)blockIdx.x * kWaves + wave;
+  const bool regs = pieces <= 64 * kRowPieces;
+  // rows held in registers: gamma's pieces once per wave, the wave's first
+  // row in flight before the tensor scale is reduced
+  uint4 gv[kRowPieces], v[kRowPieces];
+  auto load_row = [&](int64_t row, uint4 (&dst)[kRowPieces]) __attribute__((always_inline)) {
+    const uint4* xr = x + row * pieces;
+#pragma unroll
+    for (int k = 0; k < kRowPieces; ++k) {
+      const int p = lane + 64 * k;
+      dst[k] = (p < pieces && row < rows) ? ld_stream(&xr[p]) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (regs) {
+#pragma unroll
+    for (int k = 0; k < kRowPieces; ++k) {
+      const int p = lane + 64 * k;
+      gv[k] = p < pieces ? g[p] : make_uint4(0, 0, 0, 0);
+    }
+    load_row(r, v);
+  }
+  // the partial maxima (the count clamped to the record's capacity)
+  const uint32_t n = min(rec->nparts, (uint32_t)MQ_AMAX_PARTS);
+  uint32_t m = 0;
+  for (uint32_t j = threadIdx.x; j < n; j += kRThreads) {
+    const uint32_t pv = rec->part[j];
+    m = m > pv ? m : pv;
+  }
+  const uint32_t amax = block_max_bits<kRThreads>(m, shm);
+  const float s_t = tensor_scale_from_amax(amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    rec->s_t = s_t;
+    rec->amax_bits = amax;
+  }
+  const GroupScaleTab tab = group_scale_tab<kRThreads>(s_t, recip);
+  auto run = [&](auto ovf_c) __attribute__((always_inline)) {
+    constexpr bool OVF = decltype(ovf_c)::value;
+    uint32_t unused = 0;
+    if (regs) {
+      // one row ahead: the next row's loads go out before this row's math
+      for (; r < rows; r += rstride) {
+        uint4 nv[kRowPieces];
+        load_row(r + rstride, nv);
+        float ss = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kRowPieces; ++k) ss += sumsq_piece(v[k]);
+        const float rstd = 1.0f / sqrtf(wave_sum_f32(ss) * inv_cols + eps);
+        const int64_t h0 = r * pieces;  // the row's first half-group
+#pragma unroll
+        for (int k = 0; k < kRowPieces; ++k) {
+          const int p = lane + 64 * k;
+          if (p < pieces) encode_piece<OVF>(rms_piece(v[k], gv[k], rstd, unused), h0 + p, tab, codes, scales);
+        }
+#pragma unroll
+        for (int k = 0; k < kRowPieces; ++k) v[k] = nv[k];
+      }
+    } else {
+      for (; r < rows; r += rstride) {
+        const uint4* xr = x + r * pieces;
+        float ss = 0.0f;
+        for (int p = lane; p < pieces; p += 64) ss += sumsq_piece(xr[p]);
+        const float rstd = 1.0f / sqrtf(wave_sum_f32(ss) * inv_cols + eps);
+        for (int p = lane; p < pieces; p += 64)
+          encode_piece<OVF>(rms_piece(xr[p], g[p], rstd, unused), r * pieces + p, tab, codes, scales);
+      }
+    }
+  };
+  if (tab.ovf)
+    run(BoolC<true>{});
+  else
+    run(BoolC<false>{});
 }
 
 // Elementwise over n8 pieces of 8 elements, grid-stride.
@@ -169,14 +328,39 @@ __global__ __launch_bounds__(kPThreads) void swiglu_amax_kernel(const uint4* __r
   }
 }
 
-hipError_t launch_rmsnorm_amax(const void* x, const void* g, void* y, int64_t rows, int64_t cols, float eps,
-                               mq_scale_rec* rec, const DeviceInfo& dev, hipStream_t stream) {
+static int64_t rmsnorm_blocks(int64_t rows, const DeviceInfo& dev) {
   const int64_t row_groups = (rows + kRThreads / 64 - 1) / (kRThreads / 64);  // eight rows per workgroup
   int64_t blocks = row_groups < 2 * (int64_t)dev.num_cu ? row_groups : 2 * (int64_t)dev.num_cu;
-  if (blocks > MQ_AMAX_PARTS) blocks = MQ_AMAX_PARTS;
-  log_launch("rmsnorm_amax_kernel", blocks, kRThreads, 0, "rows=%lld cols=%lld", (long long)rows, (long long)cols);
-  hipLaunchKernelGGL(rmsnorm_amax_kernel, dim3((unsigned)blocks), dim3(kRThreads), 0, stream, (const uint4*)x,
-                     (const uint4*)g, (uint4*)y, rows, (int)cols, eps, rec);
+  return blocks > MQ_AMAX_PARTS ? MQ_AMAX_PARTS : blocks;
+}
+
+hipError_t launch_rmsnorm_amax(const void* x, const void* g, void* y, int64_t rows, int64_t cols, float eps,
+                               mq_scale_rec* rec, const DeviceInfo& dev, hipStream_t stream) {
+  const int64_t blocks = rmsnorm_blocks(rows, dev);
+  log_launch("rmsnorm_amax_kernel", blocks, kRThreads, 0, "rows=%lld cols=%lld store=1", (long long)rows,
+             (long long)cols);
+  hipLaunchKernelGGL(rmsnorm_amax_kernel<true>, dim3((unsigned)blocks), dim3(kRThreads), 0, stream,
+                     (const uint4*)x, (const uint4*)g, (uint4*)y, rows, (int)cols, eps, rec);
+  return hipGetLastError();
+}
+
+// The fused passes take a workgroup per CU, so that each wave has rows to
+// pipeline (two at 4096 rows).
+hipError_t launch_rmsnorm_quantize(const void* x, const void* g, int64_t rows, int64_t cols, float eps,
+                                   uint8_t* codes, uint8_t* scales, mq_scale_rec* rec, const DeviceInfo& dev,
+                                   hipStream_t stream) {
+  const int64_t row_groups = (rows + kRThreads / 64 - 1) / (kRThreads / 64);
+  const int64_t blocks = row_groups < (int64_t)dev.num_cu ? row_groups : (int64_t)dev.num_cu;
+  log_launch("rmsnorm_amax_kernel", blocks, kRThreads, 0, "rows=%lld cols=%lld store=0", (long long)rows,
+             (long long)cols);
+  hipLaunchKernelGGL(rmsnorm_amax_kernel<false>, dim3((unsigned)blocks), dim3(kRThreads), 0, stream,
+                     (const uint4*)x, (const uint4*)g, nullptr, rows, (int)cols, eps, rec);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  log_launch("rmsnorm_encode_kernel", blocks, kRThreads, 0, "rows=%lld cols=%lld", (long long)rows,
+             (long long)cols);
+  hipLaunchKernelGGL(rmsnorm_encode_kernel, dim3((unsigned)blocks), dim3(kRThreads), 0, stream, (const uint4*)x,
+                     (const uint4*)g, rows, (int)cols, eps, (uint32_t*)codes, scales, rec);
   return hipGetLastError();
 }
 

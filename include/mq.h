@@ -23,6 +23,9 @@
  *   mq_rmsnorm_amax / mq_swiglu_amax
  *                          the ops that write the linears' activations,
  *                          emitting the amax pass's partial maxima
+ *   mq_rmsnorm_quantize_nvfp4
+ *                          RMSNorm whose output goes straight to NVFP4
+ *                          (the bf16 output is never stored)
  *   mq_gemv_nvfp4_decode   the decode GEMV with X and W in NVFP4 (the
  *                          uniform-quantization baseline the method avoids)
  *   mq_linear_prepare / mq_linear_forward / mq_linear_path
@@ -300,6 +303,29 @@ mq_status mq_gemv_bf16_decode_grouped(const void* x_bf16, int32_t n_group,
 mq_status mq_rmsnorm_amax(const void* x_bf16, const void* gamma_bf16, void* y_bf16,
                           mq_scale_rec* rec, int64_t rows, int64_t cols, float eps,
                           uint32_t flags, void* hip_stream);
+
+/*
+ * mq_rmsnorm_quantize_nvfp4 - out = NVFP4(RMSNorm(x) * gamma), the bf16
+ *   output of the RMSNorm never stored.  For an RMSNorm whose output feeds
+ *   only prefill linears (the q/k/v and gate/up inputs of a layer): the
+ *   dynamic tensor scale of the quantizer (gist.science explainer, s.2
+ *   Hybrid Precision Strategy) taken on the op's own output.  Two passes
+ *   over x: the first takes y's partial maxima into out->rec without
+ *   storing y, the second recomputes y and encodes it.  Codes, scale bytes
+ *   and s_t are bit-identical to mq_rmsnorm_amax(x, gamma, y, out->rec, ...)
+ *   followed by mq_quantize_nvfp4(y, out, MQ_SCALE_PARTIALS), and y is the
+ *   same bf16 tensor mq_rmsnorm_amax writes.
+ * x_bf16      DEVICE bf16 [rows][cols], 16-byte aligned.
+ * gamma_bf16  DEVICE bf16 [cols], 16-byte aligned.
+ * out         HOST pointer to caller-owned NVFP4 buffers [rows][cols]:
+ *             codes 16-byte, scales 8-byte, rec 16-byte aligned (no
+ *             initialisation needed).
+ * rows, cols  >= 1; cols % 16 == 0.
+ * eps         finite, >= 0.
+ * flags       0.
+ */
+mq_status mq_rmsnorm_quantize_nvfp4(const void* x_bf16, const void* gamma_bf16, int64_t rows, int64_t cols,
+                                    float eps, const mq_nvfp4* out, uint32_t flags, void* hip_stream);
 
 /*
  * mq_swiglu_amax - y = bf16(silu(a) * b) elementwise, silu(a) = a/(1+exp(-a))

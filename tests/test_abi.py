@@ -37,6 +37,7 @@ def test_header_declares_the_entry_points():
     fns = _header_functions()
     for f in ("mq_quantize_nvfp4", "mq_gemm_nvfp4_prefill", "mq_gemm_nvfp4_prefill_grouped",
               "mq_gemv_bf16_decode", "mq_gemv_nvfp4_decode", "mq_rmsnorm_amax", "mq_swiglu_amax",
+              "mq_rmsnorm_quantize_nvfp4",
               "mq_linear_path", "mq_linear_prepare", "mq_linear_forward"):
         assert f in fns
 
@@ -213,6 +214,17 @@ def test_producer_argument_errors(L):
     assert r(P16, P16, P16 + 16, P16, 4, 24, 1e-5, 0, None) == mq.MQ_ERR_SHAPE
     assert r(P8, P16, P16 + 16, P16, 4, 16, 1e-5, 0, None) == mq.MQ_ERR_ALIGN
     assert r(P16, P16, P16 + 16, P8, 4, 16, 1e-5, 0, None) == mq.MQ_ERR_ALIGN
+    rq = L.mq_rmsnorm_quantize_nvfp4
+    assert rq(None, P16, 4, 16, 1e-5, _q(P16, P16, P16), 0, None) == mq.MQ_ERR_INVALID
+    assert rq(P16, P16, 4, 16, 1e-5, None, 0, None) == mq.MQ_ERR_INVALID
+    assert rq(P16, P16, 4, 16, 1e-5, _q(P16, None, P16), 0, None) == mq.MQ_ERR_INVALID
+    assert rq(P16, P16, 4, 16, 1e-5, _q(P16, P16, P16), 1, None) == mq.MQ_ERR_INVALID
+    assert rq(P16, P16, 4, 16, -1.0, _q(P16, P16, P16), 0, None) == mq.MQ_ERR_INVALID
+    assert rq(P16, P16, 0, 16, 1e-5, _q(P16, P16, P16), 0, None) == mq.MQ_ERR_SHAPE
+    assert rq(P16, P16, 4, 24, 1e-5, _q(P16, P16, P16), 0, None) == mq.MQ_ERR_SHAPE
+    assert rq(P8, P16, 4, 16, 1e-5, _q(P16, P16, P16), 0, None) == mq.MQ_ERR_ALIGN
+    assert rq(P16, P16, 4, 16, 1e-5, _q(P8, P16, P16), 0, None) == mq.MQ_ERR_ALIGN
+    assert rq(P16, P16, 4, 16, 1e-5, _q(P16, P1, P16), 0, None) == mq.MQ_ERR_ALIGN
     s = L.mq_swiglu_amax
     assert s(P16, None, P16 + 16, P16, 4, 16, 0, None) == mq.MQ_ERR_INVALID
     assert s(P16, P16, P16 + 16, P16, 4, 16, 2, None) == mq.MQ_ERR_INVALID
@@ -323,6 +335,7 @@ def test_valid_arguments_without_a_gpu_report_device_error(L):
                                   None) == mq.MQ_ERR_DEVICE
     assert L.mq_rmsnorm_amax(P16, P16, P16 + 16, P16, 4, 16, 1e-5, 0, None) == mq.MQ_ERR_DEVICE
     assert L.mq_swiglu_amax(P16, P16 + 16, P16 + 32, P16, 4, 16, 0, None) == mq.MQ_ERR_DEVICE
+    assert L.mq_rmsnorm_quantize_nvfp4(P16, P16, 4, 16, 1e-5, _q(P16, P16, P16), 0, None) == mq.MQ_ERR_DEVICE
     assert L.mq_quantize_nvfp4(P16, 4, 16, _q(P16, P16, P16), mq.MQ_SCALE_PARTIALS, None) == mq.MQ_ERR_DEVICE
     assert L.mq_linear_prepare(_lin(), None) == mq.MQ_ERR_DEVICE
     assert L.mq_linear_forward(_lin(), P16, 1, None, P1 + 1, 0, None) == mq.MQ_ERR_DEVICE

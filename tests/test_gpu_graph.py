@@ -187,3 +187,26 @@ def test_phase_aware_linear_replay(M):
         ye = lin.forward(xr)
         torch.cuda.synchronize()
         assert _same(y, ye), f"replay {r}"
+
+
+def test_rmsnorm_quantize_replay():
+    # the RMSNorm fused with quantization: both passes captured; each replay
+    # on new data equals the eager call bit for bit
+    announce("graph: rmsnorm fused with quantization")
+    import torch
+    mq = _mq()
+    M, K = 256, 4096
+    x = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    x.copy_(to_dev_bf16(workloads.random_bf16((M, K), 50, 1.0, "lognormal_mixed")))
+    g = to_dev_bf16(workloads.random_bf16((K,), 51, 1.0))
+    q = mq.NVFP4.empty(M, K)
+    graph = _capture(lambda: mq.mq_rmsnorm_quantize_nvfp4(x, g, q))
+    for r in range(REPLAYS):
+        xr = to_dev_bf16(workloads.random_bf16((M, K), 52 + r, 4.0 ** r, "lognormal_mixed"))
+        x.copy_(xr)
+        graph.replay()
+        qe = mq.NVFP4.empty(M, K)
+        mq.mq_rmsnorm_quantize_nvfp4(xr, g, qe)
+        torch.cuda.synchronize()
+        assert torch.equal(q.codes, qe.codes) and torch.equal(q.scales, qe.scales), f"replay {r}"
+        assert torch.equal(q.rec[:1], qe.rec[:1]), f"replay {r}: s_t"

@@ -1,5 +1,7 @@
 """GPU parity of the producer ops with the amax pass folded in
-(mq_rmsnorm_amax, mq_swiglu_amax).
+(mq_rmsnorm_amax, mq_swiglu_amax), and of the RMSNorm fused with the
+quantization (mq_rmsnorm_quantize_nvfp4, bit-identical to the producer
+followed by the partial-maxima quantization).
 
 Each output is compared element by element with the float64 oracle (within
 bf16 rounding of binary32 arithmetic).  The partial maxima they leave in the
@@ -124,3 +126,35 @@ def test_fused_gemm_and_linear_take_the_partials():
     torch.cuda.synchronize()
     assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
     assert torch.equal(c3.view(torch.int16), c2.view(torch.int16))
+
+
+@pytest.mark.parametrize("rows,cols,seed", [(1, 16, 10), (7, 48, 11), (37, 4096, 12), (300, 1040, 13),
+                                            (4096, 4096, 14), (3, 14336, 15), (2, 4112, 16)])
+def test_rmsnorm_quantize_nvfp4(rows, cols, seed):
+    # the RMSNorm fused with quantization (its bf16 output never stored):
+    # codes, scales and s_t bit-identical to mq_rmsnorm_amax followed by
+    # the partial-maxima quantization, and to the oracle's quantization of
+    # that y; rows past 4096 elements (read twice) and odd group counts
+    # included
+    announce("rmsnorm_quantize_nvfp4", rows, cols)
+    import torch
+    mq = _mq()
+    xb = workloads.random_bf16((rows, cols), seed, 1.0, "lognormal_mixed")
+    gb = workloads.random_bf16((cols,), seed + 100, 1.0)
+    eps = 1e-5
+    x, g = to_dev_bf16(xb), to_dev_bf16(gb)
+    q = mq.NVFP4.empty(rows, cols)
+    mq.mq_rmsnorm_quantize_nvfp4(x, g, q, eps)
+    y = torch.empty_like(x)
+    q2 = mq.NVFP4.empty(rows, cols)
+    mq.mq_rmsnorm_amax(x, g, y, q2, eps)
+    mq.mq_quantize_nvfp4(y, q2, mq.MQ_SCALE_PARTIALS)
+    torch.cuda.synchronize()
+    c1, s1, t1 = quantized_host(q)
+    c2, s2, t2 = quantized_host(q2)
+    assert t1 == t2 and np.array_equal(s1, s2) and np.array_equal(c1, c2)
+    yb = _host_bits(y)
+    ref = oracle.quantize_nvfp4(yb)
+    assert t1 == int(np.float32(ref.s_t).view(np.uint32))
+    assert np.array_equal(s1, ref.scales) and np.array_equal(c1, ref.codes)
+    _check_values(yb, oracle.rmsnorm_ref(xb, gb, eps))
