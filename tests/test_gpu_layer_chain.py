@@ -13,7 +13,9 @@ those -> down GEMM.  Every link is held to the oracle on sampled rows:
 * every quantized activation byte for byte against ``oracle.quantize_nvfp4``
   of the bf16 tensor the GPU actually produced (whole-tensor scale);
 * every GEMM output by rule T against the float64 product of the oracle's
-  quantized operands.
+  quantized operands;
+* the RMSNorms straight to NVFP4 (as the benchmark's layer runs them now):
+  the same activation bytes and tensor scales as the chain.
 """
 
 import numpy as np
@@ -130,3 +132,12 @@ def test_llama8b_layer_nvfp4_chain():
     for p in workloads.PROJS:
         ow, cols = ows[p]
         _gemm_ok(out[p], oa[workloads.PROJ_INPUT[p]], ow, rows, cols, p)
+
+    # the RMSNorms straight to NVFP4 (their bf16 outputs never stored): the
+    # same activation bytes and tensor scales as the chain above
+    for a, hb, gb in (("x_qkv", h, g1), ("x_gu", h2, g2)):
+        qf = mq.NVFP4.empty(M, D)
+        mq.mq_rmsnorm_quantize_nvfp4(to_dev_bf16(hb), to_dev_bf16(gb), qf, EPS)
+        torch.cuda.synchronize()
+        assert torch.equal(qf.codes, qa[a].codes) and torch.equal(qf.scales, qa[a].scales), a
+        assert torch.equal(qf.rec[:1], qa[a].rec[:1]), f"{a}: tensor scale"
