@@ -128,19 +128,23 @@ def test_fused_gemm_and_linear_take_the_partials():
     assert torch.equal(c3.view(torch.int16), c2.view(torch.int16))
 
 
-@pytest.mark.parametrize("rows,cols,seed", [(1, 16, 10), (7, 48, 11), (37, 4096, 12), (300, 1040, 13),
-                                            (4096, 4096, 14), (3, 14336, 15), (2, 4112, 16)])
-def test_rmsnorm_quantize_nvfp4(rows, cols, seed):
+@pytest.mark.parametrize("rows,cols,seed,gscale", [(1, 16, 10, 1.0), (7, 48, 11, 1.0), (37, 4096, 12, 1.0),
+                                                   (300, 1040, 13, 1.0), (4096, 4096, 14, 1.0),
+                                                   (3, 14336, 15, 1.0), (2, 4112, 16, 1.0),
+                                                   (64, 512, 17, 1.0e-38)])
+def test_rmsnorm_quantize_nvfp4(rows, cols, seed, gscale):
     # the RMSNorm fused with quantization (its bf16 output never stored):
     # codes, scales and s_t bit-identical to mq_rmsnorm_amax followed by
     # the partial-maxima quantization, and to the oracle's quantization of
     # that y; rows past 4096 elements (read twice) and odd group counts
-    # included
-    announce("rmsnorm_quantize_nvfp4", rows, cols)
+    # included, and a gamma near the bottom of bf16's range (y tiny, the
+    # tensor scale subnormal: reciprocal group scales overflow, the
+    # encoder's fix-up path)
+    announce("rmsnorm_quantize_nvfp4", rows, cols, gscale)
     import torch
     mq = _mq()
     xb = workloads.random_bf16((rows, cols), seed, 1.0, "lognormal_mixed")
-    gb = workloads.random_bf16((cols,), seed + 100, 1.0)
+    gb = workloads.random_bf16((cols,), seed + 100, gscale)
     eps = 1e-5
     x, g = to_dev_bf16(xb), to_dev_bf16(gb)
     q = mq.NVFP4.empty(rows, cols)
@@ -157,4 +161,8 @@ def test_rmsnorm_quantize_nvfp4(rows, cols, seed):
     ref = oracle.quantize_nvfp4(yb)
     assert t1 == int(np.float32(ref.s_t).view(np.uint32))
     assert np.array_equal(s1, ref.scales) and np.array_equal(c1, ref.codes)
-    _check_values(yb, oracle.rmsnorm_ref(xb, gb, eps))
+    if gscale >= 1.0e-30:
+        _check_values(yb, oracle.rmsnorm_ref(xb, gb, eps))
+    else:
+        # the fix-up path was taken: some reciprocal group scale overflows
+        assert np.float32(ref.s_t) < np.float32(2.0 ** -126)
